@@ -1,0 +1,43 @@
+"""CPU oracle for the OSDN forward pass and its Gated DeltaNet-2 generalisation.
+
+This package is TEST INFRASTRUCTURE. Only the test suite, the smoke check and
+the CPU-baseline leg of the benchmark may import it. The HIP library never
+calls it, and it shares no code, header, table or helper with the HIP path.
+
+Sources (cited by page title and section; the pages are web summaries of the
+two papers):
+
+* [OSDN-it]  "Riepilogo Tecnico: OSDN: Miglioramento della Regola Delta con
+  Precondizionamento Online Provabile nell'Attenzione Lineare"
+  (gist.science/it/paper/2605.13473).
+* [OSDN-de]  "OSDN: Improving Delta Rule with Provable Online Preconditioning
+  in Linear Attention", its "Technische Zusammenfassung" part
+  (gist.science/de/paper/2605.13473). Its sections mirror [OSDN-it].
+* [GDN2-it]  "Riepilogo Tecnico: Gated DeltaNet-2"
+  (gist.science/it/paper/2605.22791).
+
+Modules:
+
+* ``recurrence``  fp64 NumPy token-by-token recurrences (OSDN, phase 1 alone,
+  GDN-2) and the surrogate h_t, by definition and in closed form.
+* ``exact``     the same recurrences in exact rational arithmetic
+  (``fractions.Fraction``) plus an independent closed-form unrolling of the
+  state as a sum of products of transition matrices, for tiny inputs.
+
+Every function is pinned by a CPU test in ``tests/test_oracle_pins.py``
+against something other than itself (closed forms, invariants, special cases,
+exact arithmetic). Values the pages print for trained models (recall,
+perplexity, q_geo) cannot be reproduced without weights and datasets: those are
+"parity unpinned" and are not used.
+"""
+
+from .recurrence import (  # noqa: F401
+    osdn_ref,
+    precond_scan_ref,
+    deltanet_ref,
+    gdn2_ref,
+    h_closed_form,
+    h_by_definition,
+    grad_h_closed_form,
+    regression_loss,
+)
