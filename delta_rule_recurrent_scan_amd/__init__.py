@@ -1,0 +1,195 @@
+"""Python binding of libosdn.so, the MI355X (gfx950) OSDN / GDN-2 forward library.
+
+Argument marshalling only: shapes and dtypes are checked, outputs and the
+workspace are allocated with PyTorch on the inputs' device, and the C ABI
+(include/osdn.h) is called with raw device pointers and the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback. If the library is missing, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
+           "workspace_bytes", "supported",
+           "OsdnError", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libosdn.so")
+_lib = None
+
+OSDN_F32, OSDN_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: OSDN_F32, torch.bfloat16: OSDN_BF16}
+
+
+class OsdnError(RuntimeError):
+    def __init__(self, status, where):
+        msg = load_library().osdn_strerror(status).decode()
+        super().__init__("%s failed with status %d: %s" % (where, status, msg))
+        self.status = status
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libosdn.so (built in-tree); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            "libosdn.so is not built (%s); run "
+            "`python -m delta_rule_recurrent_scan_amd.build`" % _LIB_PATH)
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.osdn_strerror.argtypes = [I]
+    L.osdn_strerror.restype = ctypes.c_char_p
+    L.osdn_forward_supported.argtypes = [I, I, I, I]
+    L.osdn_forward_supported.restype = I
+    L.osdn_forward_workspace_bytes.argtypes = [I] * 7
+    L.osdn_forward_workspace_bytes.restype = Z
+    L.osdn_forward.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, F, P, P, P, P,
+                                          Z, P])
+    L.osdn_forward.restype = I
+    L.osdn_precond_scan.argtypes = [I, I, I, I, I, P, P, P, F, P, P, P, P]
+    L.osdn_precond_scan.restype = I
+    L.osdn_chunk_forward.argtypes = [I] * 7 + [P, P, P, P, P, P, F, P, P, P]
+    L.osdn_chunk_forward.restype = I
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape),
+                                                           tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def supported(Dk, Dv, chunk, dtype):
+    return bool(load_library().osdn_forward_supported(Dk, Dv, chunk,
+                                                      _DTYPE_CODE[dtype]))
+
+
+def workspace_bytes(B, H, T, Dk, Dv, chunk, dtype):
+    return int(load_library().osdn_forward_workspace_bytes(
+        B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dtype]))
+
+
+def osdn_forward(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None, chunk=64,
+                 scale=1.0, out=None, workspace=None):
+    """OSDN forward on the GPU: returns (o, S_T, d_T).
+
+    q, k: [B,H,T,Dk]; v: [B,H,T,Dv] (fp32 or bf16, one dtype); beta, r:
+    [B,H,T] fp32 (r=None: no forgetting gate); d0: [B,H,Dk] fp32 (None: ones);
+    S0: [B,H,Dv,Dk] fp32 (None: zeros). ``out`` may pass preallocated
+    (o, S_T, d_T) (S_T or d_T may be None to skip it) and ``workspace`` a
+    preallocated uint8 device buffer, so that a call allocates nothing.
+    """
+    L = load_library()
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    _check(r, "r", (B, H, T), torch.float32, dev)
+    _check(d0, "d0", (B, H, Dk), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+        d_T = torch.empty((B, H, Dk), dtype=torch.float32, device=dev)
+    else:
+        o, S_T, d_T = out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    _check(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    _check(d_T, "d_T", (B, H, Dk), torch.float32, dev)
+    need = L.osdn_forward_workspace_bytes(B, H, T, Dk, Dv, chunk,
+                                          _DTYPE_CODE[dt])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = L.osdn_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt], _ptr(q),
+                        _ptr(k), _ptr(v), _ptr(beta), _ptr(r), float(eta),
+                        _ptr(d0), _ptr(S0), float(scale), _ptr(o), _ptr(S_T),
+                        _ptr(d_T), _ptr(workspace), workspace.numel(),
+                        _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_forward")
+    return o, S_T, d_T
+
+
+def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True):
+    """Phase 1 alone on the GPU: returns (ktilde or None, d_T)."""
+    L = load_library()
+    dev = k.device
+    B, H, T, Dk = k.shape
+    dt = k.dtype
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    _check(r, "r", (B, H, T), torch.float32, dev)
+    _check(d0, "d0", (B, H, Dk), torch.float32, dev)
+    kt = torch.empty_like(k) if want_ktilde else None
+    d_T = torch.empty((B, H, Dk), dtype=torch.float32, device=dev)
+    rc = L.osdn_precond_scan(B, H, T, Dk, _DTYPE_CODE[dt], _ptr(k), _ptr(beta),
+                             _ptr(r), float(eta), _ptr(d0), _ptr(kt), _ptr(d_T),
+                             _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_precond_scan")
+    return kt, d_T
+
+
+def osdn_chunk_forward(q, k, ktilde, v, beta, S0=None, chunk=64, scale=1.0,
+                       out=None):
+    """Phase 2 alone on the GPU (write keys ktilde given): returns (o, S_T)."""
+    L = load_library()
+    dev = q.device
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (ktilde, "ktilde")):
+        _check(t, n, (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    else:
+        o, S_T = out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    _check(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    rc = L.osdn_chunk_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt], _ptr(q),
+                              _ptr(k), _ptr(ktilde), _ptr(v), _ptr(beta),
+                              _ptr(S0), float(scale), _ptr(o), _ptr(S_T),
+                              _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_chunk_forward")
+    return o, S_T

@@ -1,0 +1,117 @@
+// Device helpers shared by the OSDN / GDN-2 kernels (gfx950, wave64).
+//
+// * bf16 <-> fp32 conversion (hardware round-to-nearest-even on gfx950),
+// * an "NT" MFMA tile helper: acc(16x16, fp32) += A(16 x K) * B(16 x K)^T with
+//   both operands read from LDS as K-contiguous rows,
+// * wave-level reductions built from DPP row operations and the gfx950
+//   cross-row lane swaps (no LDS round trip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osdn {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---------------------------------------------------------------------------
+// MFMA tile: acc[16x16] += A[16 x KEXT] * Bt[16 x KEXT]^T
+//
+// A and Bt point at the tile origin in LDS (row-major, leading dimensions lda
+// and ldb elements). Output layout (all 16x16 fp32 MFMAs on CDNA): lane l holds
+// rows 4*(l/16) + i, i = 0..3, of column l%16 in acc[i].
+//
+// Operand layout: lane l supplies row l%16 of A and of Bt and a run of K
+// indices chosen by l/16. A and Bt use the same (lane group, slot) -> k map, so
+// the product is independent of the order the hardware assigns within a run.
+// ---------------------------------------------------------------------------
+template <int KEXT>
+__device__ __forceinline__ void mma_nt(f32x4& acc, const __bf16* A, int lda,
+                                       const __bf16* Bt, int ldb) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const __bf16* a = A + r * lda;
+  const __bf16* b = Bt + r * ldb;
+#pragma unroll
+  for (int kk = 0; kk + 32 <= KEXT; kk += 32) {
+    bf16x8 av = *reinterpret_cast<const bf16x8*>(a + kk + g * 8);
+    bf16x8 bv = *reinterpret_cast<const bf16x8*>(b + kk + g * 8);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+  if constexpr (KEXT % 32 == 16) {
+    constexpr int kk = KEXT - 16;
+    bf16x4 av = *reinterpret_cast<const bf16x4*>(a + kk + g * 4);
+    bf16x4 bv = *reinterpret_cast<const bf16x4*>(b + kk + g * 4);
+    typedef __attribute__((ext_vector_type(4))) short s4;
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(s4, av), __builtin_bit_cast(s4, bv), acc, 0, 0, 0);
+  }
+  static_assert(KEXT % 16 == 0, "K extent must be a multiple of 16");
+}
+
+template <int KEXT>
+__device__ __forceinline__ void mma_nt(f32x4& acc, const float* A, int lda,
+                                       const float* Bt, int ldb) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const float* a = A + r * lda + g;
+  const float* b = Bt + r * ldb + g;
+#pragma unroll
+  for (int kk = 0; kk < KEXT; kk += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b[kk], acc, 0, 0, 0);
+  static_assert(KEXT % 4 == 0, "K extent must be a multiple of 4");
+}
+
+// Row (within a 16x16 output tile) of element i held by this lane.
+__device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
+__device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
+
+// ---------------------------------------------------------------------------
+// Wave reductions
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                         0xf, 0xf, false));
+}
+
+// Sum over each row of 16 lanes; every lane of the row receives the row sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+
+// Sum over all 64 lanes; every lane receives the total. The two cross-row
+// steps use the gfx950 row swaps (lane l <-> l^16, l <-> l^32).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, x),
+                                              false, false);
+  x = __builtin_bit_cast(float, s16[0]) + __builtin_bit_cast(float, s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, x),
+                                              false, false);
+  x = __builtin_bit_cast(float, s32[0]) + __builtin_bit_cast(float, s32[1]);
+  return x;
+}
+
+}  // namespace osdn

@@ -1,0 +1,42 @@
+// Host-side argument bundles passed from the C-ABI layer to the kernel
+// launchers. Pointers are device pointers owned by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace osdn {
+
+struct PrecondArgs {
+  int B, H, T, Dk;
+  int bf16;                 // 1: k and ktilde are bf16, 0: fp32
+  const void* k;            // [B,H,T,Dk]
+  const float* beta;        // [B,H,T]
+  const float* r;           // [B,H,T] or null (gate off)
+  float eta;
+  const float* d0;          // [B,H,Dk] or null (ones)
+  void* ktilde;             // [B,H,T,Dk] in the k dtype
+  float* dT;                // [B,H,Dk] or null
+};
+
+struct ChunkArgs {
+  int B, H, T, Dk, Dv, chunk;
+  int bf16;
+  const void* q;            // [B,H,T,Dk]
+  const void* k;            // [B,H,T,Dk]
+  const void* ktilde;       // [B,H,T,Dk]
+  const void* v;            // [B,H,T,Dv]
+  const float* beta;        // [B,H,T]
+  const float* S0;          // [B,H,Dv,Dk] or null
+  float scale;
+  void* o;                  // [B,H,T,Dv]
+  float* ST;                // [B,H,Dv,Dk] or null
+};
+
+// Each returns a hipError_t-compatible code (0 = success) or -1 when the
+// (dims, dtype) combination has no kernel instance.
+int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
+int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
+bool osdn_chunk_supported(int Dk, int chunk, int bf16);
+
+}  // namespace osdn

@@ -1,0 +1,169 @@
+// C ABI of libosdn.so: host-side validation, workspace sizing and the launch
+// sequence. Declarations and the full contract are in include/osdn.h.
+#include "../../include/osdn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace {
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+size_t elem(int dtype) { return dtype == OSDN_BF16 ? 2 : 4; }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool valid() const { return lo != 0 && hi > lo; }
+};
+Range rng(const void* p, size_t bytes) {
+  return Range{(uintptr_t)p, (uintptr_t)p + bytes};
+}
+bool overlap(Range a, Range b) {
+  return a.valid() && b.valid() && a.lo < b.hi && b.lo < a.hi;
+}
+bool same(Range a, Range b) { return a.lo == b.lo && a.hi == b.hi; }
+
+// Outputs must not overlap inputs or each other, except for the exact
+// in-place pairs listed in `allowed` (output index, input index).
+template <int NO, int NI>
+bool aliasing_ok(const Range (&outs)[NO], const Range (&ins)[NI],
+                 const int (*allowed)[2], int nallowed) {
+  for (int i = 0; i < NO; ++i) {
+    for (int j = 0; j < NI; ++j) {
+      if (!overlap(outs[i], ins[j])) continue;
+      bool ok = false;
+      for (int a = 0; a < nallowed; ++a)
+        if (allowed[a][0] == i && allowed[a][1] == j && same(outs[i], ins[j]))
+          ok = true;
+      if (!ok) return false;
+    }
+    for (int j = i + 1; j < NO; ++j)
+      if (overlap(outs[i], outs[j])) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* osdn_strerror(int status) {
+  switch (status) {
+    case OSDN_OK: return "ok";
+    case OSDN_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case OSDN_ERR_BAD_DIMS: return "bad dimensions: B, H and T must be >= 0";
+    case OSDN_ERR_UNSUPPORTED:
+      return "unsupported combination of Dk, Dv, chunk and dtype";
+    case OSDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case OSDN_ERR_ALIASING:
+      return "an output overlaps an input or another output";
+    case OSDN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+  }
+  return "unknown status";
+}
+
+int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype) {
+  if (!dim_ok(Dk) || !dim_ok(Dv) || !chunk_ok(chunk)) return 0;
+  if (dtype != OSDN_F32 && dtype != OSDN_BF16) return 0;
+  return osdn::osdn_chunk_supported(Dk, chunk, dtype == OSDN_BF16) ? 1 : 0;
+}
+
+size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                    int chunk, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
+      !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return 0;
+  return round256((size_t)B * H * T * Dk * elem(dtype));
+}
+
+int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
+                      const float* beta, const float* r, float eta,
+                      const float* d0, void* ktilde, float* d_T,
+                      void* stream) {
+  if (!k || !beta) return OSDN_ERR_NULL_ARG;
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if (!dim_ok(Dk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return OSDN_ERR_UNSUPPORTED;
+  if ((size_t)B * H == 0) return OSDN_OK;
+  const size_t BH = (size_t)B * H, es = elem(dtype);
+  const Range ins[] = {rng(k, BH * T * Dk * es), rng(beta, BH * T * 4),
+                       rng(r, r ? BH * T * 4 : 0), rng(d0, d0 ? BH * Dk * 4 : 0)};
+  const Range outs[] = {rng(ktilde, ktilde ? BH * T * Dk * es : 0),
+                        rng(d_T, d_T ? BH * Dk * 4 : 0)};
+  const int allowed[][2] = {{1, 3}};  // d_T == d0
+  if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
+  osdn::PrecondArgs a{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                      ktilde, d_T};
+  const int rc = osdn::launch_precond_scan(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
+                 const void* q, const void* k, const void* v,
+                 const float* beta, const float* r, float eta,
+                 const float* d0, const float* S0, float scale, void* o,
+                 float* S_T, float* d_T, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !beta || !o) return OSDN_ERR_NULL_ARG;
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if (!osdn_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
+  const size_t need = osdn_forward_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
+  if ((size_t)B * H == 0) return OSDN_OK;
+
+  const size_t BH = (size_t)B * H, es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(beta, BH * T * 4),
+                       rng(r, r ? BH * T * 4 : 0), rng(d0, d0 ? BH * Dk * 4 : 0),
+                       rng(S0, S0 ? BH * Dv * Dk * 4 : 0)};
+  const Range outs[] = {rng(o, BH * T * Dv * es),
+                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0),
+                        rng(d_T, d_T ? BH * Dk * 4 : 0),
+                        rng(workspace, need)};
+  const int allowed[][2] = {{1, 6}, {2, 5}};  // S_T == S0, d_T == d0
+  if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
+
+  hipStream_t s = (hipStream_t)stream;
+  osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                       workspace, d_T};
+  int rc = osdn::launch_precond_scan(pa, s);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  if (rc != 0) return OSDN_ERR_HIP;
+  osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                     workspace, v, beta, S0, scale, o, S_T};
+  rc = osdn::launch_osdn_chunk(ca, s);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
+                       int dtype, const void* q, const void* k,
+                       const void* ktilde, const void* v, const float* beta,
+                       const float* S0, float scale, void* o, float* S_T,
+                       void* stream) {
+  if (!q || !k || !ktilde || !v || !beta || !o) return OSDN_ERR_NULL_ARG;
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if (!osdn_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
+  if ((size_t)B * H == 0) return OSDN_OK;
+  const size_t BH = (size_t)B * H, es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(ktilde, BH * T * Dk * es), rng(v, BH * T * Dv * es),
+                       rng(beta, BH * T * 4), rng(S0, S0 ? BH * Dv * Dk * 4 : 0)};
+  const Range outs[] = {rng(o, BH * T * Dv * es),
+                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0)};
+  const int allowed[][2] = {{1, 5}};  // S_T == S0
+  if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
+  osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                     ktilde, v, beta, S0, scale, o, S_T};
+  const int rc = osdn::launch_osdn_chunk(ca, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+}  // extern "C"

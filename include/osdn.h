@@ -1,0 +1,134 @@
+/*
+ * osdn.h - C ABI of the MI355X (gfx950) OSDN / Gated DeltaNet-2 forward library
+ * (libosdn.so).
+ *
+ * Method sources, cited by page title and section:
+ *  [OSDN-it] "Riepilogo Tecnico: OSDN: Miglioramento della Regola Delta con
+ *            Precondizionamento Online Provabile nell'Attenzione Lineare"
+ *            (gist.science/it/paper/2605.13473), sections 2.1-2.3.
+ *  [GDN2-it] "Riepilogo Tecnico: Gated DeltaNet-2"
+ *            (gist.science/it/paper/2605.22791), method parts 1-3.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller, contiguous, row-major, in the layouts stated below. The library
+ *    allocates nothing and keeps no global mutable state; calls are reentrant.
+ *  - Inputs are read-only. Outputs are fully overwritten.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued asynchronously; the call returns without synchronising, so a
+ *    device-side fault surfaces at the caller's next synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    non-zero status means nothing was launched (except OSDN_ERR_HIP, returned
+ *    when the HIP runtime rejects a launch).
+ *  - Non-finite inputs are not checked; they propagate within their own
+ *    (batch, head) stream only.
+ *  - Supported sizes: Dk, Dv in {32, 64, 128}; chunk in {16, 32, 64};
+ *    B, H, T >= 0 (any T: a last chunk shorter than `chunk` is handled;
+ *    T = 0 returns the initial state; B*H = 0 enqueues nothing). The fp32 path
+ *    additionally needs the chunk working set to fit in one compute unit's LDS
+ *    (see osdn_forward_supported); otherwise OSDN_ERR_UNSUPPORTED.
+ */
+#ifndef OSDN_H_
+#define OSDN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of q, k, v (and b, w for GDN-2) and of the output o. */
+enum { OSDN_F32 = 0, OSDN_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  OSDN_OK = 0,
+  OSDN_ERR_NULL_ARG = 1,     /* a required pointer is NULL                */
+  OSDN_ERR_BAD_DIMS = 2,     /* B, H or T negative                        */
+  OSDN_ERR_UNSUPPORTED = 3,  /* Dk, Dv, chunk or dtype has no kernel      */
+  OSDN_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required   */
+  OSDN_ERR_ALIASING = 5,     /* partial overlap of an input and an output */
+  OSDN_ERR_HIP = 6           /* the HIP runtime rejected a launch         */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* osdn_strerror(int status);
+
+/* 1 if (Dk, Dv, chunk, dtype) has a kernel instance on this build, else 0. */
+int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype);
+
+/*
+ * Device workspace, in bytes, that osdn_forward needs for these sizes
+ * (0 if the sizes are invalid or the call needs none). The workspace holds the preconditioned keys
+ * produced by phase 1 ([B,H,T,Dk] in the storage dtype) and is only valid
+ * for the duration of one call.
+ */
+size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                    int chunk, int dtype);
+
+/*
+ * OSDN forward: phase 1 (preconditioner scan) then phase 2 (chunked WY delta
+ * rule with K~ = d*k in the chunk Gram matrix and intra-chunk scores).
+ *
+ * Per (batch b, head h), tokens t = 1..T ([OSDN-it] 2.1-2.3):
+ *   a = k_t*k_t, n = ||k_t||^2, c = <d_t, a>, k~_t = d_t*k_t
+ *   S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k~_t^T
+ *   o_t = scale * S_t q_t                        (after the token-t update)
+ *   d_{t+1} = r_t d_t + eta beta_t (1 - beta_t c)/n * a   (0 step if n = 0)
+ * i.e. online gradient descent on h_t(d) = ((1 - beta<d,k^2>)^2 - 1)/(2||k||^2)
+ * with the forgetting gate r (r = 1 when r is NULL).
+ *
+ *   q, k     [B,H,T,Dk]  dtype            (required)
+ *   v        [B,H,T,Dv]  dtype            (required)
+ *   beta     [B,H,T]     fp32             (required)
+ *   r        [B,H,T]     fp32             (NULL: no forgetting gate)
+ *   eta      scalar step size of the preconditioner learner
+ *   d0       [B,H,Dk]    fp32             (NULL: all ones)
+ *   S0       [B,H,Dv,Dk] fp32             (NULL: zeros)
+ *   scale    readout scale (1.0 is the plain reading)
+ *   o        [B,H,T,Dv]  dtype            (required)
+ *   S_T      [B,H,Dv,Dk] fp32 final state (NULL: not written)
+ *   d_T      [B,H,Dk]    fp32 preconditioner after the last token (NULL: not
+ *                        written)
+ *   workspace / workspace_bytes: device scratch of at least
+ *            osdn_forward_workspace_bytes(...) bytes, 256-byte aligned.
+ * S_T may be exactly S0 and d_T exactly d0 (in-place state update); any other
+ * overlap between an output and an input returns OSDN_ERR_ALIASING.
+ */
+int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
+                 const void* q, const void* k, const void* v,
+                 const float* beta, const float* r, float eta,
+                 const float* d0, const float* S0, float scale,
+                 void* o, float* S_T, float* d_T,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Phase 1 alone ([OSDN-it] 2.2, first phase of the two-phase implementation):
+ * writes the preconditioned keys k~_t = d_t*k_t ([B,H,T,Dk], dtype; NULL: not
+ * written) and d_T ([B,H,Dk] fp32; NULL: not written). Reads only k, beta, r,
+ * eta and d0, with the same meaning and layout as in osdn_forward. Needs no
+ * workspace.
+ */
+int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
+                      const float* beta, const float* r, float eta,
+                      const float* d0, void* ktilde, float* d_T, void* stream);
+
+/*
+ * Phase 2 alone ([OSDN-it] 2.1-2.2, second phase): the chunkwise WY delta rule
+ * with caller-supplied write keys, S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t)
+ * ktilde_t^T, o_t = scale * S_t q_t. ktilde is [B,H,T,Dk] in the storage dtype
+ * (for OSDN, the output of osdn_precond_scan; ktilde == k gives plain
+ * DeltaNet). Other arguments as in osdn_forward; ktilde is an input and must
+ * not overlap any output. Needs no workspace.
+ */
+int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
+                       int dtype, const void* q, const void* k,
+                       const void* ktilde, const void* v, const float* beta,
+                       const float* S0, float scale, void* o, float* S_T,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSDN_H_ */

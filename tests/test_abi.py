@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+headers declare, and rejects bad arguments on the host before any launch.
+
+Every call here fails host-side validation, so no HIP work is enqueued.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import delta_rule_recurrent_scan_amd as osdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = osdn.library_path()
+
+OK, NULL_ARG, BAD_DIMS, UNSUPPORTED, WORKSPACE, ALIASING, HIP = range(7)
+
+needs_lib = pytest.mark.skipif(not os.path.exists(LIB),
+                               reason="libosdn.so not built")
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*"
+                            r"([a-z][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("osdn_forward", "osdn_forward_workspace_bytes", "osdn_strerror",
+              "osdn_forward_supported", "osdn_precond_scan"):
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\S+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, "declared but not exported: %s" % missing
+    L = osdn.load_library()
+    for n in declared_functions():
+        assert hasattr(L, n)
+
+
+@needs_lib
+def test_strerror():
+    L = osdn.load_library()
+    for s in range(7):
+        assert L.osdn_strerror(s)
+    assert L.osdn_strerror(99) == b"unknown status"
+
+
+@needs_lib
+def test_supported_and_workspace_sizes():
+    L = osdn.load_library()
+    for dk in (32, 64, 128):
+        for dv in (32, 64, 128):
+            for c in (16, 32, 64):
+                assert L.osdn_forward_supported(dk, dv, c, 1) == 1
+    assert L.osdn_forward_supported(32, 32, 16, 0) == 1
+    assert L.osdn_forward_supported(48, 32, 16, 1) == 0
+    assert L.osdn_forward_supported(32, 32, 8, 1) == 0
+    assert L.osdn_forward_supported(32, 32, 16, 7) == 0
+    assert L.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
+        4 * 16 * 4096 * 128 * 2
+    assert L.osdn_forward_workspace_bytes(1, 1, 3, 32, 32, 16, 0) == 512
+    assert L.osdn_forward_workspace_bytes(-1, 1, 3, 32, 32, 16, 0) == 0
+
+
+def _fwd(L, B=1, H=1, T=64, Dk=32, Dv=32, C=16, dt=1, q=0x10000, k=0x20000,
+         v=0x30000, beta=0x40000, r=None, d0=None, S0=None, o=0x50000,
+         ST=None, dT=None, ws=0x100000, wsb=1 << 20):
+    P = ctypes.c_void_p
+    L.osdn_forward.argtypes = ([ctypes.c_int] * 7 +
+                               [P, P, P, P, P, ctypes.c_float, P, P,
+                                ctypes.c_float, P, P, P, P, ctypes.c_size_t, P])
+    return L.osdn_forward(B, H, T, Dk, Dv, C, dt, q, k, v, beta, r, 0.1, d0,
+                          S0, 1.0, o, ST, dT, ws, wsb, None)
+
+
+@needs_lib
+def test_error_paths_are_host_side():
+    L = osdn.load_library()
+    assert _fwd(L, q=None) == NULL_ARG
+    assert _fwd(L, beta=None) == NULL_ARG
+    assert _fwd(L, o=None) == NULL_ARG
+    assert _fwd(L, T=-1) == BAD_DIMS
+    assert _fwd(L, B=-2) == BAD_DIMS
+    assert _fwd(L, Dk=48) == UNSUPPORTED
+    assert _fwd(L, C=8) == UNSUPPORTED
+    assert _fwd(L, dt=5) == UNSUPPORTED
+    assert _fwd(L, ws=None) == WORKSPACE
+    assert _fwd(L, wsb=100) == WORKSPACE
+    assert _fwd(L, ws=0x100010) == WORKSPACE          # not 256-byte aligned
+    # o overlapping v; S_T overlapping q; workspace overlapping k
+    assert _fwd(L, o=0x30000 + 64) == ALIASING
+    assert _fwd(L, ST=0x10000 + 8) == ALIASING
+    assert _fwd(L, ws=0x20000) == ALIASING
+    # partial overlap of S_T with S0 is rejected (exact aliasing would pass)
+    assert _fwd(L, S0=0x200000, ST=0x200000 + 4) == ALIASING
+    assert _fwd(L, d0=0x300000, dT=0x300000 + 4) == ALIASING
+
+
+@needs_lib
+def test_precond_scan_error_paths():
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    L.osdn_precond_scan.argtypes = [ctypes.c_int] * 5 + [P, P, P, ctypes.c_float,
+                                                         P, P, P, P]
+    assert L.osdn_precond_scan(1, 1, 8, 32, 1, None, 0x1000, None, 0.1, None,
+                               None, None, None) == NULL_ARG
+    assert L.osdn_precond_scan(1, 1, -8, 32, 1, 0x1000, 0x2000, None, 0.1,
+                               None, None, None, None) == BAD_DIMS
+    assert L.osdn_precond_scan(1, 1, 8, 40, 1, 0x1000, 0x2000, None, 0.1,
+                               None, None, None, None) == UNSUPPORTED
+    assert L.osdn_precond_scan(1, 1, 8, 32, 1, 0x1000, 0x2000, None, 0.1,
+                               None, 0x1000 + 16, None, None) == ALIASING
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(osdn, "_lib", None)
+    monkeypatch.setattr(osdn, "_LIB_PATH", "/nonexistent/libosdn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        osdn.load_library()
