@@ -99,19 +99,28 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Sum over all 64 lanes; every lane receives the total. The two cross-row
-// steps use the gfx950 row swaps (lane l <-> l^16, l <-> l^32).
+// x + (x of lane l^16): rows 0/1 and 2/3 exchange their values.
+// (The two results of the swap are read into scalars before the bit cast: a
+// bit cast applied directly to an element of the returned vector reads
+// element 0.)
+__device__ __forceinline__ float add_swap16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned lo = s[0], hi = s[1];
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
+// x + (x of lane l^32): the two 32-lane halves exchange their values.
+__device__ __forceinline__ float add_swap32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned lo = s[0], hi = s[1];
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
+// Sum over all 64 lanes; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float x) {
-  x = row16_sum(x);
-  auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
-                                              __builtin_bit_cast(unsigned, x),
-                                              false, false);
-  x = __builtin_bit_cast(float, s16[0]) + __builtin_bit_cast(float, s16[1]);
-  auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                              __builtin_bit_cast(unsigned, x),
-                                              false, false);
-  x = __builtin_bit_cast(float, s32[0]) + __builtin_bit_cast(float, s32[1]);
-  return x;
+  return add_swap32(add_swap16(row16_sum(x)));
 }
 
 }  // namespace osdn

@@ -83,8 +83,9 @@ int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
                       const float* beta, const float* r, float eta,
                       const float* d0, void* ktilde, float* d_T,
                       void* stream) {
-  if (!k || !beta) return OSDN_ERR_NULL_ARG;
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  // Pointers of zero-size tensors may be NULL.
+  if ((size_t)B * H * T > 0 && (!k || !beta)) return OSDN_ERR_NULL_ARG;
   if (!dim_ok(Dk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
     return OSDN_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return OSDN_OK;
@@ -108,8 +109,9 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  const float* d0, const float* S0, float scale, void* o,
                  float* S_T, float* d_T, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !beta || !o) return OSDN_ERR_NULL_ARG;
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if ((size_t)B * H * T > 0 && (!q || !k || !v || !beta || !o))
+    return OSDN_ERR_NULL_ARG;
   if (!osdn_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
   const size_t need = osdn_forward_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need ||
@@ -147,8 +149,9 @@ int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
                        const void* ktilde, const void* v, const float* beta,
                        const float* S0, float scale, void* o, float* S_T,
                        void* stream) {
-  if (!q || !k || !ktilde || !v || !beta || !o) return OSDN_ERR_NULL_ARG;
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if ((size_t)B * H * T > 0 && (!q || !k || !ktilde || !v || !beta || !o))
+    return OSDN_ERR_NULL_ARG;
   if (!osdn_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return OSDN_OK;
   const size_t BH = (size_t)B * H, es = elem(dtype);

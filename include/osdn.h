@@ -13,7 +13,8 @@
  *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
  *    caller, contiguous, row-major, in the layouts stated below. The library
  *    allocates nothing and keeps no global mutable state; calls are reentrant.
- *  - Inputs are read-only. Outputs are fully overwritten.
+ *  - Inputs are read-only. Outputs are fully overwritten. Pointers marked
+ *    "required" may be NULL only when the tensor has no elements (B*H*T = 0).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
  *    enqueued asynchronously; the call returns without synchronising, so a
  *    device-side fault surfaces at the caller's next synchronisation.
