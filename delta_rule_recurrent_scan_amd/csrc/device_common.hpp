@@ -118,6 +118,33 @@ __device__ __forceinline__ float add_swap32(float x) {
   return __uint_as_float(lo) + __uint_as_float(hi);
 }
 
+// Sum over aligned groups of L consecutive lanes (L = 2, 4, ..., 64); every
+// lane of a group receives the group's sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(L == 2 || L == 4 || L == 8 || L == 16 || L == 32 || L == 64,
+                "group size");
+  x += dpp_f<0xB1>(x);
+  if constexpr (L >= 4) x += dpp_f<0x4E>(x);
+  if constexpr (L >= 8) x += dpp_f<0x141>(x);
+  if constexpr (L >= 16) x += dpp_f<0x140>(x);
+  if constexpr (L >= 32) x = add_swap16(x);
+  if constexpr (L >= 64) x = add_swap32(x);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets the sum of
+// lanes 0..l), by log-step shuffles.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // Sum over all 64 lanes; every lane receives the total.
 __device__ __forceinline__ float wave_sum(float x) {
   return add_swap32(add_swap16(row16_sum(x)));
