@@ -13,6 +13,7 @@ import os
 import torch
 
 __all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
+           "gdn2_forward",
            "workspace_bytes", "supported",
            "OsdnError", "library_path", "load_library"]
 
@@ -59,6 +60,10 @@ def load_library():
     L.osdn_precond_scan.restype = I
     L.osdn_chunk_forward.argtypes = [I] * 7 + [P, P, P, P, P, P, F, P, P, P]
     L.osdn_chunk_forward.restype = I
+    L.gdn2_forward_supported.argtypes = [I, I, I, I]
+    L.gdn2_forward_supported.restype = I
+    L.gdn2_forward.argtypes = [I] * 7 + [P, P, P, P, P, P, P, F, P, P, P]
+    L.gdn2_forward.restype = I
     _lib = L
     return L
 
@@ -192,4 +197,38 @@ def osdn_chunk_forward(q, k, ktilde, v, beta, S0=None, chunk=64, scale=1.0,
                               _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_chunk_forward")
+    return o, S_T
+
+
+def gdn2_forward(q, k, v, log_alpha, b, w, S0=None, chunk=64, scale=1.0,
+                 out=None):
+    """Gated DeltaNet-2 forward on the GPU: returns (o, S_T).
+
+    q, k, b: [B,H,T,Dk]; v, w: [B,H,T,Dv] (one dtype, fp32 or bf16);
+    log_alpha: [B,H,T,Dk] fp32; S0: [B,H,Dk,Dv] fp32 (None: zeros).
+    """
+    L = load_library()
+    dev = q.device
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (b, "b")):
+        _check(t, n, (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(w, "w", (B, H, T, Dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, Dk), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dk, Dv), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    else:
+        o, S_T = out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    _check(S_T, "S_T", (B, H, Dk, Dv), torch.float32, dev)
+    rc = L.gdn2_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt], _ptr(q),
+                        _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                        _ptr(S0), float(scale), _ptr(o), _ptr(S_T),
+                        _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "gdn2_forward")
     return o, S_T

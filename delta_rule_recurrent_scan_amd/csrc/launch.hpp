@@ -19,24 +19,32 @@ struct PrecondArgs {
   float* dT;                // [B,H,Dk] or null
 };
 
+// Arguments of the chunked WY engine. OSDN uses ktilde and beta, with the
+// state stored [B,H,Dv,Dk]; GDN-2 uses log_alpha, b and w, with the state
+// stored [B,H,Dk,Dv].
 struct ChunkArgs {
   int B, H, T, Dk, Dv, chunk;
   int bf16;
   const void* q;            // [B,H,T,Dk]
   const void* k;            // [B,H,T,Dk]
-  const void* ktilde;       // [B,H,T,Dk]
+  const void* ktilde;       // OSDN: [B,H,T,Dk]
   const void* v;            // [B,H,T,Dv]
-  const float* beta;        // [B,H,T]
-  const float* S0;          // [B,H,Dv,Dk] or null
+  const float* beta;        // OSDN: [B,H,T]
+  const float* S0;          // or null (zeros)
   float scale;
   void* o;                  // [B,H,T,Dv]
-  float* ST;                // [B,H,Dv,Dk] or null
+  float* ST;                // or null
+  const float* log_alpha;   // GDN-2: [B,H,T,Dk] fp32
+  const void* b;            // GDN-2: [B,H,T,Dk] erase gate
+  const void* w;            // GDN-2: [B,H,T,Dv] write gate
 };
 
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
 // (dims, dtype) combination has no kernel instance.
 int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
+int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int chunk, int bf16);
+bool gdn2_chunk_supported(int Dk, int chunk, int bf16);
 
 }  // namespace osdn

@@ -138,7 +138,8 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   if (rc != 0) return OSDN_ERR_HIP;
   osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                     workspace, v, beta, S0, scale, o, S_T};
+                     workspace, v, beta, S0, scale, o, S_T,
+                     nullptr, nullptr, nullptr};
   rc = osdn::launch_osdn_chunk(ca, s);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
@@ -163,8 +164,41 @@ int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
   const int allowed[][2] = {{1, 5}};  // S_T == S0
   if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
   osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                     ktilde, v, beta, S0, scale, o, S_T};
+                     ktilde, v, beta, S0, scale, o, S_T,
+                     nullptr, nullptr, nullptr};
   const int rc = osdn::launch_osdn_chunk(ca, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+int gdn2_forward_supported(int Dk, int Dv, int chunk, int dtype) {
+  if (!dim_ok(Dk) || !dim_ok(Dv) || !chunk_ok(chunk)) return 0;
+  if (dtype != OSDN_F32 && dtype != OSDN_BF16) return 0;
+  return osdn::gdn2_chunk_supported(Dk, chunk, dtype == OSDN_BF16) ? 1 : 0;
+}
+
+int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
+                 const void* q, const void* k, const void* v,
+                 const float* log_alpha, const void* b, const void* w,
+                 const float* S0, float scale, void* o, float* S_T,
+                 void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if ((size_t)B * H * T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
+    return OSDN_ERR_NULL_ARG;
+  if (!gdn2_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
+  if ((size_t)B * H == 0) return OSDN_OK;
+  const size_t BH = (size_t)B * H, es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(log_alpha, BH * T * Dk * 4),
+                       rng(b, BH * T * Dk * es), rng(w, BH * T * Dv * es),
+                       rng(S0, S0 ? BH * Dv * Dk * 4 : 0)};
+  const Range outs[] = {rng(o, BH * T * Dv * es),
+                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0)};
+  const int allowed[][2] = {{1, 6}};  // S_T == S0
+  if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
+  osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                     nullptr, v, nullptr, S0, scale, o, S_T, log_alpha, b, w};
+  const int rc = osdn::launch_gdn2_chunk(ca, (hipStream_t)stream);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }

@@ -1,20 +1,30 @@
-// Chunkwise WY delta-rule engine (phase 2 of the OSDN forward).
+// Chunkwise WY delta-rule engine: phase 2 of the OSDN forward and the Gated
+// DeltaNet-2 forward.
 //
-// One engine serves every update of the form (state S: Dv x Dk, per chunk of
+// One engine serves every update of the form (state S: Dv x Dk; per chunk of
 // C tokens with entry state S0)
 //   A  = strictLower(diag(rs) Y X^T)          chunk Gram (read keys Y, write keys X)
 //   T  = (I + A)^-1
 //   W  = T diag(rs) (Z - Y S0^T)              row t of W is the token-t write
 //   O  = Q S0^T + (Q X^T masked to i <= t) W  inclusive readout
 //   S1 = S0 diag(g) + W^T X'                  exit state (g: exit decay)
+//
 // OSDN ([OSDN-it] 2.1): Y = K, X = X' = K~ (the preconditioned keys: K~
 // replaces K in the Gram matrix and the intra-chunk scores), Z = V,
-// rs = beta, g = 1. This is the token recurrence
-// S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k~_t^T rewritten exactly.
+// rs = beta, g = 1; the rewrite of S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t)
+// k~_t^T.
+//
+// GDN-2 ([GDN2-it] method, parts 1-3): S_t = (I - k_t e_t^T) Diag(alpha_t)
+// S_{t-1} + k_t z_t^T with e = b*k, z = w*v, state Dk x Dv (handled here as
+// its transpose). With gamma_t = prod_{j<=t} alpha_j inside the chunk the
+// per-channel decay is absorbed into the factors, which leaves an undecayed
+// delta rule with read key y_t = gamma_t*b_t*k_t, write key x_t = k_t/gamma_t,
+// value z_t, query gamma_t*q_t, exit keys x'_t = k_t*gamma_C/gamma_t and exit
+// decay g = gamma_C; rs = 1.
 //
 // Work decomposition: one workgroup (4 waves) per (batch, head, VT-wide value
-// tile), walking the chunks in order; the VT x Dk state slice lives in fp32
-// MFMA accumulators. Value tiles are independent given the keys, so the
+// tile) walks the chunks in order; the VT x Dk state slice lives in fp32 MFMA
+// accumulators. Value tiles are independent given the keys, so the
 // V-independent chunk quantities (A, T, Q X^T) are recomputed per tile rather
 // than written to and re-read from HBM. The next chunk's inputs are fetched
 // into registers while the current chunk computes.
@@ -22,10 +32,15 @@
 // T = (I + A)^-1: 16x16 diagonal blocks by fp32 forward substitution (one
 // lane per column), then recursive doubling, merging pairs of s x s inverses
 // into 2s x 2s ones with T21 = -T22 A21 T11 on MFMA.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace osdn {
+
+struct OsdnVariant {};
+struct Gdn2Variant {};
 
 template <int DK, int C, int VT, typename Tin>
 struct WyCfg {
@@ -37,6 +52,7 @@ struct WyCfg {
   static constexpr int LDY = 32 + PAD;
   static constexpr int TB = C / 16, VB = VT / 16, DB = DK / 16;
   static constexpr int VEC = 16 / sizeof(Tin);
+  static constexpr int NCB = DK / VEC;         // 16-byte blocks per key row
   static constexpr size_t E = sizeof(Tin);
   static constexpr size_t oX = 0;
   static constexpr size_t oY = oX + (size_t)C * LDK * E;
@@ -45,7 +61,8 @@ struct WyCfg {
   static constexpr size_t oS = oXT + (size_t)DK * LDC * E;
   static constexpr size_t oZ = oS + (size_t)VT * LDK * E;
   static constexpr size_t oRS = oZ + (size_t)C * VT * E;
-  static constexpr size_t oA = oRS + (size_t)C * 4;
+  static constexpr size_t oG = oRS + (size_t)C * 4;
+  static constexpr size_t oA = oG + (size_t)DK * 4;
   static constexpr size_t oAb = oA + (size_t)C * LDF * 4;
   static constexpr size_t oTb = oAb + (size_t)C * LDC * E;
   static constexpr size_t oTt = oTb + (size_t)C * LDC * E;
@@ -57,64 +74,85 @@ struct WyCfg {
   static constexpr bool fits = bytes <= 163840;
   static constexpr int NS = (VB * DB + NW - 1) / NW;  // state tiles per wave
   static constexpr int NO = (TB * VB + NW - 1) / NW;  // output tiles per wave
-  // 16-byte vectors per thread for a C x DK and a C x VT chunk
   static constexpr int NLK = (C * DK / VEC + NT - 1) / NT;
   static constexpr int NLV = (C * VT / VEC + NT - 1) / NT;
+  // GDN-2 decay pass: TPC threads per key channel, each over C/TPC tokens
+  static constexpr int TPC = NT / DK;
+  static constexpr int TPT = C / TPC;
 };
 
-// Register-staged inputs of one OSDN chunk (prefetched one chunk ahead).
+struct SmemPtrs {
+  void *X, *Y, *Q, *XT, *Z;
+  float *rs, *g;
+};
+
+// ---------------------------------------------------------------------------
+// Per-variant chunk inputs, fetched into registers one chunk ahead.
+// ---------------------------------------------------------------------------
+template <class V, int DK, int C, int VT, typename Tin>
+struct ChunkRegs;
+
+// OSDN: k (row-major), k~ (one lane per token row, so that its transposed
+// copy is written to consecutive LDS addresses), q, v, beta.
 template <int DK, int C, int VT, typename Tin>
-struct OsdnChunkRegs {
+struct ChunkRegs<OsdnVariant, DK, C, VT, Tin> {
   using G = WyCfg<DK, C, VT, Tin>;
   uint4 k[G::NLK], kt[G::NLK], q[G::NLK], v[G::NLV];
   float beta;
 
-  __device__ __forceinline__ void load(const Tin* __restrict__ kp,
-                                       const Tin* __restrict__ ktp,
-                                       const Tin* __restrict__ qp,
-                                       const Tin* __restrict__ vp,
-                                       const float* __restrict__ bp, size_t t0,
-                                       int valid, int Dv, int v0) {
+  __device__ __forceinline__ void load(const ChunkArgs& p, int bh, size_t t0,
+                                       int valid, int v0) {
+    const Tin* kp = (const Tin*)p.k;
+    const Tin* ktp = (const Tin*)p.ktilde;
+    const Tin* qp = (const Tin*)p.q;
+    const Tin* vp = (const Tin*)p.v;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < G::NLK; ++i) {
       const int e = tid + i * G::NT;
-      const int rr = e / (DK / G::VEC), cc = (e % (DK / G::VEC)) * G::VEC;
-      uint4 z = {0u, 0u, 0u, 0u};
+      const uint4 z = {0u, 0u, 0u, 0u};
       k[i] = z; kt[i] = z; q[i] = z;
-      if (e < C * DK / G::VEC && rr < valid) {
-        const size_t g = (t0 + rr) * DK + cc;
-        k[i] = *reinterpret_cast<const uint4*>(kp + g);
-        kt[i] = *reinterpret_cast<const uint4*>(ktp + g);
-        q[i] = *reinterpret_cast<const uint4*>(qp + g);
+      if (e < C * G::NCB) {
+        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
+        if (rr < valid) {
+          k[i] = *reinterpret_cast<const uint4*>(kp + (t0 + rr) * DK + cc);
+          q[i] = *reinterpret_cast<const uint4*>(qp + (t0 + rr) * DK + cc);
+        }
+        const int tr = e % C, tc = (e / C) * G::VEC;
+        if (tr < valid)
+          kt[i] = *reinterpret_cast<const uint4*>(ktp + (t0 + tr) * DK + tc);
       }
     }
 #pragma unroll
     for (int i = 0; i < G::NLV; ++i) {
       const int e = tid + i * G::NT;
       const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
-      uint4 z = {0u, 0u, 0u, 0u};
-      v[i] = z;
+      v[i] = uint4{0u, 0u, 0u, 0u};
       if (e < C * VT / G::VEC && rr < valid)
-        v[i] = *reinterpret_cast<const uint4*>(vp + (t0 + rr) * Dv + v0 + cc);
+        v[i] = *reinterpret_cast<const uint4*>(vp + (t0 + rr) * p.Dv + v0 + cc);
     }
-    beta = (tid < valid) ? bp[t0 + tid] : 0.f;
+    beta = (tid < valid) ? p.beta[t0 + tid] : 0.f;
   }
 
-  __device__ __forceinline__ void store(Tin* Xs, Tin* Ys, Tin* Qs, Tin* XTt,
-                                        Tin* Zs, float* rs) const {
+  __device__ __forceinline__ void store(const SmemPtrs& s) const {
+    Tin* Xs = (Tin*)s.X;
+    Tin* Ys = (Tin*)s.Y;
+    Tin* Qs = (Tin*)s.Q;
+    Tin* XTt = (Tin*)s.XT;
+    Tin* Zs = (Tin*)s.Z;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < G::NLK; ++i) {
       const int e = tid + i * G::NT;
-      if (e < C * DK / G::VEC) {
-        const int rr = e / (DK / G::VEC), cc = (e % (DK / G::VEC)) * G::VEC;
-        *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = kt[i];
+      if (e < C * G::NCB) {
+        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
         *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = k[i];
         *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
+        const int tr = e % C, tc = (e / C) * G::VEC;
+        *reinterpret_cast<uint4*>(Xs + tr * G::LDK + tc) = kt[i];
         const Tin* te = reinterpret_cast<const Tin*>(&kt[i]);
 #pragma unroll
-        for (int u = 0; u < G::VEC; ++u) XTt[(cc + u) * G::LDC + rr] = te[u];
+        for (int u = 0; u < G::VEC; ++u) XTt[(tc + u) * G::LDC + tr] = te[u];
       }
     }
 #pragma unroll
@@ -125,17 +163,159 @@ struct OsdnChunkRegs {
         *reinterpret_cast<uint4*>(Zs + rr * VT + cc) = v[i];
       }
     }
-    if (tid < C) rs[tid] = beta;
+    if (tid < C) s.rs[tid] = beta;
+  }
+
+  __device__ __forceinline__ void transform(const SmemPtrs&) const {}
+};
+
+// GDN-2: k, q, b staged raw (row-major) into the X, Q, Y buffers, z = w*v,
+// and log alpha held by the threads of the decay pass (TPC threads per key
+// channel, each over a contiguous run of TPT tokens).
+template <int DK, int C, int VT, typename Tin>
+struct ChunkRegs<Gdn2Variant, DK, C, VT, Tin> {
+  using G = WyCfg<DK, C, VT, Tin>;
+  uint4 k[G::NLK], q[G::NLK], b[G::NLK], v[G::NLV], w[G::NLV];
+  float la[G::TPT];
+
+  __device__ __forceinline__ static void chan(int& c, int& part) {
+    // lanes l and l + 64/TPC (within one wave) share a channel
+    constexpr int CPW = 64 / G::TPC;            // channels per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    c = wave * CPW + lane % CPW;
+    part = lane / CPW;
+  }
+
+  __device__ __forceinline__ void load(const ChunkArgs& p, int bh, size_t t0,
+                                       int valid, int v0) {
+    const Tin* kp = (const Tin*)p.k;
+    const Tin* qp = (const Tin*)p.q;
+    const Tin* bp = (const Tin*)p.b;
+    const Tin* vp = (const Tin*)p.v;
+    const Tin* wp = (const Tin*)p.w;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < G::NLK; ++i) {
+      const int e = tid + i * G::NT;
+      const uint4 z = {0u, 0u, 0u, 0u};
+      k[i] = z; q[i] = z; b[i] = z;
+      if (e < C * G::NCB) {
+        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
+        if (rr < valid) {
+          const size_t g = (t0 + rr) * DK + cc;
+          k[i] = *reinterpret_cast<const uint4*>(kp + g);
+          q[i] = *reinterpret_cast<const uint4*>(qp + g);
+          b[i] = *reinterpret_cast<const uint4*>(bp + g);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G::NLV; ++i) {
+      const int e = tid + i * G::NT;
+      const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
+      v[i] = uint4{0u, 0u, 0u, 0u};
+      w[i] = v[i];
+      if (e < C * VT / G::VEC && rr < valid) {
+        const size_t g = (t0 + rr) * p.Dv + v0 + cc;
+        v[i] = *reinterpret_cast<const uint4*>(vp + g);
+        w[i] = *reinterpret_cast<const uint4*>(wp + g);
+      }
+    }
+    int c, part;
+    chan(c, part);
+#pragma unroll
+    for (int m = 0; m < G::TPT; ++m) {
+      const int t = part * G::TPT + m;
+      la[m] = (t < valid) ? p.log_alpha[(t0 + t) * DK + c] : 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void store(const SmemPtrs& s) const {
+    Tin* Xs = (Tin*)s.X;
+    Tin* Ys = (Tin*)s.Y;
+    Tin* Qs = (Tin*)s.Q;
+    Tin* Zs = (Tin*)s.Z;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < G::NLK; ++i) {
+      const int e = tid + i * G::NT;
+      if (e < C * G::NCB) {
+        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
+        *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = k[i];
+        *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
+        *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = b[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G::NLV; ++i) {
+      const int e = tid + i * G::NT;
+      if (e < C * VT / G::VEC) {
+        const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
+        const Tin* vv = reinterpret_cast<const Tin*>(&v[i]);
+        const Tin* ww = reinterpret_cast<const Tin*>(&w[i]);
+        Tin zz[G::VEC];
+#pragma unroll
+        for (int u = 0; u < G::VEC; ++u)
+          zz[u] = from_f32<Tin>(to_f32(ww[u]) * to_f32(vv[u]));
+        *reinterpret_cast<uint4*>(Zs + rr * VT + cc) =
+            *reinterpret_cast<const uint4*>(zz);
+      }
+    }
+    if (tid < C) s.rs[tid] = 1.f;
+  }
+
+  // Decay pass (after the raw operands are in LDS): cumulative log decay per
+  // channel, then X = k/gamma, Y = gamma*b*k, Q = gamma*q in place, the exit
+  // keys X'^T = (k*gamma_C/gamma)^T and the exit decay g = gamma_C.
+  __device__ __forceinline__ void transform(const SmemPtrs& s) const {
+    Tin* Xs = (Tin*)s.X;
+    Tin* Ys = (Tin*)s.Y;
+    Tin* Qs = (Tin*)s.Q;
+    Tin* XTt = (Tin*)s.XT;
+    constexpr int CPW = 64 / G::TPC;
+    int c, part;
+    chan(c, part);
+    // prefix of log alpha: within this thread's run, then across the runs
+    float lam[G::TPT];
+    float run = 0.f;
+#pragma unroll
+    for (int m = 0; m < G::TPT; ++m) {
+      run += la[m];
+      lam[m] = run;
+    }
+    float incl = run;  // inclusive prefix over the runs of this channel
+#pragma unroll
+    for (int d = 1; d < G::TPC; d <<= 1) {
+      const float y = __shfl_up(incl, d * CPW, 64);
+      if (part >= d) incl += y;
+    }
+    const float excl = incl - run;
+    const float total = __shfl(incl, (G::TPC - 1) * CPW + (threadIdx.x & 63) % CPW, 64);
+    const float gC = __expf(total);
+#pragma unroll
+    for (int m = 0; m < G::TPT; ++m) {
+      const int t = part * G::TPT + m;
+      const float l = excl + lam[m];
+      const float gam = __expf(l), igam = __expf(-l);
+      const float kk = to_f32(Xs[t * G::LDK + c]);
+      const float bb = to_f32(Ys[t * G::LDK + c]);
+      const float qq = to_f32(Qs[t * G::LDK + c]);
+      Xs[t * G::LDK + c] = from_f32<Tin>(kk * igam);
+      Ys[t * G::LDK + c] = from_f32<Tin>(gam * bb * kk);
+      Qs[t * G::LDK + c] = from_f32<Tin>(gam * qq);
+      XTt[c * G::LDC + t] = from_f32<Tin>(kk * __expf(total - l));
+    }
+    if (part == 0) s.g[c] = gC;
   }
 };
 
-template <int DK, int C, int VT, typename Tin>
-__global__ __launch_bounds__(256) void osdn_wy_kernel(
-    int T, int Dv, const Tin* __restrict__ q, const Tin* __restrict__ k,
-    const Tin* __restrict__ ktil, const Tin* __restrict__ v,
-    const float* __restrict__ beta, const float* __restrict__ S0, float scale,
-    Tin* __restrict__ o, float* __restrict__ ST) {
+// ---------------------------------------------------------------------------
+// The engine
+// ---------------------------------------------------------------------------
+template <class V, int DK, int C, int VT, typename Tin>
+__global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
   using G = WyCfg<DK, C, VT, Tin>;
+  constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
   constexpr int LDK = G::LDK, LDC = G::LDC, LDF = G::LDF, LDY = G::LDY;
   constexpr int TB = G::TB, VB = G::VB, DB = G::DB;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
@@ -146,6 +326,7 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
   Tin* Ss = reinterpret_cast<Tin*>(smem + G::oS);
   Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);
   float* rs = reinterpret_cast<float*>(smem + G::oRS);
+  float* gC = reinterpret_cast<float*>(smem + G::oG);
   float* Am = reinterpret_cast<float*>(smem + G::oA);
   Tin* Ab = reinterpret_cast<Tin*>(smem + G::oAb);
   Tin* Tb = reinterpret_cast<Tin*>(smem + G::oTb);
@@ -154,7 +335,9 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
   Tin* Pb = reinterpret_cast<Tin*>(smem + G::oP);
   Tin* Rt = reinterpret_cast<Tin*>(smem + G::oR);
   Tin* Wt = reinterpret_cast<Tin*>(smem + G::oW);
+  const SmemPtrs sp{Xs, Ys, Qs, XTt, Zs, rs, gC};
 
+  const int T = p.T, Dv = p.Dv;
   const int nvt = Dv / VT;
   // XCD-aware numbering: workgroups go round-robin over the 8 XCDs; keep all
   // value tiles of one (batch, head) on one XCD so they share its L2.
@@ -166,6 +349,7 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
   const int v0 = vt * VT;
   const size_t row0 = (size_t)bh * T;
   const Tin zero = from_f32<Tin>(0.f);
+  Tin* o = (Tin*)p.o;
 
   // Blocks above the diagonal of T and P (below it for T^T) stay zero.
   for (int e = tid; e < C * C; e += G::NT) {
@@ -177,6 +361,12 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
     }
   }
 
+  // Persistent state slice S[v][dk] (v in this tile), fp32, MFMA layout.
+  // OSDN stores the state [Dv][Dk]; GDN-2 stores it [Dk][Dv].
+  auto sidx = [&](int vv, int kk) -> size_t {
+    return kGdn2 ? ((size_t)bh * DK + kk) * Dv + v0 + vv
+                 : ((size_t)bh * Dv + v0 + vv) * DK + kk;
+  };
   f32x4 Sacc[G::NS];
 #pragma unroll
   for (int s = 0; s < G::NS; ++s) {
@@ -185,9 +375,8 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float x = 0.f;
-      if (job < VB * DB && S0)
-        x = S0[((size_t)bh * Dv + v0 + vb * 16 + acc_row(i)) * DK + db * 16 +
-               acc_col()];
+      if (job < VB * DB && p.S0)
+        x = p.S0[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())];
       Sacc[s][i] = x;
     }
     if (job < VB * DB) {
@@ -199,16 +388,20 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
   }
 
   const int nchunks = (T + C - 1) / C;
-  OsdnChunkRegs<DK, C, VT, Tin> regs;
-  if (nchunks > 0) regs.load(k, ktil, q, v, beta, row0, min(C, T), Dv, v0);
+  ChunkRegs<V, DK, C, VT, Tin> regs;
+  if (nchunks > 0) regs.load(p, bh, row0, min(C, T), v0);
 
   for (int j = 0; j < nchunks; ++j) {
     const size_t t0 = row0 + (size_t)j * C;
     const int valid = min(C, T - j * C);
     // ---- S1: operands of chunk j into LDS; prefetch chunk j+1 -------------
-    regs.store(Xs, Ys, Qs, XTt, Zs, rs);
+    regs.store(sp);
+    if constexpr (kGdn2) {
+      __syncthreads();
+      regs.transform(sp);
+    }
     if (j + 1 < nchunks)
-      regs.load(k, ktil, q, v, beta, t0 + C, min(C, T - (j + 1) * C), Dv, v0);
+      regs.load(p, bh, t0 + C, min(C, T - (j + 1) * C), v0);
     __syncthreads();
 
     // ---- S2: Gram A, scores P, RHS = rs (Z - Y S0^T), Q S0^T --------------
@@ -289,13 +482,13 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
       const int jobs = npair * nt * nt;
       // Y = A21 T11 (s x s, K = s), stored transposed in the scratch.
       for (int job = wave; job < jobs; job += G::NW) {
-        const int p = job / (nt * nt), r = (job / nt) % nt, c = job % nt;
-        const int rb = 2 * s * p + s, cb = 2 * s * p;   // A21 origin
+        const int pp = job / (nt * nt), r = (job / nt) % nt, c = job % nt;
+        const int rb = 2 * s * pp + s, cb = 2 * s * pp;   // A21 origin
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < s; kk += 16)
           mma_nt<16>(acc, Ab + (rb + r * 16) * LDC + cb + kk, LDC,
                      Tt + (cb + c * 16) * LDC + cb + kk, LDC);
-        Tin* ys = Ysc + (p * s) * LDY;
+        Tin* ys = Ysc + (pp * s) * LDY;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           ys[(c * 16 + acc_col()) * LDY + r * 16 + acc_row(i)] = from_f32<Tin>(acc[i]);
@@ -303,9 +496,9 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
       __syncthreads();
       // T21 = -T22 Y
       for (int job = wave; job < jobs; job += G::NW) {
-        const int p = job / (nt * nt), r = (job / nt) % nt, c = job % nt;
-        const int rb = 2 * s * p + s, cb = 2 * s * p;
-        const Tin* ys = Ysc + (p * s) * LDY;
+        const int pp = job / (nt * nt), r = (job / nt) % nt, c = job % nt;
+        const int rb = 2 * s * pp + s, cb = 2 * s * pp;
+        const Tin* ys = Ysc + (pp * s) * LDY;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int kk = 0; kk < s; kk += 16)
           mma_nt<16>(acc, Tb + (rb + r * 16) * LDC + rb + kk, LDC,
@@ -332,7 +525,7 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
     }
     __syncthreads();
 
-    // ---- S6: O += P W (store), S += W^T X ----------------------------------
+    // ---- S6: O += P W (store), S = S diag(g) + W^T X' -----------------------
 #pragma unroll
     for (int s = 0; s < G::NO; ++s) {
       const int job = wave + G::NW * s;
@@ -344,7 +537,7 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
           const int rr = tb * 16 + acc_row(i);
           if (rr < valid)
             o[(t0 + rr) * Dv + v0 + vb * 16 + acc_col()] =
-                from_f32<Tin>(scale * Oacc[s][i]);
+                from_f32<Tin>(p.scale * Oacc[s][i]);
         }
       }
     }
@@ -353,6 +546,11 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
       const int job = wave + G::NW * s;
       if (job < VB * DB) {
         const int vb = job / DB, db = job % DB;
+        if constexpr (kGdn2) {
+          const float gd = gC[db * 16 + acc_col()];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Sacc[s][i] *= gd;
+        }
         mma_nt<C>(Sacc[s], Wt + vb * 16 * LDC, LDC, XTt + db * 16 * LDC, LDC);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -363,7 +561,7 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
     __syncthreads();
   }
 
-  if (ST) {
+  if (p.ST) {
 #pragma unroll
     for (int s = 0; s < G::NS; ++s) {
       const int job = wave + G::NW * s;
@@ -371,24 +569,24 @@ __global__ __launch_bounds__(256) void osdn_wy_kernel(
         const int vb = job / DB, db = job % DB;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ST[((size_t)bh * Dv + v0 + vb * 16 + acc_row(i)) * DK + db * 16 +
-             acc_col()] = Sacc[s][i];
+          p.ST[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())] = Sacc[s][i];
       }
     }
   }
 }
 
-template <int DK, int C, int VT, typename Tin>
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+template <class V, int DK, int C, int VT, typename Tin>
 static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
   if constexpr (!WyCfg<DK, C, VT, Tin>::fits) {
     return -1;
   } else {
     const int BH = a.B * a.H;
     dim3 grid(BH * (a.Dv / VT)), block(256);
-    hipLaunchKernelGGL((osdn_wy_kernel<DK, C, VT, Tin>), grid, block, 0, s,
-                       a.T, a.Dv, (const Tin*)a.q, (const Tin*)a.k,
-                       (const Tin*)a.ktilde, (const Tin*)a.v, a.beta, a.S0,
-                       a.scale, (Tin*)a.o, a.ST);
+    hipLaunchKernelGGL((wy_engine_kernel<V, DK, C, VT, Tin>), grid, block, 0, s,
+                       a);
     return (int)hipGetLastError();
   }
 }
@@ -397,37 +595,46 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
 // compute unit (256 CUs), else 16 for more parallelism.
 static int pick_vt(int BH, int Dv) { return (BH * (Dv / 32) >= 256) ? 32 : 16; }
 
-template <int DK, int C, typename Tin>
+template <class V, int DK, int C, typename Tin>
 static int launch_c(const ChunkArgs& a, hipStream_t s) {
-  if (pick_vt(a.B * a.H, a.Dv) == 32) return launch_cfg<DK, C, 32, Tin>(a, s);
-  return launch_cfg<DK, C, 16, Tin>(a, s);
+  if (pick_vt(a.B * a.H, a.Dv) == 32) return launch_cfg<V, DK, C, 32, Tin>(a, s);
+  return launch_cfg<V, DK, C, 16, Tin>(a, s);
 }
 
-template <int DK, typename Tin>
+template <class V, int DK, typename Tin>
 static int launch_dk(const ChunkArgs& a, hipStream_t s) {
   switch (a.chunk) {
-    case 16: return launch_c<DK, 16, Tin>(a, s);
-    case 32: return launch_c<DK, 32, Tin>(a, s);
-    case 64: return launch_c<DK, 64, Tin>(a, s);
+    case 16: return launch_c<V, DK, 16, Tin>(a, s);
+    case 32: return launch_c<V, DK, 32, Tin>(a, s);
+    case 64: return launch_c<V, DK, 64, Tin>(a, s);
+  }
+  return -1;
+}
+
+template <class V>
+static int launch_variant(const ChunkArgs& a, hipStream_t s) {
+  if (a.bf16) {
+    switch (a.Dk) {
+      case 32: return launch_dk<V, 32, __bf16>(a, s);
+      case 64: return launch_dk<V, 64, __bf16>(a, s);
+      case 128: return launch_dk<V, 128, __bf16>(a, s);
+    }
+  } else {
+    switch (a.Dk) {
+      case 32: return launch_dk<V, 32, float>(a, s);
+      case 64: return launch_dk<V, 64, float>(a, s);
+      case 128: return launch_dk<V, 128, float>(a, s);
+    }
   }
   return -1;
 }
 
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s) {
-  if (a.bf16) {
-    switch (a.Dk) {
-      case 32: return launch_dk<32, __bf16>(a, s);
-      case 64: return launch_dk<64, __bf16>(a, s);
-      case 128: return launch_dk<128, __bf16>(a, s);
-    }
-  } else {
-    switch (a.Dk) {
-      case 32: return launch_dk<32, float>(a, s);
-      case 64: return launch_dk<64, float>(a, s);
-      case 128: return launch_dk<128, float>(a, s);
-    }
-  }
-  return -1;
+  return launch_variant<OsdnVariant>(a, s);
+}
+
+int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s) {
+  return launch_variant<Gdn2Variant>(a, s);
 }
 
 template <int DK, typename Tin>
@@ -455,6 +662,12 @@ bool osdn_chunk_supported(int Dk, int chunk, int bf16) {
     }
   }
   return false;
+}
+
+// The GDN-2 decay pass splits each chunk's tokens over 256/Dk threads per
+// channel, so the chunk must hold at least that many tokens.
+bool gdn2_chunk_supported(int Dk, int chunk, int bf16) {
+  return osdn_chunk_supported(Dk, chunk, bf16) && chunk >= 256 / Dk;
 }
 
 }  // namespace osdn

@@ -8,6 +8,8 @@
  *            (gist.science/it/paper/2605.13473), sections 2.1-2.3.
  *  [GDN2-it] "Riepilogo Tecnico: Gated DeltaNet-2"
  *            (gist.science/it/paper/2605.22791), method parts 1-3.
+ * (The status codes and conventions below apply to the gdn2_* entry points
+ * too.)
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
@@ -127,6 +129,36 @@ int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
                        const void* ktilde, const void* v, const float* beta,
                        const float* S0, float scale, void* o, float* S_T,
                        void* stream);
+
+/* 1 if (Dk, Dv, chunk, dtype) has a GDN-2 kernel instance, else 0. */
+int gdn2_forward_supported(int Dk, int Dv, int chunk, int dtype);
+
+/*
+ * Gated DeltaNet-2 forward ([GDN2-it] method part 1, chunked as in part 3).
+ * Per (batch b, head h), tokens t = 1..T, with state S of shape Dk x Dv:
+ *   S_t = (I - k_t (b_t*k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t*v_t)^T
+ *   o_t = scale * S_t^T q_t                       (after the token-t update)
+ * alpha_t = exp(log_alpha_t) is a per-key-channel decay, b_t the erase gate
+ * (per key channel), w_t the write gate (per value channel).
+ *
+ *   q, k       [B,H,T,Dk] dtype     (required)
+ *   v          [B,H,T,Dv] dtype     (required)
+ *   log_alpha  [B,H,T,Dk] fp32      (required; <= 0 for a decay)
+ *   b          [B,H,T,Dk] dtype     (required)
+ *   w          [B,H,T,Dv] dtype     (required)
+ *   S0         [B,H,Dk,Dv] fp32     (NULL: zeros)
+ *   o          [B,H,T,Dv] dtype     (required)
+ *   S_T        [B,H,Dk,Dv] fp32     (NULL: not written)
+ * Inside a chunk the decay is absorbed into the keys as k / gamma_t with
+ * gamma_t the running product of alpha; the sum of log_alpha over one chunk
+ * must stay above about -80 per channel so that 1/gamma_t is finite in fp32.
+ * S_T may be exactly S0; no other overlap is allowed. Needs no workspace.
+ */
+int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
+                 const void* q, const void* k, const void* v,
+                 const float* log_alpha, const void* b, const void* w,
+                 const float* S0, float scale, void* o, float* S_T,
+                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("osdn_forward", "osdn_forward_workspace_bytes", "osdn_strerror",
-              "osdn_forward_supported", "osdn_precond_scan"):
+              "osdn_forward_supported", "osdn_precond_scan",
+              "osdn_chunk_forward", "gdn2_forward", "gdn2_forward_supported"):
         assert n in names
 
 
@@ -131,3 +132,24 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(osdn, "_LIB_PATH", "/nonexistent/libosdn.so")
     with pytest.raises(RuntimeError, match="not built"):
         osdn.load_library()
+
+
+@needs_lib
+def test_gdn2_error_paths():
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    L.gdn2_forward.argtypes = [ctypes.c_int] * 7 + [P] * 7 + [ctypes.c_float,
+                                                              P, P, P]
+
+    def call(T=64, Dk=32, q=0x10000, la=0x60000, o=0x50000, ST=None, S0=None):
+        return L.gdn2_forward(1, 1, T, Dk, 32, 16, 1, q, 0x20000, 0x30000, la,
+                              0x70000, 0x80000, S0, 1.0, o, ST, None)
+
+    assert call(q=None) == NULL_ARG
+    assert call(la=None) == NULL_ARG
+    assert call(T=-3) == BAD_DIMS
+    assert call(Dk=48) == UNSUPPORTED
+    assert call(o=0x20000 + 128) == ALIASING
+    assert call(S0=0x200000, ST=0x200000 + 8) == ALIASING
+    assert L.gdn2_forward_supported(128, 128, 64, 1) == 1
+    assert L.gdn2_forward_supported(128, 128, 8, 1) == 0
