@@ -29,6 +29,32 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
+_CSRC = os.path.join(ROOT, "delta_rule_recurrent_scan_amd", "csrc")
+_KERNEL_SOURCES = {
+    "osdn_precond_scan": ["precond_scan.hip"],
+    "osdn_chunk": ["wy_chunk.hip"],
+    "gdn2_chunk": ["wy_chunk.hip"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs (scaled by the copy-kernel calibration), or None when
+    they were taken on another workload or on kernel sources that have
+    changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in _KERNEL_SOURCES[kernel] + ["device_common.hpp", "launch.hpp"]:
+        h.update(open(os.path.join(_CSRC, f), "rb").read())
+    if rec.get("source_sha") != h.hexdigest()[:16] or rec.get("workload") != workload:
+        return None
+    return rec["bytes"]
+
 
 def bytes_per_token_head(w, apf):
     """Algorithmic bytes per token-head of each kernel and of the whole path.
@@ -46,9 +72,18 @@ def bytes_per_token_head(w, apf):
 
 
 def flops_per_token_head(w):
-    """Chunk-form flops per token-head of phase 2 (see the design notes)."""
+    """Chunk-form flops per token-head of phase 2: state chain 4 Dk Dv,
+    inter-chunk output 2 Dk Dv, intra-chunk Gram, W and scores
+    2 C (3 Dk + 2 Dv), triangular inverse about C^2 / 3."""
     C, dk, dv = w.chunk, w.Dk, w.Dv
     return 6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3.0
+
+
+def gdn2_bytes_per_token_head(w):
+    """q, k, b (Dk) and v, w (Dv) read in the storage dtype, log alpha (Dk)
+    read in fp32, o (Dv) written."""
+    s = 2 if w.dtype == "bf16" else 4
+    return (3 * w.Dk + 2 * w.Dv) * s + 4 * w.Dk + w.Dv * s
 
 
 def cpu_baseline(w, inp, budget_s=12.0):
@@ -77,23 +112,121 @@ def cpu_baseline(w, inp, budget_s=12.0):
                       "streams" % (done, w.B * w.H, w.T)}
 
 
+def bench_gdn2(args, w, inp, x, dt, dev):
+    """One step = one gdn2_forward launch over the workload."""
+    import delta_rule_recurrent_scan_amd as osdn
+    L = osdn.load_library()
+    P = osdn._ptr
+    o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
+    S_T = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+    code = {torch.float32: 0, torch.bfloat16: 1}[dt]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rc = L.gdn2_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code,
+                            P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]),
+                            P(x["b"]), P(x["w"]), None, 1.0, P(o), P(S_T), sp)
+        if ev is not None:
+            ev[1].record(stream)
+        if rc:
+            raise RuntimeError("launch failed: %s" % L.osdn_strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    th = w.B * w.H * w.T
+    alg = gdn2_bytes_per_token_head(w) * th
+    achieved = alg / (k_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "GDN-2 forward tokens/s + % HBM roofline, H=16 d=128 "
+                  "T=4096, 1 GPU",
+        "value": w.B * w.T / (ms_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T,
+                   "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk},
+        "roofline": {"bound": "hbm", "kernel": "gdn2_chunk",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("gdn2_chunk", w.name)},
+        "kernels_ms": {"gdn2_chunk": k_ms},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_gdn2(w, inp)
+    return rec
+
+
+def cpu_baseline_gdn2(w, inp, budget_s=12.0):
+    from oracle import recurrence as R
+    f = W.to_f64
+    arrs = {k: f(inp[k]) for k in ("q", "k", "v", "log_alpha", "b", "w")}
+    done, t_used = 0, 0.0
+    order = [(b, h) for b in range(w.B) for h in range(w.H)]
+    while done < len(order) and t_used < budget_s:
+        b, h = order[done]
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        R.gdn2_ref(*(arrs[k][sl] for k in ("q", "k", "v", "log_alpha", "b", "w")))
+        t_used += time.perf_counter() - t0
+        done += 1
+    total = t_used / done * w.B * w.H
+    return {"value": w.B * w.T / total, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) streams at full length T=%d, "
+                      "fp64 NumPy token recurrence, one thread; scaled to all "
+                      "streams" % (done, w.B * w.H, w.T)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="osdn-1.3b-apf",
-                    choices=[w.name for w in W.WORKLOADS if w.kind == "osdn"])
+                    choices=[w.name for w in W.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain fp32 scale-by-one kernel over 512 MiB "
+                         "(reads and writes exactly 512 MiB each per step), "
+                         "to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the forward shards over (batch, head) with no exchange; "
-              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(the forward shards over (batch, head) streams with no "
+              "exchange between GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        n = 512 * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        print(json.dumps({"calibration": "fp32 scale copy", "bytes_read": n * 4,
+                          "bytes_written": n * 4, "ms": ms,
+                          "GBs": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+        return
 
     import delta_rule_recurrent_scan_amd as osdn
 
@@ -103,6 +236,9 @@ def main():
     x = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
          for k, v in inp.items()}
     dt = W.torch_dtype(w.dtype)
+    if w.kind == "gdn2":
+        print(json.dumps(bench_gdn2(args, w, inp, x, dt, dev)), flush=True)
+        return
     o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
     S_T = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
     d_T = torch.empty((w.B, w.H, w.Dk), dtype=torch.float32, device=dev)
@@ -173,7 +309,9 @@ def main():
                    "forgetting_gate": apf, "eta": w.eta},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(dom, w.name),
+                     "alg_bytes": kernels[dom]["alg_bytes"]},
         "kernels_ms": {n: kernels[n]["ms"] for n in kernels},
         "path": {"alg_bytes": path_b * th,
                  "hbm_GBs": path_b * th / (ms_step * 1e-3) / 1e9,

@@ -15,7 +15,7 @@ Layout (all arrays are NumPy, any float dtype, widened to float64 exactly):
 * OSDN state S: [B, H, Dv, Dk] (so that the read is S @ k_t); d: [B, H, Dk]
 * GDN-2 state S: [B, H, Dk, Dv] (the read is S^T @ e_t, the output S^T @ q_t)
 
-Readings of points the pages leave open (each is listed in the design notes):
+Readings of points the pages leave open:
 
 * Preconditioner step sign: descent, d_{t+1} = r_t d_t - eta * grad h_t(d_t).
   [OSDN-it] section 2.3 prints a plus sign in front of the gradient, while
