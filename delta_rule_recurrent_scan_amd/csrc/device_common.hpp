@@ -76,6 +76,96 @@ __device__ __forceinline__ void mma_nt(f32x4& acc, const float* A, int lda,
   static_assert(KEXT % 4 == 0, "K extent must be a multiple of 4");
 }
 
+// Operand fragment of a 16 x KEXT tile held in registers, loaded once from
+// LDS (row l%16, k-run chosen by l/16, as in mma_nt) and reusable across
+// several MFMAs.
+template <int KEXT, typename Tin>
+struct Frag;
+
+template <int KEXT>
+struct Frag<KEXT, __bf16> {
+  static constexpr int N32 = KEXT / 32, R16 = (KEXT % 32) / 16;
+  bf16x8 v[N32 > 0 ? N32 : 1];
+  bf16x4 t;
+  __device__ __forceinline__ void load(const __bf16* base, int ld) {
+    const int lane = threadIdx.x & 63;
+    const __bf16* p = base + (lane & 15) * ld;
+    const int g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < N32; ++i)
+      v[i] = *reinterpret_cast<const bf16x8*>(p + 32 * i + g * 8);
+    if constexpr (R16) t = *reinterpret_cast<const bf16x4*>(p + 32 * N32 + g * 4);
+  }
+};
+
+template <int KEXT>
+struct Frag<KEXT, float> {
+  float v[KEXT / 4];
+  __device__ __forceinline__ void load(const float* base, int ld) {
+    const int lane = threadIdx.x & 63;
+    const float* p = base + (lane & 15) * ld + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < KEXT / 4; ++i) v[i] = p[4 * i];
+  }
+};
+
+// B-operand fragment of a KEXT x 16 block stored k-major (row k, 16
+// consecutive n), loaded with the gfx950 LDS transpose read: within each
+// group of 16 lanes, lane s reads 4 consecutive n of row base + s/4 at column
+// 4*(s%4), and receives the 4 consecutive k of column s%16. Two reads give the
+// 8 k of one 16x16x32 step (slots 0-3 and 4-7), matching Frag's k order.
+// `base` points at element (k0, n0); ld is the row stride in elements.
+template <int KEXT>
+__device__ __forceinline__ Frag<KEXT, __bf16> load_frag_kmajor(const __bf16* base,
+                                                               int ld) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  Frag<KEXT, __bf16> f;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, s = lane & 15;
+  const __bf16* p = base + (s >> 2) * ld + 4 * (s & 3);
+#pragma unroll
+  for (int i = 0; i < Frag<KEXT, __bf16>::N32; ++i) {
+    const __bf16* q = p + (32 * i + 8 * g) * ld;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
+    const bf16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 4 * ld));
+    f.v[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  if constexpr (Frag<KEXT, __bf16>::R16) {
+    const __bf16* q = p + (32 * Frag<KEXT, __bf16>::N32 + 4 * g) * ld;
+    f.t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
+  }
+  return f;
+}
+
+// acc += A * B^T from two register fragments.
+template <int KEXT>
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<KEXT, __bf16>& a,
+                                    const Frag<KEXT, __bf16>& b) {
+#pragma unroll
+  for (int i = 0; i < Frag<KEXT, __bf16>::N32; ++i)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[i], b.v[i], acc, 0, 0, 0);
+  if constexpr (Frag<KEXT, __bf16>::R16) {
+    typedef __attribute__((ext_vector_type(4))) short s4;
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        __builtin_bit_cast(s4, a.t), __builtin_bit_cast(s4, b.t), acc, 0, 0, 0);
+  }
+}
+
+template <int KEXT>
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<KEXT, float>& a,
+                                    const Frag<KEXT, float>& b) {
+#pragma unroll
+  for (int i = 0; i < KEXT / 4; ++i)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads (data
+// exchanged between lanes of one wave needs no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // Row (within a 16x16 output tile) of element i held by this lane.
 __device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }

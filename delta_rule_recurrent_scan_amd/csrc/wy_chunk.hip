@@ -62,8 +62,10 @@ struct WyCfg {
   static constexpr size_t oZ = oS + (size_t)VT * LDK * E;
   static constexpr size_t oRS = oZ + (size_t)C * VT * E;
   static constexpr size_t oG = oRS + (size_t)C * 4;
+  // fp32 diagonal 16x16 blocks of A, each stored transposed (column-major)
+  static constexpr int LDD = 20;
   static constexpr size_t oA = oG + (size_t)DK * 4;
-  static constexpr size_t oAb = oA + (size_t)C * LDF * 4;
+  static constexpr size_t oAb = oA + (size_t)TB * 16 * LDD * 4;
   static constexpr size_t oTb = oAb + (size_t)C * LDC * E;
   static constexpr size_t oTt = oTb + (size_t)C * LDC * E;
   static constexpr size_t oYs = oTt + (size_t)C * LDC * E;
@@ -72,8 +74,10 @@ struct WyCfg {
   static constexpr size_t oW = oR + (size_t)VT * LDC * E;
   static constexpr size_t bytes = oW + (size_t)VT * LDC * E;
   static constexpr bool fits = bytes <= 163840;
-  static constexpr int NS = (VB * DB + NW - 1) / NW;  // state tiles per wave
-  static constexpr int NO = (TB * VB + NW - 1) / NW;  // output tiles per wave
+  // State tiles per wave: every value tile times a contiguous run of DPW key
+  // tiles.
+  static constexpr int DPW = (DB + NW - 1) / NW;
+  static constexpr int NS = VB * DPW;
   static constexpr int NLK = (C * DK / VEC + NT - 1) / NT;
   static constexpr int NLV = (C * VT / VEC + NT - 1) / NT;
   // GDN-2 decay pass: TPC threads per key channel, each over C/TPC tokens
@@ -292,18 +296,39 @@ struct ChunkRegs<Gdn2Variant, DK, C, VT, Tin> {
     const float excl = incl - run;
     const float total = __shfl(incl, (G::TPC - 1) * CPW + (threadIdx.x & 63) % CPW, 64);
     const float gC = __expf(total);
+    // Batches of BT tokens: all loads of a batch are issued before its
+    // arithmetic and stores; 1/gamma by the hardware reciprocal.
+    constexpr int BT = G::TPT >= 8 ? 8 : G::TPT;
 #pragma unroll
-    for (int m = 0; m < G::TPT; ++m) {
-      const int t = part * G::TPT + m;
-      const float l = excl + lam[m];
-      const float gam = __expf(l), igam = __expf(-l);
-      const float kk = to_f32(Xs[t * G::LDK + c]);
-      const float bb = to_f32(Ys[t * G::LDK + c]);
-      const float qq = to_f32(Qs[t * G::LDK + c]);
-      Xs[t * G::LDK + c] = from_f32<Tin>(kk * igam);
-      Ys[t * G::LDK + c] = from_f32<Tin>(gam * bb * kk);
-      Qs[t * G::LDK + c] = from_f32<Tin>(gam * qq);
-      XTt[c * G::LDC + t] = from_f32<Tin>(kk * __expf(total - l));
+    for (int m0 = 0; m0 < G::TPT; m0 += BT) {
+      const int tb0 = part * G::TPT + m0;
+      float kk[BT], bb[BT], qq[BT];
+#pragma unroll
+      for (int u = 0; u < BT; ++u) {
+        kk[u] = to_f32(Xs[(tb0 + u) * G::LDK + c]);
+        bb[u] = to_f32(Ys[(tb0 + u) * G::LDK + c]);
+        qq[u] = to_f32(Qs[(tb0 + u) * G::LDK + c]);
+      }
+      Tin xt[BT];
+#pragma unroll
+      for (int u = 0; u < BT; ++u) {
+        const float l = excl + lam[m0 + u];
+        const float gam = __expf(l);
+        const float igam = __builtin_amdgcn_rcpf(gam);
+        Xs[(tb0 + u) * G::LDK + c] = from_f32<Tin>(kk[u] * igam);
+        Ys[(tb0 + u) * G::LDK + c] = from_f32<Tin>(gam * bb[u] * kk[u]);
+        Qs[(tb0 + u) * G::LDK + c] = from_f32<Tin>(gam * qq[u]);
+        xt[u] = from_f32<Tin>(kk[u] * igam * gC);
+      }
+      if constexpr ((BT * sizeof(Tin)) % 16 == 0) {
+#pragma unroll
+        for (int w4 = 0; w4 < (int)(BT * sizeof(Tin) / 16); ++w4)
+          *reinterpret_cast<uint4*>(XTt + c * G::LDC + tb0 + w4 * (16 / sizeof(Tin))) =
+              reinterpret_cast<const uint4*>(xt)[w4];
+      } else {
+#pragma unroll
+        for (int u = 0; u < BT; ++u) XTt[c * G::LDC + tb0 + u] = xt[u];
+      }
     }
     if (part == 0) s.g[c] = gC;
   }
@@ -369,21 +394,24 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
   };
   f32x4 Sacc[G::NS];
 #pragma unroll
-  for (int s = 0; s < G::NS; ++s) {
-    const int job = wave + G::NW * s;
-    const int vb = job / DB, db = job % DB;
+  for (int vb = 0; vb < VB; ++vb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = 0.f;
-      if (job < VB * DB && p.S0)
-        x = p.S0[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())];
-      Sacc[s][i] = x;
-    }
-    if (job < VB * DB) {
+    for (int u = 0; u < G::DPW; ++u) {
+      const int db = wave * G::DPW + u;
+      f32x4& acc = Sacc[vb * G::DPW + u];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
-            from_f32<Tin>(Sacc[s][i]);
+      for (int i = 0; i < 4; ++i) {
+        float x = 0.f;
+        if (db < DB && p.S0)
+          x = p.S0[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())];
+        acc[i] = x;
+      }
+      if (db < DB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
+              from_f32<Tin>(acc[i]);
+      }
     }
   }
 
@@ -404,111 +432,139 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
       regs.load(p, bh, t0 + C, min(C, T - (j + 1) * C), v0);
     __syncthreads();
 
-    // ---- S2: Gram A, scores P, RHS = rs (Z - Y S0^T), Q S0^T --------------
-    constexpr int NL = TB * (TB + 1) / 2;
-    for (int job = wave; job < 2 * NL + TB * VB; job += G::NW) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (job < 2 * NL) {
-        const bool isP = job >= NL;
-        int l = isP ? job - NL : job, a = 0;
-        while (l > a) { l -= a + 1; ++a; }
-        const int b = l;
-        mma_nt<DK>(acc, (isP ? Qs : Ys) + a * 16 * LDK, LDK, Xs + b * 16 * LDK,
-                   LDK);
+    // ---- S2: Gram A, scores P, RHS = rs (Z - Y S0^T), Q S0^T; diagonal
+    // blocks of T. Wave w owns the 16-row block w: its read-key and query
+    // fragments stay in registers across all tiles of the row.
+    f32x4 Oacc[VB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = a * 16 + acc_row(i), cc = b * 16 + acc_col();
-          if (isP) {
-            Pb[rr * LDC + cc] = from_f32<Tin>(cc <= rr ? acc[i] : 0.f);
+    for (int vb = 0; vb < VB; ++vb) Oacc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave < TB) {
+      const int rb = wave;
+      Frag<DK, Tin> fy, fq;
+      fy.load(Ys + rb * 16 * LDK, LDK);
+      fq.load(Qs + rb * 16 * LDK, LDK);
+      float rsr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rsr[i] = rs[rb * 16 + acc_row(i)];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if (b <= rb) {
+          Frag<DK, Tin> fx;
+          fx.load(Xs + b * 16 * LDK, LDK);
+          f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+          mma(aa, fy, fx);
+          mma(pa, fq, fx);
+          if (b < rb) {
+            // off-diagonal tile: operand copy for the doubling merges
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rr = rb * 16 + acc_row(i), cc = b * 16 + acc_col();
+              Ab[rr * LDC + cc] = from_f32<Tin>(rsr[i] * aa[i]);
+              Pb[rr * LDC + cc] = from_f32<Tin>(pa[i]);
+            }
           } else {
-            const float x = cc < rr ? rs[rr] * acc[i] : 0.f;
-            Am[rr * LDF + cc] = x;
-            Ab[rr * LDC + cc] = from_f32<Tin>(x);
+            // diagonal tile: fp32, transposed, strictly lower part only
+            float4 col;
+            col.x = acc_row(0) > acc_col() ? rsr[0] * aa[0] : 0.f;
+            col.y = acc_row(1) > acc_col() ? rsr[1] * aa[1] : 0.f;
+            col.z = acc_row(2) > acc_col() ? rsr[2] * aa[2] : 0.f;
+            col.w = acc_row(3) > acc_col() ? rsr[3] * aa[3] : 0.f;
+            *reinterpret_cast<float4*>(Am + (rb * 16 + acc_col()) * G::LDD +
+                                       acc_row(0)) = col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rr = rb * 16 + acc_row(i), cc = b * 16 + acc_col();
+              Pb[rr * LDC + cc] = from_f32<Tin>(cc <= rr ? pa[i] : 0.f);
+            }
           }
         }
-      } else {
-        const int l = job - 2 * NL, tb = l / VB, vb = l % VB;
-        mma_nt<DK>(acc, Ys + tb * 16 * LDK, LDK, Ss + vb * 16 * LDK, LDK);
+      }
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        Frag<DK, Tin> fs;
+        fs.load(Ss + vb * 16 * LDK, LDK);
+        f32x4 ka = {0.f, 0.f, 0.f, 0.f};
+        mma(ka, fy, fs);
+        mma(Oacc[vb], fq, fs);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = tb * 16 + acc_row(i), cc = vb * 16 + acc_col();
+          const int rr = rb * 16 + acc_row(i), cc = vb * 16 + acc_col();
           Rt[cc * LDC + rr] =
-              from_f32<Tin>(rs[rr] * (to_f32(Zs[rr * VT + cc]) - acc[i]));
+              from_f32<Tin>(rsr[i] * (to_f32(Zs[rr * VT + cc]) - ka[i]));
         }
       }
-    }
-    f32x4 Oacc[G::NO];
+      // Diagonal block rb of T = (I + A)^-1 by fp32 forward substitution:
+      // lane c < 16 owns column c; pending sums are updated as soon as each
+      // entry is final, so the dependent chain is 15 FMAs long. Column m of
+      // the block is read as four broadcast 16-byte loads. The block was
+      // written by this wave, so only a wave-level LDS ordering is needed.
+      wave_lds_sync();
+      if (lane < 16) {
+        const int c = lane;
+        const float* Acol = Am + rb * 16 * G::LDD;
+        float x[16], sv[16];
 #pragma unroll
-    for (int s = 0; s < G::NO; ++s) {
-      Oacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int job = wave + G::NW * s;
-      if (job < TB * VB) {
-        const int tb = job / VB, vb = job % VB;
-        mma_nt<DK>(Oacc[s], Qs + tb * 16 * LDK, LDK, Ss + vb * 16 * LDK, LDK);
-      }
-    }
-    __syncthreads();
-
-    // ---- S3: diagonal 16x16 blocks of T, fp32 forward substitution --------
-    // Wave b < TB solves block b; lane c < 16 owns column c. Pending sums are
-    // updated as soon as each entry is final, so the dependent chain is 15
-    // FMAs long.
-    if (wave < TB && lane < 16) {
-      const int b = wave, c = lane;
-      const float* Ablk = Am + b * 16 * LDF + b * 16;
-      float x[16], s[16];
+        for (int i = 0; i < 16; ++i) sv[i] = (i == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = (i == c) ? 1.f : 0.f;
+        for (int m = 0; m < 16; ++m) {
+          x[m] = sv[m];
+          float col[16];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        x[m] = s[m];
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(Acol + m * G::LDD + 4 * q4);
+            col[4 * q4] = v4.x; col[4 * q4 + 1] = v4.y;
+            col[4 * q4 + 2] = v4.z; col[4 * q4 + 3] = v4.w;
+          }
 #pragma unroll
-        for (int i = m + 1; i < 16; ++i) s[i] -= Ablk[i * LDF + m] * x[m];
-      }
+          for (int i = m + 1; i < 16; ++i) sv[i] -= col[i] * x[m];
+        }
+        Tin xt[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const Tin xv = from_f32<Tin>(x[i]);
-        Tb[(b * 16 + i) * LDC + b * 16 + c] = xv;
-        Tt[(b * 16 + c) * LDC + b * 16 + i] = xv;
+        for (int i = 0; i < 16; ++i) {
+          xt[i] = from_f32<Tin>(x[i]);
+          Tb[(rb * 16 + i) * LDC + rb * 16 + c] = xt[i];
+        }
+        // row c of the transposed block is contiguous
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tt[(rb * 16 + c) * LDC + rb * 16 + i] = xt[i];
       }
     }
     __syncthreads();
 
     // ---- S4: recursive doubling, T21 = -T22 (A21 T11) ----------------------
+    // One job = one 16-wide column of T21 in one pair: the wave computes that
+    // column of Y = A21 T11 (into the scratch) and then the same column of
+    // T21 = -T22 Y, so the two stages need no barrier between them.
 #pragma unroll
     for (int s = 16; s < C; s *= 2) {
-      const int npair = C / (2 * s);
-      const int nt = s / 16;                 // tiles per side of an s x s block
-      const int jobs = npair * nt * nt;
-      // Y = A21 T11 (s x s, K = s), stored transposed in the scratch.
+      const int nt = s / 16;
+      const int jobs = (C / (2 * s)) * nt;
       for (int job = wave; job < jobs; job += G::NW) {
-        const int pp = job / (nt * nt), r = (job / nt) % nt, c = job % nt;
-        const int rb = 2 * s * pp + s, cb = 2 * s * pp;   // A21 origin
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < s; kk += 16)
-          mma_nt<16>(acc, Ab + (rb + r * 16) * LDC + cb + kk, LDC,
-                     Tt + (cb + c * 16) * LDC + cb + kk, LDC);
-        Tin* ys = Ysc + (pp * s) * LDY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ys[(c * 16 + acc_col()) * LDY + r * 16 + acc_row(i)] = from_f32<Tin>(acc[i]);
-      }
-      __syncthreads();
-      // T21 = -T22 Y
-      for (int job = wave; job < jobs; job += G::NW) {
-        const int pp = job / (nt * nt), r = (job / nt) % nt, c = job % nt;
+        const int pp = job / nt, c = job % nt;
         const int rb = 2 * s * pp + s, cb = 2 * s * pp;
-        const Tin* ys = Ysc + (pp * s) * LDY;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < s; kk += 16)
-          mma_nt<16>(acc, Tb + (rb + r * 16) * LDC + rb + kk, LDC,
-                     ys + (c * 16) * LDY + kk, LDY);
+        Tin* ys = Ysc + (pp * s) * LDY;
+        for (int r = 0; r < nt; ++r) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int kk = 0; kk < s; kk += 16)
+            mma_nt<16>(acc, Ab + (rb + r * 16) * LDC + cb + kk, LDC,
+                       Tt + (cb + c * 16) * LDC + cb + kk, LDC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = rb + r * 16 + acc_row(i), cc = cb + c * 16 + acc_col();
-          const Tin xv = from_f32<Tin>(-acc[i]);
-          Tb[rr * LDC + cc] = xv;
-          Tt[cc * LDC + rr] = xv;
+          for (int i = 0; i < 4; ++i)
+            ys[(c * 16 + acc_col()) * LDY + r * 16 + acc_row(i)] = from_f32<Tin>(acc[i]);
+        }
+        wave_lds_sync();
+        for (int r = 0; r < nt; ++r) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int kk = 0; kk < s; kk += 16)
+            mma_nt<16>(acc, Tb + (rb + r * 16) * LDC + rb + kk, LDC,
+                       ys + (c * 16) * LDY + kk, LDY);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = rb + r * 16 + acc_row(i), cc = cb + c * 16 + acc_col();
+            const Tin xv = from_f32<Tin>(-acc[i]);
+            Tb[rr * LDC + cc] = xv;
+            Tt[cc * LDC + rr] = xv;
+          }
         }
       }
       __syncthreads();
@@ -526,36 +582,52 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
     __syncthreads();
 
     // ---- S6: O += P W (store), S = S diag(g) + W^T X' -----------------------
+    if (wave < TB) {
+      const int tb = wave;
+      Frag<C, Tin> fp;
+      fp.load(Pb + tb * 16 * LDC, LDC);
 #pragma unroll
-    for (int s = 0; s < G::NO; ++s) {
-      const int job = wave + G::NW * s;
-      if (job < TB * VB) {
-        const int tb = job / VB, vb = job % VB;
-        mma_nt<C>(Oacc[s], Pb + tb * 16 * LDC, LDC, Wt + vb * 16 * LDC, LDC);
+      for (int vb = 0; vb < VB; ++vb) {
+        Frag<C, Tin> fw;
+        fw.load(Wt + vb * 16 * LDC, LDC);
+        mma(Oacc[vb], fp, fw);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = tb * 16 + acc_row(i);
           if (rr < valid)
             o[(t0 + rr) * Dv + v0 + vb * 16 + acc_col()] =
-                from_f32<Tin>(p.scale * Oacc[s][i]);
+                from_f32<Tin>(p.scale * Oacc[vb][i]);
         }
       }
     }
+    // State tiles (vb, db): wave w takes a contiguous run of db for every vb,
+    // so each W^T and X' fragment is loaded once per wave.
+    {
+      constexpr int DPW = G::DPW;
+      Frag<C, Tin> fw[VB];
 #pragma unroll
-    for (int s = 0; s < G::NS; ++s) {
-      const int job = wave + G::NW * s;
-      if (job < VB * DB) {
-        const int vb = job / DB, db = job % DB;
-        if constexpr (kGdn2) {
-          const float gd = gC[db * 16 + acc_col()];
+      for (int vb = 0; vb < VB; ++vb) fw[vb].load(Wt + vb * 16 * LDC, LDC);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Sacc[s][i] *= gd;
+      for (int u = 0; u < DPW; ++u) {
+        const int db = wave * DPW + u;
+        if (db < DB) {
+          Frag<C, Tin> fx;
+          fx.load(XTt + db * 16 * LDC, LDC);
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) {
+            f32x4& acc = Sacc[vb * G::DPW + u];
+            if constexpr (kGdn2) {
+              const float gd = gC[db * 16 + acc_col()];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[i] *= gd;
+            }
+            mma(acc, fw[vb], fx);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
+                  from_f32<Tin>(acc[i]);
+          }
         }
-        mma_nt<C>(Sacc[s], Wt + vb * 16 * LDC, LDC, XTt + db * 16 * LDC, LDC);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
-              from_f32<Tin>(Sacc[s][i]);
       }
     }
     __syncthreads();
@@ -563,13 +635,16 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
 
   if (p.ST) {
 #pragma unroll
-    for (int s = 0; s < G::NS; ++s) {
-      const int job = wave + G::NW * s;
-      if (job < VB * DB) {
-        const int vb = job / DB, db = job % DB;
+    for (int vb = 0; vb < VB; ++vb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p.ST[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())] = Sacc[s][i];
+      for (int u = 0; u < G::DPW; ++u) {
+        const int db = wave * G::DPW + u;
+        if (db < DB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            p.ST[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())] =
+                Sacc[vb * G::DPW + u][i];
+        }
       }
     }
   }
