@@ -96,6 +96,29 @@ struct Frag<KEXT, __bf16> {
       v[i] = *reinterpret_cast<const bf16x8*>(p + 32 * i + g * 8);
     if constexpr (R16) t = *reinterpret_cast<const bf16x4*>(p + 32 * N32 + g * 4);
   }
+  // The same fragment of the transpose of a KEXT x 16 block stored k-major
+  // (row k holds 16 consecutive n), by the gfx950 LDS transpose read: within
+  // each group of 16 lanes, lane s reads 4 consecutive n of row s/4 (plus the
+  // group's row offset) at column 4*(s%4), and receives 4 consecutive k of
+  // column s%16. Two reads give the 8 k of one 16x16x32 step in Frag's k
+  // order. `base` points at element (k0, n0); ld is the row stride.
+  __device__ __forceinline__ void load_kmajor(const __bf16* base, int ld) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, s = lane & 15;
+    const __bf16* p = base + (s >> 2) * ld + 4 * (s & 3);
+#pragma unroll
+    for (int i = 0; i < N32; ++i) {
+      const __bf16* q = p + (32 * i + 8 * g) * ld;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 4 * ld));
+      v[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if constexpr (R16)
+      t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(p + (32 * N32 + 4 * g) * ld));
+  }
 };
 
 template <int KEXT>
@@ -107,36 +130,15 @@ struct Frag<KEXT, float> {
 #pragma unroll
     for (int i = 0; i < KEXT / 4; ++i) v[i] = p[4 * i];
   }
-};
-
-// B-operand fragment of a KEXT x 16 block stored k-major (row k, 16
-// consecutive n), loaded with the gfx950 LDS transpose read: within each
-// group of 16 lanes, lane s reads 4 consecutive n of row base + s/4 at column
-// 4*(s%4), and receives the 4 consecutive k of column s%16. Two reads give the
-// 8 k of one 16x16x32 step (slots 0-3 and 4-7), matching Frag's k order.
-// `base` points at element (k0, n0); ld is the row stride in elements.
-template <int KEXT>
-__device__ __forceinline__ Frag<KEXT, __bf16> load_frag_kmajor(const __bf16* base,
-                                                               int ld) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  Frag<KEXT, __bf16> f;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, s = lane & 15;
-  const __bf16* p = base + (s >> 2) * ld + 4 * (s & 3);
+  // Transpose of a KEXT x 16 block stored k-major: lane l takes column l%16
+  // of rows 4i + l/16.
+  __device__ __forceinline__ void load_kmajor(const float* base, int ld) {
+    const int lane = threadIdx.x & 63;
+    const float* p = base + (lane >> 4) * ld + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < Frag<KEXT, __bf16>::N32; ++i) {
-    const __bf16* q = p + (32 * i + 8 * g) * ld;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
-    const bf16x4 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 4 * ld));
-    f.v[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int i = 0; i < KEXT / 4; ++i) v[i] = p[4 * i * ld];
   }
-  if constexpr (Frag<KEXT, __bf16>::R16) {
-    const __bf16* q = p + (32 * Frag<KEXT, __bf16>::N32 + 4 * g) * ld;
-    f.t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
-  }
-  return f;
-}
+};
 
 // acc += A * B^T from two register fragments.
 template <int KEXT>

@@ -48,8 +48,8 @@ struct WyCfg {
   static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
   static constexpr int LDK = DK + PAD;
   static constexpr int LDC = C + PAD;
-  static constexpr int LDF = C + 4;
-  static constexpr int LDY = 32 + PAD;
+  static constexpr int LDR = VT + PAD;         // rows of R and W ([C][VT])
+  static constexpr int LDS16 = 16 + PAD;       // doubling scratch ([C/2][16])
   static constexpr int TB = C / 16, VB = VT / 16, DB = DK / 16;
   static constexpr int VEC = 16 / sizeof(Tin);
   static constexpr int NCB = DK / VEC;         // 16-byte blocks per key row
@@ -57,8 +57,7 @@ struct WyCfg {
   static constexpr size_t oX = 0;
   static constexpr size_t oY = oX + (size_t)C * LDK * E;
   static constexpr size_t oQ = oY + (size_t)C * LDK * E;
-  static constexpr size_t oXT = oQ + (size_t)C * LDK * E;
-  static constexpr size_t oS = oXT + (size_t)DK * LDC * E;
+  static constexpr size_t oS = oQ + (size_t)C * LDK * E;
   static constexpr size_t oZ = oS + (size_t)VT * LDK * E;
   static constexpr size_t oRS = oZ + (size_t)C * VT * E;
   static constexpr size_t oG = oRS + (size_t)C * 4;
@@ -67,12 +66,11 @@ struct WyCfg {
   static constexpr size_t oA = oG + (size_t)DK * 4;
   static constexpr size_t oAb = oA + (size_t)TB * 16 * LDD * 4;
   static constexpr size_t oTb = oAb + (size_t)C * LDC * E;
-  static constexpr size_t oTt = oTb + (size_t)C * LDC * E;
-  static constexpr size_t oYs = oTt + (size_t)C * LDC * E;
-  static constexpr size_t oP = oYs + (size_t)32 * LDY * E;
+  static constexpr size_t oYs = oTb + (size_t)C * LDC * E;
+  static constexpr size_t oP = oYs + (size_t)NW * (C / 2) * LDS16 * E;
   static constexpr size_t oR = oP + (size_t)C * LDC * E;
-  static constexpr size_t oW = oR + (size_t)VT * LDC * E;
-  static constexpr size_t bytes = oW + (size_t)VT * LDC * E;
+  static constexpr size_t oW = oR + (size_t)C * LDR * E;
+  static constexpr size_t bytes = oW + (size_t)C * LDR * E;
   static constexpr bool fits = bytes <= 163840;
   // State tiles per wave: every value tile times a contiguous run of DPW key
   // tiles.
@@ -86,7 +84,7 @@ struct WyCfg {
 };
 
 struct SmemPtrs {
-  void *X, *Y, *Q, *XT, *Z;
+  void *X, *Y, *Q, *Z;
   float *rs, *g;
 };
 
@@ -96,8 +94,7 @@ struct SmemPtrs {
 template <class V, int DK, int C, int VT, typename Tin>
 struct ChunkRegs;
 
-// OSDN: k (row-major), k~ (one lane per token row, so that its transposed
-// copy is written to consecutive LDS addresses), q, v, beta.
+// OSDN: k, k~, q (row-major [C][Dk]), v, beta.
 template <int DK, int C, int VT, typename Tin>
 struct ChunkRegs<OsdnVariant, DK, C, VT, Tin> {
   using G = WyCfg<DK, C, VT, Tin>;
@@ -119,12 +116,11 @@ struct ChunkRegs<OsdnVariant, DK, C, VT, Tin> {
       if (e < C * G::NCB) {
         const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
         if (rr < valid) {
-          k[i] = *reinterpret_cast<const uint4*>(kp + (t0 + rr) * DK + cc);
-          q[i] = *reinterpret_cast<const uint4*>(qp + (t0 + rr) * DK + cc);
+          const size_t g = (t0 + rr) * DK + cc;
+          k[i] = *reinterpret_cast<const uint4*>(kp + g);
+          q[i] = *reinterpret_cast<const uint4*>(qp + g);
+          kt[i] = *reinterpret_cast<const uint4*>(ktp + g);
         }
-        const int tr = e % C, tc = (e / C) * G::VEC;
-        if (tr < valid)
-          kt[i] = *reinterpret_cast<const uint4*>(ktp + (t0 + tr) * DK + tc);
       }
     }
 #pragma unroll
@@ -142,7 +138,6 @@ struct ChunkRegs<OsdnVariant, DK, C, VT, Tin> {
     Tin* Xs = (Tin*)s.X;
     Tin* Ys = (Tin*)s.Y;
     Tin* Qs = (Tin*)s.Q;
-    Tin* XTt = (Tin*)s.XT;
     Tin* Zs = (Tin*)s.Z;
     const int tid = threadIdx.x;
 #pragma unroll
@@ -152,11 +147,7 @@ struct ChunkRegs<OsdnVariant, DK, C, VT, Tin> {
         const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
         *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = k[i];
         *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
-        const int tr = e % C, tc = (e / C) * G::VEC;
-        *reinterpret_cast<uint4*>(Xs + tr * G::LDK + tc) = kt[i];
-        const Tin* te = reinterpret_cast<const Tin*>(&kt[i]);
-#pragma unroll
-        for (int u = 0; u < G::VEC; ++u) XTt[(tc + u) * G::LDC + tr] = te[u];
+        *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = kt[i];
       }
     }
 #pragma unroll
@@ -269,13 +260,12 @@ struct ChunkRegs<Gdn2Variant, DK, C, VT, Tin> {
   }
 
   // Decay pass (after the raw operands are in LDS): cumulative log decay per
-  // channel, then X = k/gamma, Y = gamma*b*k, Q = gamma*q in place, the exit
-  // keys X'^T = (k*gamma_C/gamma)^T and the exit decay g = gamma_C.
+  // channel, then X = k/gamma, Y = gamma*b*k, Q = gamma*q in place, and the
+  // exit decay g = gamma_C (the exit keys are X' = X diag(g)).
   __device__ __forceinline__ void transform(const SmemPtrs& s) const {
     Tin* Xs = (Tin*)s.X;
     Tin* Ys = (Tin*)s.Y;
     Tin* Qs = (Tin*)s.Q;
-    Tin* XTt = (Tin*)s.XT;
     constexpr int CPW = 64 / G::TPC;
     int c, part;
     chan(c, part);
@@ -309,7 +299,6 @@ struct ChunkRegs<Gdn2Variant, DK, C, VT, Tin> {
         bb[u] = to_f32(Ys[(tb0 + u) * G::LDK + c]);
         qq[u] = to_f32(Qs[(tb0 + u) * G::LDK + c]);
       }
-      Tin xt[BT];
 #pragma unroll
       for (int u = 0; u < BT; ++u) {
         const float l = excl + lam[m0 + u];
@@ -318,16 +307,6 @@ struct ChunkRegs<Gdn2Variant, DK, C, VT, Tin> {
         Xs[(tb0 + u) * G::LDK + c] = from_f32<Tin>(kk[u] * igam);
         Ys[(tb0 + u) * G::LDK + c] = from_f32<Tin>(gam * bb[u] * kk[u]);
         Qs[(tb0 + u) * G::LDK + c] = from_f32<Tin>(gam * qq[u]);
-        xt[u] = from_f32<Tin>(kk[u] * igam * gC);
-      }
-      if constexpr ((BT * sizeof(Tin)) % 16 == 0) {
-#pragma unroll
-        for (int w4 = 0; w4 < (int)(BT * sizeof(Tin) / 16); ++w4)
-          *reinterpret_cast<uint4*>(XTt + c * G::LDC + tb0 + w4 * (16 / sizeof(Tin))) =
-              reinterpret_cast<const uint4*>(xt)[w4];
-      } else {
-#pragma unroll
-        for (int u = 0; u < BT; ++u) XTt[c * G::LDC + tb0 + u] = xt[u];
       }
     }
     if (part == 0) s.g[c] = gC;
@@ -341,13 +320,12 @@ template <class V, int DK, int C, int VT, typename Tin>
 __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
   using G = WyCfg<DK, C, VT, Tin>;
   constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
-  constexpr int LDK = G::LDK, LDC = G::LDC, LDF = G::LDF, LDY = G::LDY;
+  constexpr int LDK = G::LDK, LDC = G::LDC, LDR = G::LDR, LDS16 = G::LDS16;
   constexpr int TB = G::TB, VB = G::VB, DB = G::DB;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
   Tin* Xs = reinterpret_cast<Tin*>(smem + G::oX);
   Tin* Ys = reinterpret_cast<Tin*>(smem + G::oY);
   Tin* Qs = reinterpret_cast<Tin*>(smem + G::oQ);
-  Tin* XTt = reinterpret_cast<Tin*>(smem + G::oXT);
   Tin* Ss = reinterpret_cast<Tin*>(smem + G::oS);
   Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);
   float* rs = reinterpret_cast<float*>(smem + G::oRS);
@@ -355,12 +333,11 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
   float* Am = reinterpret_cast<float*>(smem + G::oA);
   Tin* Ab = reinterpret_cast<Tin*>(smem + G::oAb);
   Tin* Tb = reinterpret_cast<Tin*>(smem + G::oTb);
-  Tin* Tt = reinterpret_cast<Tin*>(smem + G::oTt);
   Tin* Ysc = reinterpret_cast<Tin*>(smem + G::oYs);
   Tin* Pb = reinterpret_cast<Tin*>(smem + G::oP);
-  Tin* Rt = reinterpret_cast<Tin*>(smem + G::oR);
-  Tin* Wt = reinterpret_cast<Tin*>(smem + G::oW);
-  const SmemPtrs sp{Xs, Ys, Qs, XTt, Zs, rs, gC};
+  Tin* Rm = reinterpret_cast<Tin*>(smem + G::oR);
+  Tin* Wm = reinterpret_cast<Tin*>(smem + G::oW);
+  const SmemPtrs sp{Xs, Ys, Qs, Zs, rs, gC};
 
   const int T = p.T, Dv = p.Dv;
   const int nvt = Dv / VT;
@@ -376,13 +353,12 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
   const Tin zero = from_f32<Tin>(0.f);
   Tin* o = (Tin*)p.o;
 
-  // Blocks above the diagonal of T and P (below it for T^T) stay zero.
+  // Blocks above the diagonal of T and P stay zero.
   for (int e = tid; e < C * C; e += G::NT) {
     const int rr = e / C, cc = e % C;
     if ((cc >> 4) > (rr >> 4)) {
       Tb[rr * LDC + cc] = zero;
       Pb[rr * LDC + cc] = zero;
-      Tt[cc * LDC + rr] = zero;
     }
   }
 
@@ -489,7 +465,7 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = rb * 16 + acc_row(i), cc = vb * 16 + acc_col();
-          Rt[cc * LDC + rr] =
+          Rm[rr * LDR + cc] =
               from_f32<Tin>(rsr[i] * (to_f32(Zs[rr * VT + cc]) - ka[i]));
         }
       }
@@ -518,66 +494,71 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
 #pragma unroll
           for (int i = m + 1; i < 16; ++i) sv[i] -= col[i] * x[m];
         }
-        Tin xt[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          xt[i] = from_f32<Tin>(x[i]);
-          Tb[(rb * 16 + i) * LDC + rb * 16 + c] = xt[i];
-        }
-        // row c of the transposed block is contiguous
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Tt[(rb * 16 + c) * LDC + rb * 16 + i] = xt[i];
+        for (int i = 0; i < 16; ++i)
+          Tb[(rb * 16 + i) * LDC + rb * 16 + c] = from_f32<Tin>(x[i]);
       }
     }
     __syncthreads();
 
     // ---- S4: recursive doubling, T21 = -T22 (A21 T11) ----------------------
     // One job = one 16-wide column of T21 in one pair: the wave computes that
-    // column of Y = A21 T11 (into the scratch) and then the same column of
-    // T21 = -T22 Y, so the two stages need no barrier between them.
+    // column of Y = A21 T11 (into its own scratch, row-major) and then the
+    // same column of T21 = -T22 Y, so the two stages need no barrier between
+    // them. The right operands (T11, Y) are read k-major.
+    {
+      Tin* ys = Ysc + wave * (C / 2) * LDS16;
 #pragma unroll
-    for (int s = 16; s < C; s *= 2) {
-      const int nt = s / 16;
-      const int jobs = (C / (2 * s)) * nt;
-      for (int job = wave; job < jobs; job += G::NW) {
-        const int pp = job / nt, c = job % nt;
-        const int rb = 2 * s * pp + s, cb = 2 * s * pp;
-        Tin* ys = Ysc + (pp * s) * LDY;
-        for (int r = 0; r < nt; ++r) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          for (int kk = 0; kk < s; kk += 16)
-            mma_nt<16>(acc, Ab + (rb + r * 16) * LDC + cb + kk, LDC,
-                       Tt + (cb + c * 16) * LDC + cb + kk, LDC);
+      for (int s = 16; s < C; s *= 2) {
+        const int nt = s / 16;
+        const int jobs = (C / (2 * s)) * nt;
+        for (int job = wave; job < jobs; job += G::NW) {
+          const int pp = job / nt, c = job % nt;
+          const int rb = 2 * s * pp + s, cb = 2 * s * pp;
+          for (int r = 0; r < nt; ++r) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < s; kk += 16) {
+              Frag<16, Tin> fa, fb;
+              fa.load(Ab + (rb + r * 16) * LDC + cb + kk, LDC);
+              fb.load_kmajor(Tb + (cb + kk) * LDC + cb + c * 16, LDC);
+              mma(acc, fa, fb);
+            }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ys[(c * 16 + acc_col()) * LDY + r * 16 + acc_row(i)] = from_f32<Tin>(acc[i]);
-        }
-        wave_lds_sync();
-        for (int r = 0; r < nt; ++r) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          for (int kk = 0; kk < s; kk += 16)
-            mma_nt<16>(acc, Tb + (rb + r * 16) * LDC + rb + kk, LDC,
-                       ys + (c * 16) * LDY + kk, LDY);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = rb + r * 16 + acc_row(i), cc = cb + c * 16 + acc_col();
-            const Tin xv = from_f32<Tin>(-acc[i]);
-            Tb[rr * LDC + cc] = xv;
-            Tt[cc * LDC + rr] = xv;
+            for (int i = 0; i < 4; ++i)
+              ys[(r * 16 + acc_row(i)) * LDS16 + acc_col()] = from_f32<Tin>(acc[i]);
           }
+          wave_lds_sync();
+          for (int r = 0; r < nt; ++r) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < s; kk += 16) {
+              Frag<16, Tin> fa, fb;
+              fa.load(Tb + (rb + r * 16) * LDC + rb + kk, LDC);
+              fb.load_kmajor(ys + kk * LDS16, LDS16);
+              mma(acc, fa, fb);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              Tb[(rb + r * 16 + acc_row(i)) * LDC + cb + c * 16 + acc_col()] =
+                  from_f32<Tin>(-acc[i]);
+          }
+          // the scratch is rewritten by this wave's next job
+          wave_lds_sync();
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
 
-    // ---- S5: W = T RHS, stored transposed ---------------------------------
+    // ---- S5: W = T RHS (row-major [C][VT]) --------------------------------
     for (int job = wave; job < TB * VB; job += G::NW) {
       const int tb = job / VB, vb = job % VB;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma_nt<C>(acc, Tb + tb * 16 * LDC, LDC, Rt + vb * 16 * LDC, LDC);
+      Frag<C, Tin> ft, fr;
+      ft.load(Tb + tb * 16 * LDC, LDC);
+      fr.load_kmajor(Rm + vb * 16, LDR);
+      mma(acc, ft, fr);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        Wt[(vb * 16 + acc_col()) * LDC + tb * 16 + acc_row(i)] = from_f32<Tin>(acc[i]);
+        Wm[(tb * 16 + acc_row(i)) * LDR + vb * 16 + acc_col()] = from_f32<Tin>(acc[i]);
     }
     __syncthreads();
 
@@ -589,7 +570,7 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         Frag<C, Tin> fw;
-        fw.load(Wt + vb * 16 * LDC, LDC);
+        fw.load_kmajor(Wm + vb * 16, LDR);
         mma(Oacc[vb], fp, fw);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -601,27 +582,29 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
       }
     }
     // State tiles (vb, db): wave w takes a contiguous run of db for every vb,
-    // so each W^T and X' fragment is loaded once per wave.
+    // so each W^T and X fragment is loaded once per wave; both are read
+    // k-major (token rows) from their row-major tiles. GDN-2 applies the exit
+    // decay after the product: g (S + W^T X) = S diag(g) + W^T X'.
     {
       constexpr int DPW = G::DPW;
       Frag<C, Tin> fw[VB];
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) fw[vb].load(Wt + vb * 16 * LDC, LDC);
+      for (int vb = 0; vb < VB; ++vb) fw[vb].load_kmajor(Wm + vb * 16, LDR);
 #pragma unroll
       for (int u = 0; u < DPW; ++u) {
         const int db = wave * DPW + u;
         if (db < DB) {
           Frag<C, Tin> fx;
-          fx.load(XTt + db * 16 * LDC, LDC);
+          fx.load_kmajor(Xs + db * 16, LDK);
 #pragma unroll
           for (int vb = 0; vb < VB; ++vb) {
             f32x4& acc = Sacc[vb * G::DPW + u];
+            mma(acc, fw[vb], fx);
             if constexpr (kGdn2) {
               const float gd = gC[db * 16 + acc_col()];
 #pragma unroll
               for (int i = 0; i < 4; ++i) acc[i] *= gd;
             }
-            mma(acc, fw[vb], fx);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
