@@ -245,6 +245,8 @@ def main():
     ktil = torch.empty((w.B, w.H, w.T, w.Dk), dtype=dt, device=dev)
     L = osdn.load_library()
     code = {torch.float32: 0, torch.bfloat16: 1}[dt]
+    pws_n = L.osdn_precond_workspace_bytes(w.B, w.H, w.T, w.Dk, code)
+    pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
     P = osdn._ptr
@@ -254,7 +256,7 @@ def main():
             ev[0].record(stream)
         rc = L.osdn_precond_scan(w.B, w.H, w.T, w.Dk, code, P(x["k"]),
                                  P(x["beta"]), P(x["r"]), float(x["eta"]), None,
-                                 P(ktil), P(d_T), sp)
+                                 P(ktil), P(d_T), P(pws), pws.numel(), sp)
         if ev is not None:
             ev[1].record(stream)
         rc |= L.osdn_chunk_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code,

@@ -14,7 +14,7 @@ import torch
 
 __all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
            "gdn2_forward",
-           "workspace_bytes", "supported",
+           "workspace_bytes", "precond_workspace_bytes", "supported",
            "OsdnError", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +56,9 @@ def load_library():
     L.osdn_forward.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, F, P, P, P, P,
                                           Z, P])
     L.osdn_forward.restype = I
-    L.osdn_precond_scan.argtypes = [I, I, I, I, I, P, P, P, F, P, P, P, P]
+    L.osdn_precond_workspace_bytes.argtypes = [I] * 5
+    L.osdn_precond_workspace_bytes.restype = Z
+    L.osdn_precond_scan.argtypes = [I, I, I, I, I, P, P, P, F, P, P, P, P, Z, P]
     L.osdn_precond_scan.restype = I
     L.osdn_chunk_forward.argtypes = [I] * 7 + [P, P, P, P, P, P, F, P, P, P]
     L.osdn_chunk_forward.restype = I
@@ -151,8 +153,18 @@ def osdn_forward(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None, chunk=64,
     return o, S_T, d_T
 
 
-def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True):
-    """Phase 1 alone on the GPU: returns (ktilde or None, d_T)."""
+def precond_workspace_bytes(B, H, T, Dk, dtype):
+    return int(load_library().osdn_precond_workspace_bytes(
+        B, H, T, Dk, _DTYPE_CODE[dtype]))
+
+
+def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True,
+                      out=None, workspace=None):
+    """Phase 1 alone on the GPU: returns (ktilde or None, d_T).
+
+    ``out`` may pass preallocated (ktilde, d_T) (ktilde may be None to skip
+    it) and ``workspace`` a preallocated uint8 device buffer.
+    """
     L = load_library()
     dev = k.device
     B, H, T, Dk = k.shape
@@ -161,11 +173,19 @@ def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True):
     _check(beta, "beta", (B, H, T), torch.float32, dev)
     _check(r, "r", (B, H, T), torch.float32, dev)
     _check(d0, "d0", (B, H, Dk), torch.float32, dev)
-    kt = torch.empty_like(k) if want_ktilde else None
-    d_T = torch.empty((B, H, Dk), dtype=torch.float32, device=dev)
+    if out is None:
+        kt = torch.empty_like(k) if want_ktilde else None
+        d_T = torch.empty((B, H, Dk), dtype=torch.float32, device=dev)
+    else:
+        kt, d_T = out
+    _check(kt, "ktilde", (B, H, T, Dk), dt, dev)
+    _check(d_T, "d_T", (B, H, Dk), torch.float32, dev)
+    need = L.osdn_precond_workspace_bytes(B, H, T, Dk, _DTYPE_CODE[dt])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = L.osdn_precond_scan(B, H, T, Dk, _DTYPE_CODE[dt], _ptr(k), _ptr(beta),
                              _ptr(r), float(eta), _ptr(d0), _ptr(kt), _ptr(d_T),
-                             _stream(dev))
+                             _ptr(workspace), workspace.numel(), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_precond_scan")
     return kt, d_T

@@ -15,8 +15,9 @@ struct PrecondArgs {
   const float* r;           // [B,H,T] or null (gate off)
   float eta;
   const float* d0;          // [B,H,Dk] or null (ones)
-  void* ktilde;             // [B,H,T,Dk] in the k dtype
+  void* ktilde;             // [B,H,T,Dk] in the k dtype, or null
   float* dT;                // [B,H,Dk] or null
+  void* ws;                 // precond_workspace_bytes(...) bytes, 16-byte aligned
 };
 
 // Arguments of the chunked WY engine. OSDN uses ktilde and beta, with the
@@ -42,6 +43,9 @@ struct ChunkArgs {
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
 // (dims, dtype) combination has no kernel instance.
 int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
+// Device scratch of the chunk-parallel phase 1: per chunk, the record
+// {log gate prefix, g, V} and the entry value of d.
+size_t precond_workspace_bytes(int B, int H, int T, int Dk, int bf16);
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int chunk, int bf16);

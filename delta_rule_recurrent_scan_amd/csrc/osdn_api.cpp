@@ -71,33 +71,45 @@ int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype) {
   return osdn::osdn_chunk_supported(Dk, chunk, dtype == OSDN_BF16) ? 1 : 0;
 }
 
+size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) ||
+      (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return 0;
+  return round256(osdn::precond_workspace_bytes(B, H, T, Dk, dtype == OSDN_BF16));
+}
+
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype) {
   if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
       !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
     return 0;
-  return round256((size_t)B * H * T * Dk * elem(dtype));
+  return round256((size_t)B * H * T * Dk * elem(dtype)) +
+         osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
 }
 
 int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
                       const float* beta, const float* r, float eta,
                       const float* d0, void* ktilde, float* d_T,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
   // Pointers of zero-size tensors may be NULL.
   if ((size_t)B * H * T > 0 && (!k || !beta)) return OSDN_ERR_NULL_ARG;
   if (!dim_ok(Dk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
     return OSDN_ERR_UNSUPPORTED;
+  const size_t need = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
   if ((size_t)B * H == 0) return OSDN_OK;
   const size_t BH = (size_t)B * H, es = elem(dtype);
   const Range ins[] = {rng(k, BH * T * Dk * es), rng(beta, BH * T * 4),
                        rng(r, r ? BH * T * 4 : 0), rng(d0, d0 ? BH * Dk * 4 : 0)};
   const Range outs[] = {rng(ktilde, ktilde ? BH * T * Dk * es : 0),
-                        rng(d_T, d_T ? BH * Dk * 4 : 0)};
+                        rng(d_T, d_T ? BH * Dk * 4 : 0), rng(workspace, need)};
   const int allowed[][2] = {{1, 3}};  // d_T == d0
   if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
   osdn::PrecondArgs a{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                      ktilde, d_T};
+                      ktilde, d_T, workspace};
   const int rc = osdn::launch_precond_scan(a, (hipStream_t)stream);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
@@ -132,8 +144,11 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
   if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
 
   hipStream_t s = (hipStream_t)stream;
+  // workspace: the preconditioned keys, then the phase-1 scratch
+  const size_t kt_bytes = round256(BH * T * Dk * es);
+  void* pws = static_cast<unsigned char*>(workspace) + kt_bytes;
   osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                       workspace, d_T};
+                       workspace, d_T, pws};
   int rc = osdn::launch_precond_scan(pa, s);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   if (rc != 0) return OSDN_ERR_HIP;

@@ -1,254 +1,220 @@
 // Phase 1 of the OSDN forward: the preconditioner scan over the key stream,
-// in chunked form.
+// in chunk-parallel form.
 //
 // [OSDN-it] sections 2.2 and 2.3 define, per (batch, head) and token t,
-//   a_t = k_t*k_t, n_t = ||k_t||^2, c_t = <d_t, a_t>, k~_t = d_t * k_t,
-//   g_t = eta beta_t (1 - beta_t c_t) / n_t          (0 when n_t = 0),
+//   a_t = k_t*k_t, n_t = ||k_t||^2, x_t = <d_t, a_t>, k~_t = d_t * k_t,
+//   g_t = eta beta_t (1 - beta_t x_t) / n_t          (0 when n_t = 0),
 //   d_{t+1} = r_t d_t + g_t a_t                       (descent on the closed-form
 //                                                     surrogate, gate r_t).
 // The step is affine in d, so a chunk of C tokens with entry value d0 is
 // solved at once. With P_t = prod_{j<t} r_j (P_0 = 1) inside the chunk,
 //   d_t   = P_t d0 + sum_{i<t} (P_t / P_{i+1}) g_i a_i,
-//   c_t   = P_t <d0, a_t> + sum_{i<t} (P_t / P_{i+1}) g_i <a_i, a_t>,
-// so g solves the unit lower-triangular system (I + M) g = b with
+// and g solves the unit lower-triangular system (I + M) g = b with
 //   M[t][i] = (eta beta_t^2 / n_t) (P_t / P_{i+1}) <a_i, a_t>   (i < t),
-//   b_t     = (eta beta_t / n_t) (1 - beta_t P_t <d0, a_t>).
-// M depends on the keys and gates only, so the Gram matrix and the inverse
-// (I + M)^-1 are computed without d; the serial part per chunk is three
-// matrix-vector products (<d0, a_t>, the inverse applied to b, and the exit
-// value d_C). The preconditioned keys of the chunk follow as
-// K~ = (P d0^T + L A) * K with L[t][i] = (P_t / P_{i+1}) g_i for i < t.
-//
-// One workgroup (4 waves) per (batch, head) walks the chunks in order.
+//   b_t     = e_t - h_t <d0, a_t>,  e_t = eta beta_t / n_t,  h_t = e_t beta_t P_t.
+// With T = (I + M)^-1, g0 = T e and V = T diag(h), and x = A d0 (rows a_t):
+//   g   = g0 - V x,
+//   d_C = P_C d0 + A^T (c * g),   c_i = P_C / P_{i+1},
+//   K~  = (P d0^T + L A) * K,     L[t][i] = (P_t / P_{i+1}) g_i  (i < t).
+// Only the middle line links the chunks. Three kernels:
+//   prep    one workgroup per chunk, all chunks at once: the Gram matrix of
+//           a, M, T, and the chunk record {log P prefix, g0, V};
+//   chain   one workgroup per (batch, head): the serial part, three
+//           matrix-vector products per chunk (x = A d, g = g0 - V x,
+//           d <- P_C d + A^T (c*g)); records d at each chunk entry and g;
+//   ktilde  one workgroup per chunk: K~ from d, g and the keys.
 // Precision: d never passes through bf16. The Gram matrix of a is formed on
 // MFMA from an exact two-term bf16 split of a (a bf16 key squared has a 16-bit
-// significand), the inverse and the chain run in fp32; only the correction
-// term L A of K~, rounded afterwards to the key dtype, uses bf16 operands.
+// significand), T and V are fp32 and the chain runs in fp32; only the
+// correction term L A of K~, rounded afterwards to the key dtype, uses
+// operands in the key dtype.
 #include "device_common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace osdn {
 
-template <int DK, int C, typename Tin>
-struct PcCfg {
-  static constexpr int NW = 4, NT = 256;
-  static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
-  static constexpr int LDK = DK + PAD;      // rows of Dk key elements
-  static constexpr int LDH = DK + 8;        // rows of Dk bf16 elements
-  static constexpr int LDC = C + PAD;       // rows of C operand elements
-  static constexpr int LDF = C + 4;         // rows of C fp32 elements
-  static constexpr int LDY = 32 + 4;        // fp32 merge scratch
-  static constexpr int TB = C / 16, DB = DK / 16;
-  static constexpr int VEC = 16 / sizeof(Tin);
-  static constexpr int NCB = DK / VEC;      // 16-byte column blocks per key row
-  static constexpr int NLK = (C * NCB + NT - 1) / NT;
+constexpr int kPrecondChunk = 64;
+
+template <int DK, typename Tin>
+struct P1Cfg {
+  static constexpr int C = kPrecondChunk, NW = 4, NT = 256, TB = C / 16,
+                       DB = DK / 16;
+  static_assert(C == 64, "one token per lane in the gate prefix");
   static constexpr size_t E = sizeof(Tin);
-  static constexpr size_t oK = 0;
-  static constexpr size_t oAh = oK + (size_t)C * LDK * E;
-  static constexpr size_t oAl = oAh + (size_t)C * LDH * 2;
-  static constexpr size_t oAT = oAl + (size_t)C * LDH * 2;
-  static constexpr size_t oM = oAT + (size_t)DK * LDC * E;
-  static constexpr size_t oT = oM + (size_t)C * LDF * 4;
-  static constexpr size_t oTt = oT + (size_t)C * LDF * 4;
-  static constexpr size_t oY = oTt + (size_t)C * LDF * 4;
-  static constexpr size_t oL = oY + (size_t)32 * LDY * 4;
-  static constexpr size_t oV = oL + (size_t)C * LDC * E;
-  // vectors: n, beta, rho, e, lp (C+4), P (C+4), lambda, b, g (C each);
-  // d0, dn (DK each); per-thread partial norms (NT)
-  static constexpr size_t bytes = oV + (size_t)(9 * C + 8 + 2 * DK + NT) * 4;
-  static constexpr bool fits = bytes <= 163840;
-  // The K~ staging buffer reuses the (no longer needed) split-a buffers.
-  static_assert((size_t)C * LDK * E <= (size_t)2 * C * LDH * 2, "staging");
+  static constexpr int VEC = 16 / sizeof(Tin);
+  static constexpr int NCB = DK / VEC;           // 16-byte blocks per key row
+  static constexpr int NLK = C * NCB / NT;       // key blocks per thread
+  static_assert((C * NCB) % NT == 0, "whole key blocks per thread");
+  // chunk record (fp32): lp_0..lp_C (lp_t = log P_t), g (g0 from prep,
+  // replaced by g in the chain), V (C x C, zero above the diagonal)
+  static constexpr int R_LP = 0, R_G = C + 4, R_V = 2 * C + 4;
+  static constexpr int RS = 2 * C + 4 + C * C;
+  // prep: split squares (bf16), then T and the doubling scratch in their place
+  static constexpr int LDH = DK + 8;
+  static constexpr int LDF = C + 4;
+  static constexpr int LDYS = 16 + 4;
+  static constexpr size_t uSplit = (size_t)2 * C * LDH * 2;
+  static constexpr size_t uT = (size_t)C * LDF * 4 + (size_t)NW * (C / 2) * LDYS * 4;
+  static constexpr size_t pAh = 0, pAl = (size_t)C * LDH * 2;
+  static constexpr size_t pT = 0, pY = (size_t)C * LDF * 4;
+  static constexpr size_t pM = uSplit > uT ? uSplit : uT;
+  static constexpr size_t pVec = pM + (size_t)C * LDF * 4;
+  static constexpr size_t prep_bytes = pVec + (size_t)(C + 4 + 5 * C) * 4;
+  // ktilde: keys (overwritten in place by K~), squares, L
+  static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
+  static constexpr int LDK = DK + PAD, LDC = C + PAD;
+  static constexpr size_t kK = 0, kA = kK + (size_t)C * LDK * E;
+  static constexpr size_t kL = kA + (size_t)C * LDK * E;
+  static constexpr size_t kVec = kL + (size_t)C * LDC * E;
+  static constexpr size_t kt_bytes = kVec + (size_t)(C + 4 + 2 * C + DK) * 4;
+  static_assert(prep_bytes <= 163840 && kt_bytes <= 163840, "LDS");
 };
 
-template <typename Tin>
 __device__ __forceinline__ void split_bf16(float a, __bf16& hi, __bf16& lo) {
   hi = (__bf16)a;
   lo = (__bf16)(a - (float)hi);
 }
 
-template <int DK, int C, typename Tin>
-__global__ __launch_bounds__(256) void precond_chunk_kernel(
-    int T, const Tin* __restrict__ k, const float* __restrict__ beta,
-    const float* __restrict__ r, float eta, const float* __restrict__ d0in,
-    Tin* __restrict__ ktil, float* __restrict__ dT) {
-  using G = PcCfg<DK, C, Tin>;
-  constexpr int LDK = G::LDK, LDH = G::LDH, LDC = G::LDC, LDF = G::LDF,
-                LDY = G::LDY, TB = G::TB, DB = G::DB, VEC = G::VEC;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
-  Tin* Ks = reinterpret_cast<Tin*>(smem + G::oK);
-  __bf16* Ah = reinterpret_cast<__bf16*>(smem + G::oAh);
-  __bf16* Al = reinterpret_cast<__bf16*>(smem + G::oAl);
-  Tin* KTst = reinterpret_cast<Tin*>(smem + G::oAh);   // aliases Ah, Al
-  Tin* ATt = reinterpret_cast<Tin*>(smem + G::oAT);
-  float* Mf = reinterpret_cast<float*>(smem + G::oM);
-  float* Tf = reinterpret_cast<float*>(smem + G::oT);
-  float* Tft = reinterpret_cast<float*>(smem + G::oTt);
-  float* Ysc = reinterpret_cast<float*>(smem + G::oY);
-  Tin* Lb = reinterpret_cast<Tin*>(smem + G::oL);
-  float* nv = reinterpret_cast<float*>(smem + G::oV);
-  float* bev = nv + C;           // beta
-  float* rhov = bev + C;         // eta beta^2 / n
-  float* ev = rhov + C;          // eta beta / n
-  float* lpv = ev + C;           // C + 4 slots: lp[0..C], lp_t = sum_{j<t} log r_j
-  float* Pv = lpv + C + 4;       // C + 4 slots: P_t = exp(lp_t)
-  float* lamv = Pv + C + 4;      // P_C / P_{i+1}
-  float* bvec = lamv + C;
-  float* gv = bvec + C;
-  float* d0v = gv + C;
-  float* dnv = d0v + DK;
-  float* npart = dnv + DK;       // NT partial key norms
+// ---------------------------------------------------------------------------
+// prep: everything of a chunk that does not depend on d
+// ---------------------------------------------------------------------------
+template <int DK, typename Tin>
+__global__ __launch_bounds__(256) void precond_prep_kernel(
+    int T, int nchunks, const Tin* __restrict__ k, const float* __restrict__ beta,
+    const float* __restrict__ r, float eta, float* __restrict__ rec) {
+  using G = P1Cfg<DK, Tin>;
+  constexpr int C = G::C, LDH = G::LDH, LDF = G::LDF, LDYS = G::LDYS,
+                TB = G::TB, VEC = G::VEC, NCB = G::NCB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::prep_bytes];
+  __bf16* Ah = reinterpret_cast<__bf16*>(smem + G::pAh);
+  __bf16* Al = reinterpret_cast<__bf16*>(smem + G::pAl);
+  float* Tf = reinterpret_cast<float*>(smem + G::pT);     // after the Gram
+  float* Ysc = reinterpret_cast<float*>(smem + G::pY);    // after the Gram
+  float* Mf = reinterpret_cast<float*>(smem + G::pM);
+  float* lpv = reinterpret_cast<float*>(smem + G::pVec);  // C + 4
+  float* bev = lpv + C + 4;
+  float* nv = bev + C;
+  float* ev = nv + C;     // eta beta / n
+  float* rho = ev + C;    // eta beta^2 / n
+  float* hv = rho + C;    // rho P
 
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / nchunks, j = blockIdx.x - bh * nchunks;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int NCB = G::NCB;
-  const size_t row0 = (size_t)bh * T;
-  const float* bp = beta + row0;
-  const float* rp = r ? r + row0 : nullptr;
+  const int valid = min(C, T - j * C);
+  const size_t t0 = (size_t)bh * T + (size_t)j * C;
+  float* out = rec + (size_t)blockIdx.x * G::RS;
 
-  for (int c = tid; c < DK; c += G::NT)
-    d0v[c] = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
-  // Upper 16x16 blocks of the inverse (and its transpose's lower blocks)
-  // and of L stay zero.
+  // ---- keys: split squares and row norms; gates --------------------------
+#pragma unroll
+  for (int i = 0; i < G::NLK; ++i) {
+    const int e = tid + i * G::NT;
+    const int rr = e / NCB, cc = (e % NCB) * VEC;
+    uint4 kr = {0u, 0u, 0u, 0u};
+    if (rr < valid) kr = *reinterpret_cast<const uint4*>(k + (t0 + rr) * DK + cc);
+    const Tin* kv = reinterpret_cast<const Tin*>(&kr);
+    __bf16 hi[VEC], lo[VEC];
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      const float x = to_f32(kv[u]);
+      const float a = x * x;
+      part += a;
+      split_bf16(a, hi[u], lo[u]);
+    }
+    if constexpr (VEC == 8) {
+      *reinterpret_cast<uint4*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint4*>(hi);
+      *reinterpret_cast<uint4*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint4*>(lo);
+    } else {
+      *reinterpret_cast<uint2*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint2*>(hi);
+      *reinterpret_cast<uint2*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint2*>(lo);
+    }
+    // the NCB lanes of one row are consecutive and aligned
+    part = group_sum<NCB>(part);
+    if (e % NCB == 0) nv[rr] = part;
+  }
+  if (wave == 0) {
+    // exclusive prefix of log r (r clamped away from 0 so that ratios of
+    // prefixes stay finite); padding tokens have r = 1, beta = 0
+    const float rt = (lane < valid && r) ? r[t0 + lane] : 1.f;
+    const float bt = (lane < valid) ? beta[t0 + lane] : 0.f;
+    const float lr = logf(fmaxf(rt, 1e-30f));
+    const float inc = wave_prefix_sum(lr);
+    lpv[lane] = inc - lr;
+    if (lane == C - 1) lpv[C] = inc;
+    bev[lane] = bt;
+  }
+  __syncthreads();
+
+  // ---- per-token scalars; Gram of a (split bf16 MFMA) ----------------------
+  if (wave == 0) {
+    const int t = lane;
+    const float n = nv[t], bt = bev[t];
+    const float e = n > 0.f ? eta * bt / n : 0.f;
+    ev[t] = e;
+    rho[t] = e * bt;
+    hv[t] = e * bt * expf(lpv[t]);
+  }
+  // Tile list: wave w owns the diagonal tile (w, w) and a share of the
+  // off-diagonal lower tiles, and keeps its accumulators in registers.
+  constexpr int NL = TB * (TB + 1) / 2;
+  constexpr int NJ = 1 + (NL - TB + G::NW - 1) / G::NW;
+  f32x4 gacc[NJ];
+  int gja[NJ], gjb[NJ];
+#pragma unroll
+  for (int s2 = 0; s2 < NJ; ++s2) {
+    int a = -1, b = -1;
+    const int job = wave + G::NW * s2;
+    if (s2 == 0) {
+      if (wave < TB) { a = wave; b = wave; }
+    } else {
+      // off-diagonal tiles in row-major order, dealt round-robin
+      int l = job - G::NW, aa = 1;
+      if (l >= 0) {
+        while (l >= aa) { l -= aa; ++aa; }
+        if (aa < TB) { a = aa; b = l; }
+      }
+    }
+    gja[s2] = a;
+    gjb[s2] = b;
+    gacc[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a >= 0) {
+      Frag<DK, __bf16> ah, al, bh_, bl;
+      ah.load(Ah + a * 16 * LDH, LDH);
+      al.load(Al + a * 16 * LDH, LDH);
+      bh_.load(Ah + b * 16 * LDH, LDH);
+      bl.load(Al + b * 16 * LDH, LDH);
+      mma(gacc[s2], ah, bh_);
+      mma(gacc[s2], ah, bl);
+      mma(gacc[s2], al, bh_);
+    }
+  }
+  __syncthreads();  // the split squares are dead from here on (T reuses them)
+  // M[t][i] = rho_t (P_t / P_{i+1}) <a_i, a_t> for i < t
+#pragma unroll
+  for (int s2 = 0; s2 < NJ; ++s2) {
+    const int a = gja[s2], b = gjb[s2];
+    if (a >= 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = a * 16 + acc_row(i), c = b * 16 + acc_col();
+        Mf[t * LDF + c] =
+            c < t ? rho[t] * __expf(lpv[t] - lpv[c + 1]) * gacc[s2][i] : 0.f;
+      }
+    }
+  }
+  // Blocks of T above the diagonal are zero.
   for (int e = tid; e < C * C; e += G::NT) {
     const int rr = e / C, cc = e % C;
-    if ((cc >> 4) > (rr >> 4)) {
-      Tf[rr * LDF + cc] = 0.f;
-      Tft[cc * LDF + rr] = 0.f;
-    }
-    if (cc >= rr) Lb[rr * LDC + cc] = from_f32<Tin>(0.f);
+    if ((cc >> 4) > (rr >> 4)) Tf[rr * LDF + cc] = 0.f;
   }
 
-  const int nchunks = (T + C - 1) / C;
-  uint4 kr[G::NLK];
-  float br = 0.f, rr_ = 1.f;
-  auto prefetch = [&](int j) {
-    const int valid = min(C, T - j * C);
-    const size_t t0 = row0 + (size_t)j * C;
-#pragma unroll
-    for (int i = 0; i < G::NLK; ++i) {
-      const int e = tid + i * G::NT;
-      const int rr = e % C, cc = (e / C) * VEC;
-      kr[i] = uint4{0u, 0u, 0u, 0u};
-      if (e < C * NCB && rr < valid)
-        kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + rr) * DK + cc);
-    }
-    br = (tid < valid) ? bp[(size_t)j * C + tid] : 0.f;
-    rr_ = (tid < valid && rp) ? rp[(size_t)j * C + tid] : 1.f;
-  };
-  if (nchunks > 0) prefetch(0);
-
-  for (int j = 0; j < nchunks; ++j) {
-    const int valid = min(C, T - j * C);
-    const size_t t0 = row0 + (size_t)j * C;
-    // ---- A: keys, squares (split), transposed squares, norms, gates ------
-    // Each lane owns one token row, so the transposed writes of a from
-    // consecutive lanes land in consecutive LDS addresses.
-    {
-      float part = 0.f;
-#pragma unroll
-      for (int i = 0; i < G::NLK; ++i) {
-        const int e = tid + i * G::NT;
-        if (e < C * NCB) {
-          const int rr = e % C, cc = (e / C) * VEC;
-          *reinterpret_cast<uint4*>(Ks + rr * LDK + cc) = kr[i];
-          const Tin* kv = reinterpret_cast<const Tin*>(&kr[i]);
-          __bf16 hi[VEC], lo[VEC];
-#pragma unroll
-          for (int u = 0; u < VEC; ++u) {
-            const float x = to_f32(kv[u]);
-            const float a = x * x;
-            part += a;
-            split_bf16<Tin>(a, hi[u], lo[u]);
-            ATt[(cc + u) * LDC + rr] = from_f32<Tin>(a);
-          }
-          if constexpr (VEC == 8) {
-            *reinterpret_cast<uint4*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint4*>(hi);
-            *reinterpret_cast<uint4*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint4*>(lo);
-          } else {
-            *reinterpret_cast<uint2*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint2*>(hi);
-            *reinterpret_cast<uint2*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint2*>(lo);
-          }
-        }
-      }
-      npart[tid] = part;   // row tid % C, summed over this thread's blocks
-    }
-    if (wave == 0) {
-      // exclusive prefix of log r over the chunk (r clamped away from 0 so
-      // that ratios of prefixes stay finite)
-      const float lr = (lane < C) ? logf(fmaxf(rr_, 1e-30f)) : 0.f;
-      const float inc = wave_prefix_sum(lr);
-      if (lane < C) {
-        lpv[lane] = inc - lr;
-        bev[lane] = br;
-      }
-      if (lane == C - 1) lpv[C] = inc;
-    }
-    if (j + 1 < nchunks) prefetch(j + 1);
-    __syncthreads();
-
-    // ---- B: per-token scalars; Gram of a (split bf16 MFMA) ------------------
-    if (wave == 0 && lane < C) {
-      const int t = lane;
-      float n = 0.f;
-#pragma unroll
-      for (int m = 0; m < G::NT / C; ++m) n += npart[t + m * C];
-      const float bt = bev[t];
-      nv[t] = n;
-      ev[t] = n > 0.f ? eta * bt / n : 0.f;
-      rhov[t] = n > 0.f ? eta * bt * bt / n : 0.f;
-      Pv[t] = expf(lpv[t]);
-      lamv[t] = expf(lpv[C] - lpv[t + 1]);
-      if (t == C - 1) Pv[C] = expf(lpv[C]);
-    }
-    // Tile list: wave w owns the diagonal tile (w, w) and a share of the
-    // off-diagonal lower tiles, and keeps its accumulators in registers.
-    constexpr int NL = TB * (TB + 1) / 2;
-    constexpr int NJ = 1 + (NL - TB + G::NW - 1) / G::NW;
-    f32x4 gacc[NJ];
-    int gja[NJ], gjb[NJ];
-#pragma unroll
-    for (int s2 = 0; s2 < NJ; ++s2) {
-      int a = -1, b = -1;
-      const int job = wave + G::NW * s2;
-      if (s2 == 0) {
-        if (wave < TB) { a = wave; b = wave; }
-      } else {
-        // off-diagonal tiles in row-major order, dealt round-robin
-        int l = job - G::NW, aa = 1;
-        if (l >= 0) {
-          while (l >= aa) { l -= aa; ++aa; }
-          if (aa < TB) { a = aa; b = l; }
-        }
-      }
-      gja[s2] = a;
-      gjb[s2] = b;
-      gacc[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (a >= 0) {
-        mma_nt<DK>(gacc[s2], Ah + a * 16 * LDH, LDH, Ah + b * 16 * LDH, LDH);
-        mma_nt<DK>(gacc[s2], Ah + a * 16 * LDH, LDH, Al + b * 16 * LDH, LDH);
-        mma_nt<DK>(gacc[s2], Al + a * 16 * LDH, LDH, Ah + b * 16 * LDH, LDH);
-      }
-    }
-    __syncthreads();
-    // M[t][i] = rho_t (P_t / P_{i+1}) <a_i, a_t> for i < t
-#pragma unroll
-    for (int s2 = 0; s2 < NJ; ++s2) {
-      const int a = gja[s2], b = gjb[s2];
-      if (a >= 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = a * 16 + acc_row(i), c = b * 16 + acc_col();
-          Mf[t * LDF + c] =
-              c < t ? rhov[t] * __expf(lpv[t] - lpv[c + 1]) * gacc[s2][i] : 0.f;
-        }
-      }
-    }
-
-    // ---- C: diagonal 16x16 blocks of (I + M)^-1 ----------------------------
-    // Wave b wrote diagonal tile (b, b) of M itself, so it can invert it
-    // without waiting for the other waves.
-    if (wave < TB && lane < 16) {
+  // ---- diagonal 16x16 blocks of T = (I + M)^-1 ----------------------------
+  // Wave b wrote diagonal tile (b, b) of M itself; lane c < 16 owns column c.
+  if (wave < TB) {
+    wave_lds_sync();
+    if (lane < 16) {
       const int b = wave, c = lane;
       const float* Mblk = Mf + b * 16 * LDF + b * 16;
       float x[16], s[16];
@@ -261,138 +227,359 @@ __global__ __launch_bounds__(256) void precond_chunk_kernel(
         for (int i = m + 1; i < 16; ++i) s[i] -= Mblk[i * LDF + m] * x[m];
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        Tf[(b * 16 + i) * LDF + b * 16 + c] = x[i];
-        Tft[(b * 16 + c) * LDF + b * 16 + i] = x[i];
-      }
+      for (int i = 0; i < 16; ++i) Tf[(b * 16 + i) * LDF + b * 16 + c] = x[i];
     }
-    __syncthreads();
+  }
+  __syncthreads();
 
-    // ---- D: recursive doubling in fp32, T21 = -T22 (M21 T11) ---------------
+  // ---- recursive doubling in fp32, T21 = -T22 (M21 T11) --------------------
+  // One job = one 16-wide column of T21 in one pair: that column of
+  // Y = M21 T11 goes to the wave's own scratch, then the same column of
+  // T21 = -T22 Y; the right operands are read k-major.
+  {
+    float* ys = Ysc + wave * (C / 2) * LDYS;
 #pragma unroll
     for (int s = 16; s < C; s *= 2) {
-      const int npair = C / (2 * s), nt = s / 16, jobs = npair * nt * nt;
+      const int nt = s / 16, jobs = (C / (2 * s)) * nt;
       for (int job = wave; job < jobs; job += G::NW) {
-        const int p = job / (nt * nt), rt = (job / nt) % nt, ct = job % nt;
-        const int rb = 2 * s * p + s, cb = 2 * s * p;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < s; kk += 16)
-          mma_nt<16>(acc, Mf + (rb + rt * 16) * LDF + cb + kk, LDF,
-                     Tft + (cb + ct * 16) * LDF + cb + kk, LDF);
-        float* ys = Ysc + (p * s) * LDY;
+        const int pp = job / nt, c = job % nt;
+        const int rb = 2 * s * pp + s, cb = 2 * s * pp;
+        for (int rt = 0; rt < nt; ++rt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int kk = 0; kk < s; kk += 16) {
+            Frag<16, float> fa, fb;
+            fa.load(Mf + (rb + rt * 16) * LDF + cb + kk, LDF);
+            fb.load_kmajor(Tf + (cb + kk) * LDF + cb + c * 16, LDF);
+            mma(acc, fa, fb);
+          }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ys[(ct * 16 + acc_col()) * LDY + rt * 16 + acc_row(i)] = acc[i];
-      }
-      __syncthreads();
-      for (int job = wave; job < jobs; job += G::NW) {
-        const int p = job / (nt * nt), rt = (job / nt) % nt, ct = job % nt;
-        const int rb = 2 * s * p + s, cb = 2 * s * p;
-        const float* ys = Ysc + (p * s) * LDY;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < s; kk += 16)
-          mma_nt<16>(acc, Tf + (rb + rt * 16) * LDF + rb + kk, LDF,
-                     ys + (ct * 16) * LDY + kk, LDY);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = rb + rt * 16 + acc_row(i), cc = cb + ct * 16 + acc_col();
-          Tf[rr * LDF + cc] = -acc[i];
-          Tft[cc * LDF + rr] = -acc[i];
+          for (int i = 0; i < 4; ++i)
+            ys[(rt * 16 + acc_row(i)) * LDYS + acc_col()] = acc[i];
         }
+        wave_lds_sync();
+        for (int rt = 0; rt < nt; ++rt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int kk = 0; kk < s; kk += 16) {
+            Frag<16, float> fa, fb;
+            fa.load(Tf + (rb + rt * 16) * LDF + rb + kk, LDF);
+            fb.load_kmajor(ys + kk * LDYS, LDYS);
+            mma(acc, fa, fb);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Tf[(rb + rt * 16 + acc_row(i)) * LDF + cb + c * 16 + acc_col()] = -acc[i];
+        }
+        wave_lds_sync();  // the scratch is rewritten by this wave's next job
       }
       __syncthreads();
     }
+  }
 
-    // ---- E: the serial chain --------------------------------------------------
-    // p_t = <d0, a_t>; b_t = (eta beta_t / n_t)(1 - beta_t P_t p_t)
+  // ---- chunk record: lp, g0 = T e, V = T diag(h) ---------------------------
+  for (int e = tid; e <= C; e += G::NT) out[G::R_LP + e] = lpv[e];
+  {
+    // four threads per row, one 16-wide block each (zero above the diagonal)
+    const int t = tid >> 2, q = tid & 3;
+    float s = 0.f;
+    if (q <= (t >> 4)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += Tf[t * LDF + 16 * q + i] * ev[16 * q + i];
+    }
+    s = group_sum<4>(s);
+    if (q == 0) out[G::R_G + t] = s;
+  }
+  for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
+    const int t = e4 / (C / 4), c0 = (e4 % (C / 4)) * 4;
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    if ((c0 >> 4) <= (t >> 4)) {
+      const float* tr = Tf + t * LDF + c0;
+      v.x = tr[0] * hv[c0];
+      v.y = tr[1] * hv[c0 + 1];
+      v.z = tr[2] * hv[c0 + 2];
+      v.w = tr[3] * hv[c0 + 3];
+    }
+    *reinterpret_cast<float4*>(out + G::R_V + t * C + c0) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chain: the serial recurrence over the chunks of one (batch, head)
+// ---------------------------------------------------------------------------
+template <typename Tin>
+struct KeyPair;
+template <>
+struct KeyPair<__bf16> {
+  using T = unsigned;
+  __device__ static float lo(T p) { return __uint_as_float(p << 16); }
+  __device__ static float hi(T p) { return __uint_as_float(p & 0xffff0000u); }
+};
+template <>
+struct KeyPair<float> {
+  using T = float2;
+  __device__ static float lo(T p) { return p.x; }
+  __device__ static float hi(T p) { return p.y; }
+};
+
+template <int DK, typename Tin>
+struct ChainRegs {
+  using G = P1Cfg<DK, Tin>;
+  static constexpr int C = G::C;
+  // x and g: four threads per token row t = tid/4, quarter q = tid%4 holds
+  // channels [q DK/4, (q+1) DK/4) of the key and the 16-wide block q of V.
+  static constexpr int SEG1 = DK / 4;
+  static constexpr int NR1 = SEG1 * sizeof(Tin) / 16;
+  // d update: wave w owns channels [w DK/4, (w+1) DK/4) as DK/8 pairs; lane l
+  // takes pair l % (DK/8) over the token rows of segment l / (DK/8).
+  static constexpr int NP = DK / 8, NSG = 64 / NP, RS3 = C / NSG;
+  using Pair = typename KeyPair<Tin>::T;
+
+  uint4 kr[NR1];
+  Pair kc[RS3];
+  float4 vr[4];
+  float g0, lpt1, lpC;
+
+  __device__ __forceinline__ void load(const Tin* k, const float* rc, size_t t0,
+                                       int valid, int t, int q, int c3, int sg) {
+#pragma unroll
+    for (int i = 0; i < NR1; ++i) {
+      kr[i] = uint4{0u, 0u, 0u, 0u};
+      if (t < valid)
+        kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + t) * DK + q * SEG1 +
+                                                i * (16 / sizeof(Tin)));
+    }
+#pragma unroll
+    for (int m = 0; m < RS3; ++m) {
+      const int row = sg * RS3 + m;
+      kc[m] = Pair{};
+      if (row < valid) kc[m] = *reinterpret_cast<const Pair*>(k + (t0 + row) * DK + c3);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vr[i] = float4{0.f, 0.f, 0.f, 0.f};
+      if (q <= (t >> 4))
+        vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + 16 * q + 4 * i);
+    }
+    g0 = rc[G::R_G + t];
+    lpt1 = rc[G::R_LP + t + 1];
+    lpC = rc[G::R_LP + C];
+  }
+};
+
+template <int DK, typename Tin>
+__global__ __launch_bounds__(256) void precond_chain_kernel(
+    int T, int nchunks, const Tin* __restrict__ k, const float* __restrict__ d0in,
+    float* __restrict__ rec, float* __restrict__ dent, float* __restrict__ dT) {
+  using G = P1Cfg<DK, Tin>;
+  using R = ChainRegs<DK, Tin>;
+  using KP = KeyPair<Tin>;
+  constexpr int C = G::C;
+  __shared__ float dv[DK], xs[C], cgs[C];
+  const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t = tid >> 2, q = tid & 3;
+  const int sg = lane / R::NP;
+  const int c3 = wave * (DK / 4) + 2 * (lane % R::NP);
+
+  for (int c = tid; c < DK; c += G::NT) dv[c] = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
+  __syncthreads();
+
+  auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
+  R cur, nxt;
+  if (nchunks > 0)
+    cur.load(k, recp(0), (size_t)bh * T, min(C, T), t, q, c3, sg);
+  for (int jj = 0; jj < nchunks; ++jj) {
+    if (jj + 1 < nchunks)
+      nxt.load(k, recp(jj + 1), (size_t)bh * T + (size_t)(jj + 1) * C,
+               min(C, T - (jj + 1) * C), t, q, c3, sg);
+    float* rc = recp(jj);
+    if (tid < DK) dent[((size_t)bh * nchunks + jj) * DK + tid] = dv[tid];
+    // x_t = <d, a_t>
     {
-      constexpr int Q = 256 / C;            // threads per token row
-      constexpr int SEG = DK / Q;           // contiguous channels per thread
-      const int t = tid / Q, q = tid % Q;
-      const Tin* krow = Ks + t * LDK + q * SEG;
-      const float* drow = d0v + q * SEG;
+      const Tin* kv = reinterpret_cast<const Tin*>(cur.kr);
+      const float* dq = dv + q * R::SEG1;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < R::SEG1; c += 2) {
+        const float x0 = to_f32(kv[c]), x1 = to_f32(kv[c + 1]);
+        s0 += x0 * x0 * dq[c];
+        s1 += x1 * x1 * dq[c + 1];
+      }
+      const float s = group_sum<4>(s0 + s1);
+      if (q == 0) xs[t] = s;
+    }
+    __syncthreads();
+    // g_t = g0_t - sum_i V[t][i] x_i
+    {
+      const float* vv = reinterpret_cast<const float*>(cur.vr);
       float s = 0.f;
 #pragma unroll
-      for (int c = 0; c < SEG; ++c) {
-        const float x = to_f32(krow[c]);
-        s += x * x * drow[c];
+      for (int i = 0; i < 16; ++i) s += vv[i] * xs[16 * q + i];
+      s = group_sum<4>(s);
+      const float g = cur.g0 - s;
+      if (q == 0) {
+        rc[G::R_G + t] = g;
+        cgs[t] = expf(cur.lpC - cur.lpt1) * g;
       }
-      s = group_sum<Q>(s);
-      if (q == 0) bvec[t] = ev[t] * (1.f - bev[t] * Pv[t] * s);
     }
     __syncthreads();
-    // g = (I + M)^-1 b (the inverse is zero above the diagonal)
+    // d <- P_C d + sum_t a_t (c_t g_t)
     {
-      constexpr int Q = 256 / C;
-      constexpr int SEG = C / Q;
-      const int t = tid / Q, q = tid % Q;
-      const float* trow = Tf + t * LDF + q * SEG;
-      const float* bseg = bvec + q * SEG;
-      float s = 0.f;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < SEG; ++i) s += trow[i] * bseg[i];
-      s = group_sum<Q>(s);
-      if (q == 0) gv[t] = s;
-    }
-    __syncthreads();
-    // exit value d_C = P_C d0 + sum_i (P_C / P_{i+1}) g_i a_i, and L
-    {
-      constexpr int Q = 256 / DK;           // threads per channel (2, 4 or 8)
-      const int c = tid / Q, q = tid % Q;
-      float s = 0.f;
-      for (int i = q; i < C; i += Q) {
-        const float x = to_f32(Ks[i * LDK + c]);
-        s += lamv[i] * gv[i] * x * x;
+      for (int m = 0; m < R::RS3; ++m) {
+        const float cg = cgs[sg * R::RS3 + m];
+        const float x0 = KP::lo(cur.kc[m]), x1 = KP::hi(cur.kc[m]);
+        s0 += x0 * x0 * cg;
+        s1 += x1 * x1 * cg;
       }
-      s = group_sum<Q>(s);
-      if (q == 0) dnv[c] = Pv[C] * d0v[c] + s;
-      for (int e = tid; e < C * C; e += G::NT) {
-        const int t = e / C, i = e % C;
-        if (i < t) Lb[t * LDC + i] = from_f32<Tin>(__expf(lpv[t] - lpv[i + 1]) * gv[i]);
+      s0 = strided_sum<R::NP>(s0);
+      s1 = strided_sum<R::NP>(s1);
+      if (sg == 0) {
+        const float PC = expf(cur.lpC);
+        dv[c3] = PC * dv[c3] + s0;
+        dv[c3 + 1] = PC * dv[c3 + 1] + s1;
       }
     }
     __syncthreads();
+    cur = nxt;
+  }
+  if (dT && tid < DK) dT[(size_t)bh * DK + tid] = dv[tid];
+}
 
-    // ---- F: K~ = (P d0^T + L A) * K, staged in LDS, stored coalesced --------
-    for (int job = wave; job < TB * DB; job += G::NW) {
-      const int tb = job / DB, db = job % DB;
+// ---------------------------------------------------------------------------
+// ktilde: K~ = (P d0^T + L A) * K per chunk
+// ---------------------------------------------------------------------------
+template <int DK, typename Tin>
+__global__ __launch_bounds__(256) void precond_ktilde_kernel(
+    int T, int nchunks, const Tin* __restrict__ k, const float* __restrict__ rec,
+    const float* __restrict__ dent, Tin* __restrict__ ktil) {
+  using G = P1Cfg<DK, Tin>;
+  constexpr int C = G::C, LDK = G::LDK, LDC = G::LDC, VEC = G::VEC, NCB = G::NCB,
+                DB = G::DB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::kt_bytes];
+  Tin* Ks = reinterpret_cast<Tin*>(smem + G::kK);
+  Tin* As = reinterpret_cast<Tin*>(smem + G::kA);
+  Tin* Lb = reinterpret_cast<Tin*>(smem + G::kL);
+  float* lpv = reinterpret_cast<float*>(smem + G::kVec);  // C + 4
+  float* Pv = lpv + C + 4;
+  float* gv = Pv + C;
+  float* dv = gv + C;
+
+  const int bh = blockIdx.x / nchunks, j = blockIdx.x - bh * nchunks;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int valid = min(C, T - j * C);
+  const size_t t0 = (size_t)bh * T + (size_t)j * C;
+  const float* rc = rec + (size_t)blockIdx.x * G::RS;
+
+#pragma unroll
+  for (int i = 0; i < G::NLK; ++i) {
+    const int e = tid + i * G::NT;
+    const int rr = e / NCB, cc = (e % NCB) * VEC;
+    uint4 kr = {0u, 0u, 0u, 0u};
+    if (rr < valid) kr = *reinterpret_cast<const uint4*>(k + (t0 + rr) * DK + cc);
+    *reinterpret_cast<uint4*>(Ks + rr * LDK + cc) = kr;
+    const Tin* kv = reinterpret_cast<const Tin*>(&kr);
+    Tin a[VEC];
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      const float x = to_f32(kv[u]);
+      a[u] = from_f32<Tin>(x * x);
+    }
+    *reinterpret_cast<uint4*>(As + rr * LDK + cc) = *reinterpret_cast<const uint4*>(a);
+  }
+  if (tid <= C) lpv[tid] = rc[G::R_LP + tid];
+  if (tid < C) gv[tid] = rc[G::R_G + tid];
+  if (tid < DK) dv[tid] = dent[(size_t)blockIdx.x * DK + tid];
+  __syncthreads();
+  if (tid < C) Pv[tid] = expf(lpv[tid]);
+  for (int e = tid; e < C * C; e += G::NT) {
+    const int tt = e / C, i = e % C;
+    Lb[tt * LDC + i] = from_f32<Tin>(i < tt ? __expf(lpv[tt] - lpv[i + 1]) * gv[i] : 0.f);
+  }
+  __syncthreads();
+  // wave w: token block w, all channel blocks; K~ overwrites K in place (each
+  // element is read and written by the same lane)
+  {
+    const int tb = wave;
+    Frag<C, Tin> fl;
+    fl.load(Lb + tb * 16 * LDC, LDC);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      Frag<C, Tin> fa;
+      fa.load_kmajor(As + db * 16, LDK);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma_nt<C>(acc, Lb + tb * 16 * LDC, LDC, ATt + db * 16 * LDC, LDC);
+      mma(acc, fl, fa);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = tb * 16 + acc_row(i), c = db * 16 + acc_col();
-        const float dt = Pv[t] * d0v[c] + acc[i];
-        KTst[t * LDK + c] = from_f32<Tin>(dt * to_f32(Ks[t * LDK + c]));
+        const int tt = tb * 16 + acc_row(i), c = db * 16 + acc_col();
+        const float dt = Pv[tt] * dv[c] + acc[i];
+        Ks[tt * LDK + c] = from_f32<Tin>(dt * to_f32(Ks[tt * LDK + c]));
       }
     }
-    __syncthreads();
-    if (ktil) {
-#pragma unroll
-      for (int i = 0; i < G::NLK; ++i) {
-        const int e = tid + i * G::NT;
-        const int rr = e / NCB, cc = (e % NCB) * VEC;
-        if (e < C * NCB && rr < valid)
-          *reinterpret_cast<uint4*>(ktil + (t0 + rr) * DK + cc) =
-              *reinterpret_cast<const uint4*>(KTst + rr * LDK + cc);
-      }
-    }
-    for (int c = tid; c < DK; c += G::NT) d0v[c] = dnv[c];
-    __syncthreads();
   }
-  if (dT)
-    for (int c = tid; c < DK; c += G::NT) dT[(size_t)bh * DK + c] = d0v[c];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < G::NLK; ++i) {
+    const int e = tid + i * G::NT;
+    const int rr = e / NCB, cc = (e % NCB) * VEC;
+    if (rr < valid)
+      *reinterpret_cast<uint4*>(ktil + (t0 + rr) * DK + cc) =
+          *reinterpret_cast<const uint4*>(Ks + rr * LDK + cc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static int nchunks_of(int T) { return (T + kPrecondChunk - 1) / kPrecondChunk; }
+
+template <int DK, typename Tin>
+static size_t ws_floats(int BH, int T) {
+  return (size_t)BH * nchunks_of(T) * (P1Cfg<DK, Tin>::RS + DK);
 }
 
 template <int DK, typename Tin>
 static int launch_dk(const PrecondArgs& a, hipStream_t s) {
-  // Phase-1 chunk: 64 tokens for bf16 keys, 32 for fp32 keys (LDS budget).
-  constexpr int C = sizeof(Tin) == 2 ? 64 : 32;
-  static_assert(PcCfg<DK, C, Tin>::fits, "phase-1 working set exceeds LDS");
-  dim3 grid(a.B * a.H), block(256);
-  hipLaunchKernelGGL((precond_chunk_kernel<DK, C, Tin>), grid, block, 0, s,
-                     a.T, (const Tin*)a.k, a.beta, a.r, a.eta, a.d0,
-                     (Tin*)a.ktilde, a.dT);
-  return (int)hipGetLastError();
+  using G = P1Cfg<DK, Tin>;
+  static_assert(G::TB == G::NW, "one token block per wave in the ktilde kernel");
+  const int BH = a.B * a.H, nch = nchunks_of(a.T);
+  float* rec = static_cast<float*>(a.ws);
+  float* dent = rec + (size_t)BH * nch * G::RS;
+  const dim3 block(256);
+  if (nch > 0) {
+    hipLaunchKernelGGL((precond_prep_kernel<DK, Tin>), dim3(BH * nch), block, 0, s,
+                       a.T, nch, (const Tin*)a.k, a.beta, a.r, a.eta, rec);
+    const int rc = (int)hipGetLastError();
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL((precond_chain_kernel<DK, Tin>), dim3(BH), block, 0, s, a.T,
+                     nch, (const Tin*)a.k, a.d0, rec, dent, a.dT);
+  int rc = (int)hipGetLastError();
+  if (rc) return rc;
+  if (nch > 0 && a.ktilde) {
+    hipLaunchKernelGGL((precond_ktilde_kernel<DK, Tin>), dim3(BH * nch), block, 0, s,
+                       a.T, nch, (const Tin*)a.k, rec, dent, (Tin*)a.ktilde);
+    rc = (int)hipGetLastError();
+  }
+  return rc;
+}
+
+size_t precond_workspace_bytes(int B, int H, int T, int Dk, int bf16) {
+  const int BH = B * H;
+  size_t f = 0;
+  if (bf16) {
+    switch (Dk) {
+      case 32: f = ws_floats<32, __bf16>(BH, T); break;
+      case 64: f = ws_floats<64, __bf16>(BH, T); break;
+      case 128: f = ws_floats<128, __bf16>(BH, T); break;
+    }
+  } else {
+    switch (Dk) {
+      case 32: f = ws_floats<32, float>(BH, T); break;
+      case 64: f = ws_floats<64, float>(BH, T); break;
+      case 128: f = ws_floats<128, float>(BH, T); break;
+    }
+  }
+  return f * 4;
 }
 
 int launch_precond_scan(const PrecondArgs& a, hipStream_t s) {

@@ -62,9 +62,10 @@ int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype);
 
 /*
  * Device workspace, in bytes, that osdn_forward needs for these sizes
- * (0 if the sizes are invalid or the call needs none). The workspace holds the preconditioned keys
- * produced by phase 1 ([B,H,T,Dk] in the storage dtype) and is only valid
- * for the duration of one call.
+ * (0 if the sizes are invalid or the call needs none). The workspace holds
+ * the preconditioned keys produced by phase 1 ([B,H,T,Dk] in the storage
+ * dtype) followed by the phase-1 scratch (osdn_precond_workspace_bytes), and
+ * its contents are only meaningful during one call.
  */
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
@@ -106,15 +107,26 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Device scratch, in bytes, that osdn_precond_scan needs (0 if the sizes are
+ * invalid or T = 0): per chunk of 64 tokens and (batch, head), a fp32 record
+ * of the gate prefix, the step sizes and the 64 x 64 matrix that maps the
+ * chunk's entry preconditioner to its step sizes, plus that entry value.
+ */
+size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype);
+
+/*
  * Phase 1 alone ([OSDN-it] 2.2, first phase of the two-phase implementation):
  * writes the preconditioned keys k~_t = d_t*k_t ([B,H,T,Dk], dtype; NULL: not
  * written) and d_T ([B,H,Dk] fp32; NULL: not written). Reads only k, beta, r,
- * eta and d0, with the same meaning and layout as in osdn_forward. Needs no
- * workspace.
+ * eta and d0, with the same meaning and layout as in osdn_forward.
+ * workspace / workspace_bytes: device scratch of at least
+ * osdn_precond_workspace_bytes(...) bytes, 256-byte aligned, not overlapping
+ * any argument.
  */
 int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
                       const float* beta, const float* r, float eta,
-                      const float* d0, void* ktilde, float* d_T, void* stream);
+                      const float* d0, void* ktilde, float* d_T,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Phase 2 alone ([OSDN-it] 2.1-2.2, second phase): the chunkwise WY delta rule

@@ -36,6 +36,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("osdn_forward", "osdn_forward_workspace_bytes", "osdn_strerror",
               "osdn_forward_supported", "osdn_precond_scan",
+              "osdn_precond_workspace_bytes",
               "osdn_chunk_forward", "gdn2_forward", "gdn2_forward_supported"):
         assert n in names
 
@@ -71,9 +72,18 @@ def test_supported_and_workspace_sizes():
     assert L.osdn_forward_supported(48, 32, 16, 1) == 0
     assert L.osdn_forward_supported(32, 32, 8, 1) == 0
     assert L.osdn_forward_supported(32, 32, 16, 7) == 0
+    # phase-1 scratch: per 64-token chunk, lp (64 + 4), g (64), V (64 x 64)
+    # and the entry value of d (Dk), all fp32; rounded up to 256 bytes
+    def pre(BH, T, Dk):
+        n = BH * ((T + 63) // 64) * (68 + 64 + 64 * 64 + Dk) * 4
+        return (n + 255) // 256 * 256
+    assert L.osdn_precond_workspace_bytes(4, 16, 4096, 128, 1) == pre(64, 4096, 128)
+    assert L.osdn_precond_workspace_bytes(1, 1, 0, 32, 1) == 0
+    assert L.osdn_precond_workspace_bytes(1, 1, 8, 40, 1) == 0
     assert L.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
-        4 * 16 * 4096 * 128 * 2
-    assert L.osdn_forward_workspace_bytes(1, 1, 3, 32, 32, 16, 0) == 512
+        4 * 16 * 4096 * 128 * 2 + pre(64, 4096, 128)
+    assert L.osdn_forward_workspace_bytes(1, 1, 3, 32, 32, 16, 0) == \
+        512 + pre(1, 3, 32)
     assert L.osdn_forward_workspace_bytes(-1, 1, 3, 32, 32, 16, 0) == 0
 
 
@@ -116,15 +126,23 @@ def test_precond_scan_error_paths():
     L = osdn.load_library()
     P = ctypes.c_void_p
     L.osdn_precond_scan.argtypes = [ctypes.c_int] * 5 + [P, P, P, ctypes.c_float,
-                                                         P, P, P, P]
-    assert L.osdn_precond_scan(1, 1, 8, 32, 1, None, 0x1000, None, 0.1, None,
-                               None, None, None) == NULL_ARG
-    assert L.osdn_precond_scan(1, 1, -8, 32, 1, 0x1000, 0x2000, None, 0.1,
-                               None, None, None, None) == BAD_DIMS
-    assert L.osdn_precond_scan(1, 1, 8, 40, 1, 0x1000, 0x2000, None, 0.1,
-                               None, None, None, None) == UNSUPPORTED
-    assert L.osdn_precond_scan(1, 1, 8, 32, 1, 0x1000, 0x2000, None, 0.1,
-                               None, 0x1000 + 16, None, None) == ALIASING
+                                                         P, P, P, P,
+                                                         ctypes.c_size_t, P]
+
+    def pre(B=1, T=8, Dk=32, k=0x1000, beta=0x2000, kt=None, dT=None,
+            ws=0x100000, wsb=1 << 20):
+        return L.osdn_precond_scan(B, 1, T, Dk, 1, k, beta, None, 0.1, None,
+                                   kt, dT, ws, wsb, None)
+    assert pre(k=None) == NULL_ARG
+    assert pre(T=-8) == BAD_DIMS
+    assert pre(Dk=40) == UNSUPPORTED
+    assert pre(ws=None) == WORKSPACE
+    assert pre(wsb=64) == WORKSPACE
+    assert pre(ws=0x100040) == WORKSPACE          # not 256-byte aligned
+    assert pre(kt=0x1000 + 16) == ALIASING
+    assert pre(ws=0x1000) == ALIASING             # workspace over k
+    # B = 0: nothing to do, no pointer or workspace needed
+    assert pre(B=0, k=None, beta=None, ws=None, wsb=0) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
