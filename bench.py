@@ -122,13 +122,17 @@ def bench_gdn2(args, w, inp, x, dt, dev):
     code = {torch.float32: 0, torch.bfloat16: 1}[dt]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    ws_n = L.gdn2_forward_workspace_bytes(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk,
+                                          code)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         rc = L.gdn2_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code,
                             P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]),
-                            P(x["b"]), P(x["w"]), None, 1.0, P(o), P(S_T), sp)
+                            P(x["b"]), P(x["w"]), None, 1.0, P(o), P(S_T),
+                            P(ws), ws.numel(), sp)
         if ev is not None:
             ev[1].record(stream)
         if rc:
@@ -245,7 +249,11 @@ def main():
     ktil = torch.empty((w.B, w.H, w.T, w.Dk), dtype=dt, device=dev)
     L = osdn.load_library()
     code = {torch.float32: 0, torch.bfloat16: 1}[dt]
-    pws_n = L.osdn_precond_workspace_bytes(w.B, w.H, w.T, w.Dk, code)
+    # one scratch buffer serves both entry points (phase-1 scratch is dead
+    # when phase 2 starts)
+    pws_n = max(L.osdn_precond_workspace_bytes(w.B, w.H, w.T, w.Dk, code),
+                L.osdn_chunk_workspace_bytes(w.B, w.H, w.T, w.Dk, w.Dv,
+                                             w.chunk, code))
     pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
@@ -261,7 +269,8 @@ def main():
             ev[1].record(stream)
         rc |= L.osdn_chunk_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code,
                                    P(x["q"]), P(x["k"]), P(ktil), P(x["v"]),
-                                   P(x["beta"]), None, 1.0, P(o), P(S_T), sp)
+                                   P(x["beta"]), None, 1.0, P(o), P(S_T),
+                                   P(pws), pws.numel(), sp)
         if ev is not None:
             ev[2].record(stream)
         if rc:

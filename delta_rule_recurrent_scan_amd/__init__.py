@@ -60,11 +60,17 @@ def load_library():
     L.osdn_precond_workspace_bytes.restype = Z
     L.osdn_precond_scan.argtypes = [I, I, I, I, I, P, P, P, F, P, P, P, P, Z, P]
     L.osdn_precond_scan.restype = I
-    L.osdn_chunk_forward.argtypes = [I] * 7 + [P, P, P, P, P, P, F, P, P, P]
+    L.osdn_chunk_workspace_bytes.argtypes = [I] * 7
+    L.osdn_chunk_workspace_bytes.restype = Z
+    L.osdn_chunk_forward.argtypes = ([I] * 7 + [P, P, P, P, P, P, F, P, P, P,
+                                                Z, P])
     L.osdn_chunk_forward.restype = I
     L.gdn2_forward_supported.argtypes = [I, I, I, I]
     L.gdn2_forward_supported.restype = I
-    L.gdn2_forward.argtypes = [I] * 7 + [P, P, P, P, P, P, P, F, P, P, P]
+    L.gdn2_forward_workspace_bytes.argtypes = [I] * 7
+    L.gdn2_forward_workspace_bytes.restype = Z
+    L.gdn2_forward.argtypes = ([I] * 7 + [P, P, P, P, P, P, P, F, P, P, P, Z,
+                                          P])
     L.gdn2_forward.restype = I
     _lib = L
     return L
@@ -192,7 +198,7 @@ def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True,
 
 
 def osdn_chunk_forward(q, k, ktilde, v, beta, S0=None, chunk=64, scale=1.0,
-                       out=None):
+                       out=None, workspace=None):
     """Phase 2 alone on the GPU (write keys ktilde given): returns (o, S_T)."""
     L = load_library()
     dev = q.device
@@ -211,17 +217,20 @@ def osdn_chunk_forward(q, k, ktilde, v, beta, S0=None, chunk=64, scale=1.0,
         o, S_T = out
     _check(o, "o", (B, H, T, Dv), dt, dev)
     _check(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    need = L.osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = L.osdn_chunk_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt], _ptr(q),
                               _ptr(k), _ptr(ktilde), _ptr(v), _ptr(beta),
                               _ptr(S0), float(scale), _ptr(o), _ptr(S_T),
-                              _stream(dev))
+                              _ptr(workspace), workspace.numel(), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_chunk_forward")
     return o, S_T
 
 
 def gdn2_forward(q, k, v, log_alpha, b, w, S0=None, chunk=64, scale=1.0,
-                 out=None):
+                 out=None, workspace=None):
     """Gated DeltaNet-2 forward on the GPU: returns (o, S_T).
 
     q, k, b: [B,H,T,Dk]; v, w: [B,H,T,Dv] (one dtype, fp32 or bf16);
@@ -245,10 +254,14 @@ def gdn2_forward(q, k, v, log_alpha, b, w, S0=None, chunk=64, scale=1.0,
         o, S_T = out
     _check(o, "o", (B, H, T, Dv), dt, dev)
     _check(S_T, "S_T", (B, H, Dk, Dv), torch.float32, dev)
+    need = L.gdn2_forward_workspace_bytes(B, H, T, Dk, Dv, chunk,
+                                          _DTYPE_CODE[dt])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = L.gdn2_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt], _ptr(q),
                         _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                         _ptr(S0), float(scale), _ptr(o), _ptr(S_T),
-                        _stream(dev))
+                        _ptr(workspace), workspace.numel(), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "gdn2_forward")
     return o, S_T

@@ -119,6 +119,25 @@ struct Frag<KEXT, __bf16> {
       t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (lds_bf16x4*)(p + (32 * N32 + 4 * g) * ld));
   }
+  // Fragment-major global storage (ELEMS elements): slot s of lane l at
+  // [s][l], so that a wave moves each slot as one contiguous block.
+  static constexpr int ELEMS = 16 * KEXT;
+  __device__ __forceinline__ void store_global(__bf16* base) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N32; ++i)
+      *reinterpret_cast<bf16x8*>(base + (i * 64 + lane) * 8) = v[i];
+    if constexpr (R16)
+      *reinterpret_cast<bf16x4*>(base + N32 * 512 + lane * 4) = t;
+  }
+  __device__ __forceinline__ void load_global(const __bf16* base) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N32; ++i)
+      v[i] = *reinterpret_cast<const bf16x8*>(base + (i * 64 + lane) * 8);
+    if constexpr (R16)
+      t = *reinterpret_cast<const bf16x4*>(base + N32 * 512 + lane * 4);
+  }
 };
 
 template <int KEXT>
@@ -138,7 +157,36 @@ struct Frag<KEXT, float> {
 #pragma unroll
     for (int i = 0; i < KEXT / 4; ++i) v[i] = p[4 * i * ld];
   }
+  static constexpr int ELEMS = 16 * KEXT;
+  __device__ __forceinline__ void store_global(float* base) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < KEXT / 4; ++i) base[i * 64 + lane] = v[i];
+  }
+  __device__ __forceinline__ void load_global(const float* base) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < KEXT / 4; ++i) v[i] = base[i * 64 + lane];
+  }
 };
+
+// A 16x16 fp32 accumulator tile in global memory in accumulator order (lane
+// l's four values contiguous at [l][0..3]), rounded to Tin.
+__device__ __forceinline__ void acc_store(const f32x4& a, __bf16* base) {
+  bf16x4 b;
+  b[0] = (__bf16)a[0]; b[1] = (__bf16)a[1]; b[2] = (__bf16)a[2]; b[3] = (__bf16)a[3];
+  *reinterpret_cast<bf16x4*>(base + (threadIdx.x & 63) * 4) = b;
+}
+__device__ __forceinline__ void acc_store(const f32x4& a, float* base) {
+  *reinterpret_cast<f32x4*>(base + (threadIdx.x & 63) * 4) = a;
+}
+__device__ __forceinline__ f32x4 acc_load(const __bf16* base) {
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(base + (threadIdx.x & 63) * 4);
+  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+__device__ __forceinline__ f32x4 acc_load(const float* base) {
+  return *reinterpret_cast<const f32x4*>(base + (threadIdx.x & 63) * 4);
+}
 
 // acc += A * B^T from two register fragments.
 template <int KEXT>

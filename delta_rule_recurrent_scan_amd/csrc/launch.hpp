@@ -38,6 +38,7 @@ struct ChunkArgs {
   const float* log_alpha;   // GDN-2: [B,H,T,Dk] fp32
   const void* b;            // GDN-2: [B,H,T,Dk] erase gate
   const void* w;            // GDN-2: [B,H,T,Dv] write gate
+  void* ws;                 // wy_workspace_bytes(...) bytes, 16-byte aligned
 };
 
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
@@ -48,7 +49,11 @@ int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
 size_t precond_workspace_bytes(int B, int H, int T, int Dk, int bf16);
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
-bool osdn_chunk_supported(int Dk, int chunk, int bf16);
-bool gdn2_chunk_supported(int Dk, int chunk, int bf16);
+bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);
+bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);
+// Device scratch of the chunk engine: per chunk, the S0-independent operands
+// of the chunk step.
+size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
+                          int bf16);
 
 }  // namespace osdn

@@ -68,7 +68,7 @@ const char* osdn_strerror(int status) {
 int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype) {
   if (!dim_ok(Dk) || !dim_ok(Dv) || !chunk_ok(chunk)) return 0;
   if (dtype != OSDN_F32 && dtype != OSDN_BF16) return 0;
-  return osdn::osdn_chunk_supported(Dk, chunk, dtype == OSDN_BF16) ? 1 : 0;
+  return osdn::osdn_chunk_supported(Dk, Dv, chunk, dtype == OSDN_BF16) ? 1 : 0;
 }
 
 size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype) {
@@ -78,13 +78,30 @@ size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype) {
   return round256(osdn::precond_workspace_bytes(B, H, T, Dk, dtype == OSDN_BF16));
 }
 
+size_t osdn_chunk_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                  int chunk, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
+      !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return 0;
+  return round256(osdn::wy_workspace_bytes(B, H, T, Dk, Dv, chunk,
+                                           dtype == OSDN_BF16));
+}
+
+size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                    int chunk, int dtype) {
+  return osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+}
+
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype) {
   if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
       !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
     return 0;
-  return round256((size_t)B * H * T * Dk * elem(dtype)) +
-         osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
+  // the preconditioned keys, then scratch shared by the two phases (the
+  // phase-1 scratch is dead when phase 2 starts)
+  const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
+  const size_t p2 = osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
 }
 
 int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
@@ -154,7 +171,7 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
   if (rc != 0) return OSDN_ERR_HIP;
   osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
                      workspace, v, beta, S0, scale, o, S_T,
-                     nullptr, nullptr, nullptr};
+                     nullptr, nullptr, nullptr, pws};
   rc = osdn::launch_osdn_chunk(ca, s);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
@@ -164,23 +181,28 @@ int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
                        int dtype, const void* q, const void* k,
                        const void* ktilde, const void* v, const float* beta,
                        const float* S0, float scale, void* o, float* S_T,
-                       void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
   if ((size_t)B * H * T > 0 && (!q || !k || !ktilde || !v || !beta || !o))
     return OSDN_ERR_NULL_ARG;
   if (!osdn_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
+  const size_t need = osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
   if ((size_t)B * H == 0) return OSDN_OK;
   const size_t BH = (size_t)B * H, es = elem(dtype);
   const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
                        rng(ktilde, BH * T * Dk * es), rng(v, BH * T * Dv * es),
                        rng(beta, BH * T * 4), rng(S0, S0 ? BH * Dv * Dk * 4 : 0)};
   const Range outs[] = {rng(o, BH * T * Dv * es),
-                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0)};
+                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0),
+                        rng(workspace, need)};
   const int allowed[][2] = {{1, 5}};  // S_T == S0
   if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
   osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
                      ktilde, v, beta, S0, scale, o, S_T,
-                     nullptr, nullptr, nullptr};
+                     nullptr, nullptr, nullptr, workspace};
   const int rc = osdn::launch_osdn_chunk(ca, (hipStream_t)stream);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
@@ -189,18 +211,22 @@ int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
 int gdn2_forward_supported(int Dk, int Dv, int chunk, int dtype) {
   if (!dim_ok(Dk) || !dim_ok(Dv) || !chunk_ok(chunk)) return 0;
   if (dtype != OSDN_F32 && dtype != OSDN_BF16) return 0;
-  return osdn::gdn2_chunk_supported(Dk, chunk, dtype == OSDN_BF16) ? 1 : 0;
+  return osdn::gdn2_chunk_supported(Dk, Dv, chunk, dtype == OSDN_BF16) ? 1 : 0;
 }
 
 int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  const void* q, const void* k, const void* v,
                  const float* log_alpha, const void* b, const void* w,
                  const float* S0, float scale, void* o, float* S_T,
-                 void* stream) {
+                 void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
   if ((size_t)B * H * T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
     return OSDN_ERR_NULL_ARG;
   if (!gdn2_forward_supported(Dk, Dv, chunk, dtype)) return OSDN_ERR_UNSUPPORTED;
+  const size_t need = gdn2_forward_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
   if ((size_t)B * H == 0) return OSDN_OK;
   const size_t BH = (size_t)B * H, es = elem(dtype);
   const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
@@ -208,11 +234,13 @@ int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                        rng(b, BH * T * Dk * es), rng(w, BH * T * Dv * es),
                        rng(S0, S0 ? BH * Dv * Dk * 4 : 0)};
   const Range outs[] = {rng(o, BH * T * Dv * es),
-                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0)};
+                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0),
+                        rng(workspace, need)};
   const int allowed[][2] = {{1, 6}};  // S_T == S0
   if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
   osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                     nullptr, v, nullptr, S0, scale, o, S_T, log_alpha, b, w};
+                     nullptr, v, nullptr, S0, scale, o, S_T, log_alpha, b, w,
+                     workspace};
   const int rc = osdn::launch_gdn2_chunk(ca, (hipStream_t)stream);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;

@@ -22,16 +22,21 @@
 // value z_t, query gamma_t*q_t, exit keys x'_t = k_t*gamma_C/gamma_t and exit
 // decay g = gamma_C; rs = 1.
 //
-// Work decomposition: one workgroup (4 waves) per (batch, head, VT-wide value
-// tile) walks the chunks in order; the VT x Dk state slice lives in fp32 MFMA
-// accumulators. Value tiles are independent given the keys, so the
-// V-independent chunk quantities (A, T, Q X^T) are recomputed per tile rather
-// than written to and re-read from HBM. The next chunk's inputs are fetched
-// into registers while the current chunk computes.
-//
-// T = (I + A)^-1: 16x16 diagonal blocks by fp32 forward substitution (one
-// lane per column), then recursive doubling, merging pairs of s x s inverses
-// into 2s x 2s ones with T21 = -T22 A21 T11 on MFMA.
+// Split by dependence on S0. With P = Q X^T masked to i <= t,
+//   Wk = T diag(rs) Y,  U = T diag(rs) Z,  Q' = Q - P Wk,  O' = P U,
+// the chunk step is
+//   W = U - Wk S0^T,    O = O' + Q' S0^T,   S1 = S0 diag(g) + W^T X'.
+// * prep: persistent workgroups of 8 waves over all chunks at once (the next
+//   chunk is fetched while the current one computes) form Wk, U, Q', O' and
+//   X' and write them to the workspace in MFMA operand order.
+//   T comes from 16x16 diagonal blocks by fp32 forward substitution (one lane
+//   per column) and recursive doubling, T21 = -T22 A21 T11, on MFMA.
+// * scan: one workgroup (4 waves) per (batch, head, VT-wide value tile) walks
+//   the chunks in order with the VT x Dk state slice in fp32 MFMA
+//   accumulators: two products into W and O, one into the state, two
+//   barriers per chunk; the next chunk's operands are loaded into registers
+//   while the current one computes.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -42,318 +47,198 @@ namespace osdn {
 struct OsdnVariant {};
 struct Gdn2Variant {};
 
-template <int DK, int C, int VT, typename Tin>
-struct WyCfg {
-  static constexpr int NW = 4, NT = 256;
+// Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
+// storage dtype (g in fp32): Wk and Q' as 16-row A fragments (row block tb
+// at tb*16*Dk), X' as k-major B fragments (channel block db at db*16*C), U
+// and O' as accumulator tiles ((tb, vb) at (tb*Dv/16 + vb)*256).
+template <typename Tin>
+struct WyBufs {
+  Tin *wk, *qp, *xp, *u, *op;
+  float* g;
+};
+
+template <typename Tin>
+static WyBufs<Tin> wy_bufs(void* ws, int BH, int nchunks, int C, int Dk, int Dv) {
+  const size_t n = (size_t)BH * nchunks * C;
+  Tin* b = static_cast<Tin*>(ws);
+  WyBufs<Tin> w;
+  w.wk = b;
+  w.qp = w.wk + n * Dk;
+  w.xp = w.qp + n * Dk;
+  w.u = w.xp + n * Dk;
+  w.op = w.u + n * Dv;
+  w.g = reinterpret_cast<float*>(w.op + n * Dv);
+  return w;
+}
+
+size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
+                          int bf16) {
+  const size_t n = (size_t)B * H * ((T + chunk - 1) / chunk);
+  const size_t e = bf16 ? 2 : 4;
+  return n * chunk * (3 * (size_t)Dk + 2 * (size_t)Dv) * e + n * Dk * 4;
+}
+
+// ---------------------------------------------------------------------------
+// prep
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int C, typename Tin>
+struct PrepCfg {
+  static constexpr int NW = 8, NT = 512;
   static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
-  static constexpr int LDK = DK + PAD;
-  static constexpr int LDC = C + PAD;
-  static constexpr int LDR = VT + PAD;         // rows of R and W ([C][VT])
-  static constexpr int LDS16 = 16 + PAD;       // doubling scratch ([C/2][16])
-  static constexpr int TB = C / 16, VB = VT / 16, DB = DK / 16;
+  static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD;
+  static constexpr int LDS16 = 16 + PAD;      // doubling scratch ([C/2][16])
+  static constexpr int LDD = 20;              // fp32 diagonal blocks, transposed
+  static constexpr int TB = C / 16, DB = DK / 16, VBT = DV / 16;
   static constexpr int VEC = 16 / sizeof(Tin);
-  static constexpr int NCB = DK / VEC;         // 16-byte blocks per key row
   static constexpr size_t E = sizeof(Tin);
-  static constexpr size_t oX = 0;
-  static constexpr size_t oY = oX + (size_t)C * LDK * E;
-  static constexpr size_t oQ = oY + (size_t)C * LDK * E;
-  static constexpr size_t oS = oQ + (size_t)C * LDK * E;
-  static constexpr size_t oZ = oS + (size_t)VT * LDK * E;
-  static constexpr size_t oRS = oZ + (size_t)C * VT * E;
-  static constexpr size_t oG = oRS + (size_t)C * 4;
-  // fp32 diagonal 16x16 blocks of A, each stored transposed (column-major)
-  static constexpr int LDD = 20;
-  static constexpr size_t oA = oG + (size_t)DK * 4;
-  static constexpr size_t oAb = oA + (size_t)TB * 16 * LDD * 4;
+  static constexpr size_t oY = 0;
+  static constexpr size_t oX = oY + (size_t)C * LDK * E;
+  static constexpr size_t oQ = oX + (size_t)C * LDK * E;
+  static constexpr size_t oZ = oQ + (size_t)C * LDK * E;
+  static constexpr size_t oAb = oZ + (size_t)C * LDV * E;
   static constexpr size_t oTb = oAb + (size_t)C * LDC * E;
-  static constexpr size_t oYs = oTb + (size_t)C * LDC * E;
-  static constexpr size_t oP = oYs + (size_t)NW * (C / 2) * LDS16 * E;
-  static constexpr size_t oR = oP + (size_t)C * LDC * E;
-  static constexpr size_t oW = oR + (size_t)C * LDR * E;
-  static constexpr size_t bytes = oW + (size_t)C * LDR * E;
+  static constexpr size_t oPb = oTb + (size_t)C * LDC * E;
+  static constexpr size_t oA = oPb + (size_t)C * LDC * E;
+  static constexpr size_t oYs = oA + (size_t)TB * 16 * LDD * 4;
+  static constexpr size_t oG = oYs + (size_t)NW * (C / 2) * LDS16 * E;
+  static constexpr size_t bytes = oG + (size_t)DK * 4;
   static constexpr bool fits = bytes <= 163840;
-  // State tiles per wave: every value tile times a contiguous run of DPW key
-  // tiles.
-  static constexpr int DPW = (DB + NW - 1) / NW;
-  static constexpr int NS = VB * DPW;
-  static constexpr int NLK = (C * DK / VEC + NT - 1) / NT;
-  static constexpr int NLV = (C * VT / VEC + NT - 1) / NT;
-  // GDN-2 decay pass: TPC threads per key channel, each over C/TPC tokens
+  // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
   static constexpr int TPC = NT / DK;
-  static constexpr int TPT = C / TPC;
+  static constexpr int TPT = C / TPC > 0 ? C / TPC : 1;
 };
 
-struct SmemPtrs {
-  void *X, *Y, *Q, *Z;
-  float *rs, *g;
-};
+// Raw operands of one chunk, fetched into registers while the previous chunk
+// computes (padding rows are zero).
+template <class V, int DK, int DV, int C, typename Tin>
+struct PrepRegs {
+  using G = PrepCfg<DK, DV, C, Tin>;
+  static constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
+  static constexpr int VEC = G::VEC;
+  static constexpr int NKB = C * (DK / VEC), NVB = C * (DV / VEC);
+  static constexpr int NLK = (NKB + G::NT - 1) / G::NT;
+  static constexpr int NLV = (NVB + G::NT - 1) / G::NT;
+  uint4 k[NLK], q[NLK], x[NLK], v[NLV], w[kGdn2 ? NLV : 1];
+  float bk[NLK], bv[NLV];          // OSDN: beta of the row
+  float la[kGdn2 ? G::TPT : 1];    // GDN-2: log alpha of the decay pass
 
-// ---------------------------------------------------------------------------
-// Per-variant chunk inputs, fetched into registers one chunk ahead.
-// ---------------------------------------------------------------------------
-template <class V, int DK, int C, int VT, typename Tin>
-struct ChunkRegs;
+  __device__ __forceinline__ void load(const ChunkArgs& p, int n, int nchunks) {
+    const int bh = n / nchunks, j = n - bh * nchunks;
+    const int T = p.T, Dv = p.Dv, tid = threadIdx.x;
+    const int valid = min(C, T - j * C);
+    const size_t t0 = (size_t)bh * T + (size_t)j * C;
+    const Tin* xs = kGdn2 ? (const Tin*)p.b : (const Tin*)p.ktilde;
+    const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NLK; ++i) {
+      const int e = tid + i * G::NT;
+      const int rr = e / (DK / VEC), cc = (e % (DK / VEC)) * VEC;
+      k[i] = z; q[i] = z; x[i] = z; bk[i] = 0.f;
+      if (e < NKB && rr < valid) {
+        const size_t gi = (t0 + rr) * DK + cc;
+        k[i] = *reinterpret_cast<const uint4*>((const Tin*)p.k + gi);
+        q[i] = *reinterpret_cast<const uint4*>((const Tin*)p.q + gi);
+        x[i] = *reinterpret_cast<const uint4*>(xs + gi);
+        if constexpr (!kGdn2) bk[i] = p.beta[t0 + rr];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) {
+      const int e = tid + i * G::NT;
+      const int rr = e / (DV / VEC), cc = (e % (DV / VEC)) * VEC;
+      v[i] = z; bv[i] = 0.f;
+      if constexpr (kGdn2) w[i] = z;
+      if (e < NVB && rr < valid) {
+        const size_t gi = (t0 + rr) * Dv + cc;
+        v[i] = *reinterpret_cast<const uint4*>((const Tin*)p.v + gi);
+        if constexpr (kGdn2)
+          w[i] = *reinterpret_cast<const uint4*>((const Tin*)p.w + gi);
+        else
+          bv[i] = p.beta[t0 + rr];
+      }
+    }
+    if constexpr (kGdn2) {
+      constexpr int CPW = 64 / G::TPC;
+      const int lane = tid & 63, wave = tid >> 6;
+      const int c = wave * CPW + lane % CPW, part = lane / CPW;
+#pragma unroll
+      for (int m = 0; m < G::TPT; ++m) {
+        const int t = part * G::TPT + m;
+        la[m] = (t < valid) ? p.log_alpha[(t0 + t) * DK + c] : 0.f;
+      }
+    }
+  }
 
-// OSDN: k, k~, q (row-major [C][Dk]), v, beta.
-template <int DK, int C, int VT, typename Tin>
-struct ChunkRegs<OsdnVariant, DK, C, VT, Tin> {
-  using G = WyCfg<DK, C, VT, Tin>;
-  uint4 k[G::NLK], kt[G::NLK], q[G::NLK], v[G::NLV];
-  float beta;
-
-  __device__ __forceinline__ void load(const ChunkArgs& p, int bh, size_t t0,
-                                       int valid, int v0) {
-    const Tin* kp = (const Tin*)p.k;
-    const Tin* ktp = (const Tin*)p.ktilde;
-    const Tin* qp = (const Tin*)p.q;
-    const Tin* vp = (const Tin*)p.v;
+  // OSDN: Y = beta*k, X = k~, Q = q, Z = beta*v. GDN-2: raw k, b, q and
+  // Z = w*v (the decay pass forms X, Y and Q in place).
+  __device__ __forceinline__ void store(Tin* Ys, Tin* Xs, Tin* Qs, Tin* Zs) const {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < G::NLK; ++i) {
+    for (int i = 0; i < NLK; ++i) {
       const int e = tid + i * G::NT;
-      const uint4 z = {0u, 0u, 0u, 0u};
-      k[i] = z; kt[i] = z; q[i] = z;
-      if (e < C * G::NCB) {
-        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
-        if (rr < valid) {
-          const size_t g = (t0 + rr) * DK + cc;
-          k[i] = *reinterpret_cast<const uint4*>(kp + g);
-          q[i] = *reinterpret_cast<const uint4*>(qp + g);
-          kt[i] = *reinterpret_cast<const uint4*>(ktp + g);
+      if (e < NKB) {
+        const int rr = e / (DK / VEC), cc = (e % (DK / VEC)) * VEC;
+        *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
+        if constexpr (kGdn2) {
+          *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = k[i];
+          *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = x[i];
+        } else {
+          const Tin* kv = reinterpret_cast<const Tin*>(&k[i]);
+          Tin y[VEC];
+#pragma unroll
+          for (int u = 0; u < VEC; ++u) y[u] = from_f32<Tin>(bk[i] * to_f32(kv[u]));
+          *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(y);
+          *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = x[i];
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < G::NLV; ++i) {
+    for (int i = 0; i < NLV; ++i) {
       const int e = tid + i * G::NT;
-      const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
-      v[i] = uint4{0u, 0u, 0u, 0u};
-      if (e < C * VT / G::VEC && rr < valid)
-        v[i] = *reinterpret_cast<const uint4*>(vp + (t0 + rr) * p.Dv + v0 + cc);
-    }
-    beta = (tid < valid) ? p.beta[t0 + tid] : 0.f;
-  }
-
-  __device__ __forceinline__ void store(const SmemPtrs& s) const {
-    Tin* Xs = (Tin*)s.X;
-    Tin* Ys = (Tin*)s.Y;
-    Tin* Qs = (Tin*)s.Q;
-    Tin* Zs = (Tin*)s.Z;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < G::NLK; ++i) {
-      const int e = tid + i * G::NT;
-      if (e < C * G::NCB) {
-        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
-        *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = k[i];
-        *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
-        *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = kt[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < G::NLV; ++i) {
-      const int e = tid + i * G::NT;
-      if (e < C * VT / G::VEC) {
-        const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
-        *reinterpret_cast<uint4*>(Zs + rr * VT + cc) = v[i];
-      }
-    }
-    if (tid < C) s.rs[tid] = beta;
-  }
-
-  __device__ __forceinline__ void transform(const SmemPtrs&) const {}
-};
-
-// GDN-2: k, q, b staged raw (row-major) into the X, Q, Y buffers, z = w*v,
-// and log alpha held by the threads of the decay pass (TPC threads per key
-// channel, each over a contiguous run of TPT tokens).
-template <int DK, int C, int VT, typename Tin>
-struct ChunkRegs<Gdn2Variant, DK, C, VT, Tin> {
-  using G = WyCfg<DK, C, VT, Tin>;
-  uint4 k[G::NLK], q[G::NLK], b[G::NLK], v[G::NLV], w[G::NLV];
-  float la[G::TPT];
-
-  __device__ __forceinline__ static void chan(int& c, int& part) {
-    // lanes l and l + 64/TPC (within one wave) share a channel
-    constexpr int CPW = 64 / G::TPC;            // channels per wave
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    c = wave * CPW + lane % CPW;
-    part = lane / CPW;
-  }
-
-  __device__ __forceinline__ void load(const ChunkArgs& p, int bh, size_t t0,
-                                       int valid, int v0) {
-    const Tin* kp = (const Tin*)p.k;
-    const Tin* qp = (const Tin*)p.q;
-    const Tin* bp = (const Tin*)p.b;
-    const Tin* vp = (const Tin*)p.v;
-    const Tin* wp = (const Tin*)p.w;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < G::NLK; ++i) {
-      const int e = tid + i * G::NT;
-      const uint4 z = {0u, 0u, 0u, 0u};
-      k[i] = z; q[i] = z; b[i] = z;
-      if (e < C * G::NCB) {
-        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
-        if (rr < valid) {
-          const size_t g = (t0 + rr) * DK + cc;
-          k[i] = *reinterpret_cast<const uint4*>(kp + g);
-          q[i] = *reinterpret_cast<const uint4*>(qp + g);
-          b[i] = *reinterpret_cast<const uint4*>(bp + g);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < G::NLV; ++i) {
-      const int e = tid + i * G::NT;
-      const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
-      v[i] = uint4{0u, 0u, 0u, 0u};
-      w[i] = v[i];
-      if (e < C * VT / G::VEC && rr < valid) {
-        const size_t g = (t0 + rr) * p.Dv + v0 + cc;
-        v[i] = *reinterpret_cast<const uint4*>(vp + g);
-        w[i] = *reinterpret_cast<const uint4*>(wp + g);
-      }
-    }
-    int c, part;
-    chan(c, part);
-#pragma unroll
-    for (int m = 0; m < G::TPT; ++m) {
-      const int t = part * G::TPT + m;
-      la[m] = (t < valid) ? p.log_alpha[(t0 + t) * DK + c] : 0.f;
-    }
-  }
-
-  __device__ __forceinline__ void store(const SmemPtrs& s) const {
-    Tin* Xs = (Tin*)s.X;
-    Tin* Ys = (Tin*)s.Y;
-    Tin* Qs = (Tin*)s.Q;
-    Tin* Zs = (Tin*)s.Z;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < G::NLK; ++i) {
-      const int e = tid + i * G::NT;
-      if (e < C * G::NCB) {
-        const int rr = e / G::NCB, cc = (e % G::NCB) * G::VEC;
-        *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = k[i];
-        *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
-        *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = b[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < G::NLV; ++i) {
-      const int e = tid + i * G::NT;
-      if (e < C * VT / G::VEC) {
-        const int rr = e / (VT / G::VEC), cc = (e % (VT / G::VEC)) * G::VEC;
+      if (e < NVB) {
+        const int rr = e / (DV / VEC), cc = (e % (DV / VEC)) * VEC;
         const Tin* vv = reinterpret_cast<const Tin*>(&v[i]);
-        const Tin* ww = reinterpret_cast<const Tin*>(&w[i]);
-        Tin zz[G::VEC];
+        Tin zz[VEC];
+        if constexpr (kGdn2) {
+          const Tin* ww = reinterpret_cast<const Tin*>(&w[i]);
 #pragma unroll
-        for (int u = 0; u < G::VEC; ++u)
-          zz[u] = from_f32<Tin>(to_f32(ww[u]) * to_f32(vv[u]));
-        *reinterpret_cast<uint4*>(Zs + rr * VT + cc) =
-            *reinterpret_cast<const uint4*>(zz);
+          for (int u = 0; u < VEC; ++u) zz[u] = from_f32<Tin>(to_f32(ww[u]) * to_f32(vv[u]));
+        } else {
+#pragma unroll
+          for (int u = 0; u < VEC; ++u) zz[u] = from_f32<Tin>(bv[i] * to_f32(vv[u]));
+        }
+        *reinterpret_cast<uint4*>(Zs + rr * G::LDV + cc) = *reinterpret_cast<const uint4*>(zz);
       }
     }
-    if (tid < C) s.rs[tid] = 1.f;
-  }
-
-  // Decay pass (after the raw operands are in LDS): cumulative log decay per
-  // channel, then X = k/gamma, Y = gamma*b*k, Q = gamma*q in place, and the
-  // exit decay g = gamma_C (the exit keys are X' = X diag(g)).
-  __device__ __forceinline__ void transform(const SmemPtrs& s) const {
-    Tin* Xs = (Tin*)s.X;
-    Tin* Ys = (Tin*)s.Y;
-    Tin* Qs = (Tin*)s.Q;
-    constexpr int CPW = 64 / G::TPC;
-    int c, part;
-    chan(c, part);
-    // prefix of log alpha: within this thread's run, then across the runs
-    float lam[G::TPT];
-    float run = 0.f;
-#pragma unroll
-    for (int m = 0; m < G::TPT; ++m) {
-      run += la[m];
-      lam[m] = run;
-    }
-    float incl = run;  // inclusive prefix over the runs of this channel
-#pragma unroll
-    for (int d = 1; d < G::TPC; d <<= 1) {
-      const float y = __shfl_up(incl, d * CPW, 64);
-      if (part >= d) incl += y;
-    }
-    const float excl = incl - run;
-    const float total = __shfl(incl, (G::TPC - 1) * CPW + (threadIdx.x & 63) % CPW, 64);
-    const float gC = __expf(total);
-    // Batches of BT tokens: all loads of a batch are issued before its
-    // arithmetic and stores; 1/gamma by the hardware reciprocal.
-    constexpr int BT = G::TPT >= 8 ? 8 : G::TPT;
-#pragma unroll
-    for (int m0 = 0; m0 < G::TPT; m0 += BT) {
-      const int tb0 = part * G::TPT + m0;
-      float kk[BT], bb[BT], qq[BT];
-#pragma unroll
-      for (int u = 0; u < BT; ++u) {
-        kk[u] = to_f32(Xs[(tb0 + u) * G::LDK + c]);
-        bb[u] = to_f32(Ys[(tb0 + u) * G::LDK + c]);
-        qq[u] = to_f32(Qs[(tb0 + u) * G::LDK + c]);
-      }
-#pragma unroll
-      for (int u = 0; u < BT; ++u) {
-        const float l = excl + lam[m0 + u];
-        const float gam = __expf(l);
-        const float igam = __builtin_amdgcn_rcpf(gam);
-        Xs[(tb0 + u) * G::LDK + c] = from_f32<Tin>(kk[u] * igam);
-        Ys[(tb0 + u) * G::LDK + c] = from_f32<Tin>(gam * bb[u] * kk[u]);
-        Qs[(tb0 + u) * G::LDK + c] = from_f32<Tin>(gam * qq[u]);
-      }
-    }
-    if (part == 0) s.g[c] = gC;
   }
 };
 
-// ---------------------------------------------------------------------------
-// The engine
-// ---------------------------------------------------------------------------
-template <class V, int DK, int C, int VT, typename Tin>
-__global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
-  using G = WyCfg<DK, C, VT, Tin>;
+// Persistent: workgroup g takes chunks g, g + gridDim.x, ... and fetches the
+// next chunk's operands while the current one computes.
+template <class V, int DK, int DV, int C, typename Tin>
+__global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
+                                                      WyBufs<Tin> wb) {
+  using G = PrepCfg<DK, DV, C, Tin>;
   constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
-  constexpr int LDK = G::LDK, LDC = G::LDC, LDR = G::LDR, LDS16 = G::LDS16;
-  constexpr int TB = G::TB, VB = G::VB, DB = G::DB;
+  constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDS16 = G::LDS16,
+                TB = G::TB, DB = G::DB, VBT = G::VBT, NW = G::NW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
+  Tin* Ys = reinterpret_cast<Tin*>(smem + G::oY);   // diag(rs) Y, then Wk
   Tin* Xs = reinterpret_cast<Tin*>(smem + G::oX);
-  Tin* Ys = reinterpret_cast<Tin*>(smem + G::oY);
-  Tin* Qs = reinterpret_cast<Tin*>(smem + G::oQ);
-  Tin* Ss = reinterpret_cast<Tin*>(smem + G::oS);
-  Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);
-  float* rs = reinterpret_cast<float*>(smem + G::oRS);
-  float* gC = reinterpret_cast<float*>(smem + G::oG);
-  float* Am = reinterpret_cast<float*>(smem + G::oA);
+  Tin* Qs = reinterpret_cast<Tin*>(smem + G::oQ);   // Q, then Q'
+  Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);   // diag(rs) Z, then U
   Tin* Ab = reinterpret_cast<Tin*>(smem + G::oAb);
   Tin* Tb = reinterpret_cast<Tin*>(smem + G::oTb);
+  Tin* Pb = reinterpret_cast<Tin*>(smem + G::oPb);
+  float* Am = reinterpret_cast<float*>(smem + G::oA);
   Tin* Ysc = reinterpret_cast<Tin*>(smem + G::oYs);
-  Tin* Pb = reinterpret_cast<Tin*>(smem + G::oP);
-  Tin* Rm = reinterpret_cast<Tin*>(smem + G::oR);
-  Tin* Wm = reinterpret_cast<Tin*>(smem + G::oW);
-  const SmemPtrs sp{Xs, Ys, Qs, Zs, rs, gC};
+  float* gC = reinterpret_cast<float*>(smem + G::oG);
 
-  const int T = p.T, Dv = p.Dv;
-  const int nvt = Dv / VT;
-  // XCD-aware numbering: workgroups go round-robin over the 8 XCDs; keep all
-  // value tiles of one (batch, head) on one XCD so they share its L2.
-  int lin = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int bh = lin / nvt, vt = lin - bh * nvt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int v0 = vt * VT;
-  const size_t row0 = (size_t)bh * T;
+  const int total = p.B * p.H * nchunks;
   const Tin zero = from_f32<Tin>(0.f);
-  Tin* o = (Tin*)p.o;
 
-  // Blocks above the diagonal of T and P stay zero.
+  // Blocks above the diagonal of T and P are zero (and never written).
   for (int e = tid; e < C * C; e += G::NT) {
     const int rr = e / C, cc = e % C;
     if ((cc >> 4) > (rr >> 4)) {
@@ -362,157 +247,168 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
     }
   }
 
-  // Persistent state slice S[v][dk] (v in this tile), fp32, MFMA layout.
-  // OSDN stores the state [Dv][Dk]; GDN-2 stores it [Dk][Dv].
-  auto sidx = [&](int vv, int kk) -> size_t {
-    return kGdn2 ? ((size_t)bh * DK + kk) * Dv + v0 + vv
-                 : ((size_t)bh * Dv + v0 + vv) * DK + kk;
-  };
-  f32x4 Sacc[G::NS];
-#pragma unroll
-  for (int vb = 0; vb < VB; ++vb) {
-#pragma unroll
-    for (int u = 0; u < G::DPW; ++u) {
-      const int db = wave * G::DPW + u;
-      f32x4& acc = Sacc[vb * G::DPW + u];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = 0.f;
-        if (db < DB && p.S0)
-          x = p.S0[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())];
-        acc[i] = x;
-      }
-      if (db < DB) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
-              from_f32<Tin>(acc[i]);
-      }
-    }
-  }
-
-  const int nchunks = (T + C - 1) / C;
-  ChunkRegs<V, DK, C, VT, Tin> regs;
-  if (nchunks > 0) regs.load(p, bh, row0, min(C, T), v0);
-
-  for (int j = 0; j < nchunks; ++j) {
-    const size_t t0 = row0 + (size_t)j * C;
-    const int valid = min(C, T - j * C);
-    // ---- S1: operands of chunk j into LDS; prefetch chunk j+1 -------------
-    regs.store(sp);
+  PrepRegs<V, DK, DV, C, Tin> regs;
+  if ((int)blockIdx.x < total) regs.load(p, blockIdx.x, nchunks);
+  for (int n = blockIdx.x; n < total; n += gridDim.x) {
+    regs.store(Ys, Xs, Qs, Zs);
     if constexpr (kGdn2) {
+      // Decay pass: TPC threads per channel c (lanes l and l + 64/TPC of one
+      // wave), each over TPT consecutive tokens. Cumulative log decay within
+      // the chunk, then X = k/gamma, Y = gamma*b*k, Q = gamma*q in place and
+      // the exit decay g = gamma_C.
+      constexpr int TPC = G::TPC, TPT = G::TPT, CPW = 64 / TPC;
+      const int c = wave * CPW + lane % CPW, part = lane / CPW;
       __syncthreads();
-      regs.transform(sp);
+      float lam[TPT];
+      float run = 0.f;
+  #pragma unroll
+      for (int m = 0; m < TPT; ++m) {
+        run += regs.la[m];
+        lam[m] = run;
+      }
+      float incl = run;
+  #pragma unroll
+      for (int d = 1; d < TPC; d <<= 1) {
+        const float y = __shfl_up(incl, d * CPW, 64);
+        if (part >= d) incl += y;
+      }
+      const float excl = incl - run;
+      const float total_la = __shfl(incl, (TPC - 1) * CPW + lane % CPW, 64);
+      constexpr int BT = TPT >= 8 ? 8 : TPT;
+  #pragma unroll
+      for (int m0 = 0; m0 < TPT; m0 += BT) {
+        const int tb0 = part * TPT + m0;
+        float kk[BT], bb[BT], qq[BT];
+  #pragma unroll
+        for (int u = 0; u < BT; ++u) {
+          kk[u] = to_f32(Xs[(tb0 + u) * LDK + c]);
+          bb[u] = to_f32(Ys[(tb0 + u) * LDK + c]);
+          qq[u] = to_f32(Qs[(tb0 + u) * LDK + c]);
+        }
+  #pragma unroll
+        for (int u = 0; u < BT; ++u) {
+          const float gam = __expf(excl + lam[m0 + u]);
+          const float igam = __builtin_amdgcn_rcpf(gam);
+          Xs[(tb0 + u) * LDK + c] = from_f32<Tin>(kk[u] * igam);
+          Ys[(tb0 + u) * LDK + c] = from_f32<Tin>(gam * bb[u] * kk[u]);
+          Qs[(tb0 + u) * LDK + c] = from_f32<Tin>(gam * qq[u]);
+        }
+      }
+      if (part == 0) gC[c] = __expf(total_la);
     }
-    if (j + 1 < nchunks)
-      regs.load(p, bh, t0 + C, min(C, T - (j + 1) * C), v0);
+    if (n + (int)gridDim.x < total) regs.load(p, n + gridDim.x, nchunks);
     __syncthreads();
 
-    // ---- S2: Gram A, scores P, RHS = rs (Z - Y S0^T), Q S0^T; diagonal
-    // blocks of T. Wave w owns the 16-row block w: its read-key and query
-    // fragments stay in registers across all tiles of the row.
-    f32x4 Oacc[VB];
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) Oacc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave < TB) {
-      const int rb = wave;
-      Frag<DK, Tin> fy, fq;
-      fy.load(Ys + rb * 16 * LDK, LDK);
-      fq.load(Qs + rb * 16 * LDK, LDK);
-      float rsr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rsr[i] = rs[rb * 16 + acc_row(i)];
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        if (b <= rb) {
-          Frag<DK, Tin> fx;
-          fx.load(Xs + b * 16 * LDK, LDK);
-          f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
-          mma(aa, fy, fx);
-          mma(pa, fq, fx);
-          if (b < rb) {
-            // off-diagonal tile: operand copy for the doubling merges
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int rr = rb * 16 + acc_row(i), cc = b * 16 + acc_col();
-              Ab[rr * LDC + cc] = from_f32<Tin>(rsr[i] * aa[i]);
-              Pb[rr * LDC + cc] = from_f32<Tin>(pa[i]);
+    // ---- Gram A, scores P, diagonal blocks of T; X' fragments ---------------
+    // Jobs: the TB diagonal tiles first (job b on wave b, which then inverts
+    // its block), then the off-diagonal lower tiles in row-major order.
+    {
+      constexpr int NL = TB * (TB + 1) / 2;
+      for (int job = wave; job < NL; job += NW) {
+        int a, b;
+        if (job < TB) {
+          a = b = job;
+        } else {
+          int l = job - TB;
+          a = 1;
+          while (l >= a) { l -= a; ++a; }
+          b = l;
+        }
+        Frag<DK, Tin> fy, fq, fx;
+        fy.load(Ys + a * 16 * LDK, LDK);
+        fq.load(Qs + a * 16 * LDK, LDK);
+        fx.load(Xs + b * 16 * LDK, LDK);
+        f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+        mma(aa, fy, fx);
+        mma(pa, fq, fx);
+        if (a > b) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = a * 16 + acc_row(i), cc = b * 16 + acc_col();
+            Ab[rr * LDC + cc] = from_f32<Tin>(aa[i]);
+            Pb[rr * LDC + cc] = from_f32<Tin>(pa[i]);
+          }
+        } else {
+          // diagonal tile: A in fp32, transposed, strictly lower part only
+          float4 col;
+          col.x = acc_row(0) > acc_col() ? aa[0] : 0.f;
+          col.y = acc_row(1) > acc_col() ? aa[1] : 0.f;
+          col.z = acc_row(2) > acc_col() ? aa[2] : 0.f;
+          col.w = acc_row(3) > acc_col() ? aa[3] : 0.f;
+          float* Ad = Am + a * 16 * G::LDD;
+          *reinterpret_cast<float4*>(Ad + acc_col() * G::LDD + acc_row(0)) = col;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = a * 16 + acc_row(i), cc = a * 16 + acc_col();
+            Pb[rr * LDC + cc] = from_f32<Tin>(cc <= rr ? pa[i] : 0.f);
+          }
+          // T's diagonal block by forward substitution: lane c < 16 owns
+          // column c; pending sums are updated as soon as each entry is final.
+          wave_lds_sync();
+          if (lane < 16) {
+            const int c = lane;
+            float x[16], sv[16];
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = (i == c) ? 1.f : 0.f;
+  #pragma unroll
+            for (int m = 0; m < 16; ++m) {
+              x[m] = sv[m];
+              float cv[16];
+  #pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(Ad + m * G::LDD + 4 * q4);
+                cv[4 * q4] = v4.x; cv[4 * q4 + 1] = v4.y;
+                cv[4 * q4 + 2] = v4.z; cv[4 * q4 + 3] = v4.w;
+              }
+  #pragma unroll
+              for (int i = m + 1; i < 16; ++i) sv[i] -= cv[i] * x[m];
+            }
+  #pragma unroll
+            for (int i = 0; i < 16; ++i)
+              Tb[(a * 16 + i) * LDC + a * 16 + c] = from_f32<Tin>(x[i]);
+          }
+        }
+      }
+      // X' = X diag(g) as k-major fragments, one channel block per job
+      const size_t xoff = (size_t)n * C * DK;
+      for (int db = wave; db < DB; db += NW) {
+        Frag<C, Tin> fx;
+        fx.load_kmajor(Xs + db * 16, LDK);
+        if constexpr (kGdn2) {
+          const float gd = gC[db * 16 + (lane & 15)];
+          if constexpr (sizeof(Tin) == 2) {
+  #pragma unroll
+            for (int i = 0; i < Frag<C, Tin>::N32; ++i)
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) fx.v[i][e] = (__bf16)((float)fx.v[i][e] * gd);
+            if constexpr (Frag<C, Tin>::R16) {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) fx.t[e] = (__bf16)((float)fx.t[e] * gd);
             }
           } else {
-            // diagonal tile: fp32, transposed, strictly lower part only
-            float4 col;
-            col.x = acc_row(0) > acc_col() ? rsr[0] * aa[0] : 0.f;
-            col.y = acc_row(1) > acc_col() ? rsr[1] * aa[1] : 0.f;
-            col.z = acc_row(2) > acc_col() ? rsr[2] * aa[2] : 0.f;
-            col.w = acc_row(3) > acc_col() ? rsr[3] * aa[3] : 0.f;
-            *reinterpret_cast<float4*>(Am + (rb * 16 + acc_col()) * G::LDD +
-                                       acc_row(0)) = col;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int rr = rb * 16 + acc_row(i), cc = b * 16 + acc_col();
-              Pb[rr * LDC + cc] = from_f32<Tin>(cc <= rr ? pa[i] : 0.f);
-            }
+  #pragma unroll
+            for (int i = 0; i < C / 4; ++i) fx.v[i] *= gd;
           }
         }
+        fx.store_global(wb.xp + xoff + (size_t)db * 16 * C);
       }
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        Frag<DK, Tin> fs;
-        fs.load(Ss + vb * 16 * LDK, LDK);
-        f32x4 ka = {0.f, 0.f, 0.f, 0.f};
-        mma(ka, fy, fs);
-        mma(Oacc[vb], fq, fs);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = rb * 16 + acc_row(i), cc = vb * 16 + acc_col();
-          Rm[rr * LDR + cc] =
-              from_f32<Tin>(rsr[i] * (to_f32(Zs[rr * VT + cc]) - ka[i]));
-        }
-      }
-      // Diagonal block rb of T = (I + A)^-1 by fp32 forward substitution:
-      // lane c < 16 owns column c; pending sums are updated as soon as each
-      // entry is final, so the dependent chain is 15 FMAs long. Column m of
-      // the block is read as four broadcast 16-byte loads. The block was
-      // written by this wave, so only a wave-level LDS ordering is needed.
-      wave_lds_sync();
-      if (lane < 16) {
-        const int c = lane;
-        const float* Acol = Am + rb * 16 * G::LDD;
-        float x[16], sv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sv[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          x[m] = sv[m];
-          float col[16];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(Acol + m * G::LDD + 4 * q4);
-            col[4 * q4] = v4.x; col[4 * q4 + 1] = v4.y;
-            col[4 * q4 + 2] = v4.z; col[4 * q4 + 3] = v4.w;
-          }
-#pragma unroll
-          for (int i = m + 1; i < 16; ++i) sv[i] -= col[i] * x[m];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          Tb[(rb * 16 + i) * LDC + rb * 16 + c] = from_f32<Tin>(x[i]);
+      if constexpr (kGdn2) {
+        if (tid < DK) wb.g[(size_t)n * DK + tid] = gC[tid];
       }
     }
     __syncthreads();
 
-    // ---- S4: recursive doubling, T21 = -T22 (A21 T11) ----------------------
-    // One job = one 16-wide column of T21 in one pair: the wave computes that
-    // column of Y = A21 T11 (into its own scratch, row-major) and then the
-    // same column of T21 = -T22 Y, so the two stages need no barrier between
-    // them. The right operands (T11, Y) are read k-major.
+    // ---- recursive doubling, T21 = -T22 (A21 T11) ----------------------------
+    // One job = one 16-wide column of T21 in one pair: that column of
+    // Y = A21 T11 goes to the wave's own scratch (row-major), then the same
+    // column of T21 = -T22 Y; the right operands are read k-major.
     {
       Tin* ys = Ysc + wave * (C / 2) * LDS16;
-#pragma unroll
+  #pragma unroll
       for (int s = 16; s < C; s *= 2) {
         const int nt = s / 16;
         const int jobs = (C / (2 * s)) * nt;
-        for (int job = wave; job < jobs; job += G::NW) {
+        for (int job = wave; job < jobs; job += NW) {
           const int pp = job / nt, c = job % nt;
           const int rb = 2 * s * pp + s, cb = 2 * s * pp;
           for (int r = 0; r < nt; ++r) {
@@ -523,7 +419,7 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
               fb.load_kmajor(Tb + (cb + kk) * LDC + cb + c * 16, LDC);
               mma(acc, fa, fb);
             }
-#pragma unroll
+  #pragma unroll
             for (int i = 0; i < 4; ++i)
               ys[(r * 16 + acc_row(i)) * LDS16 + acc_col()] = from_f32<Tin>(acc[i]);
           }
@@ -536,97 +432,373 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
               fb.load_kmajor(ys + kk * LDS16, LDS16);
               mma(acc, fa, fb);
             }
-#pragma unroll
+  #pragma unroll
             for (int i = 0; i < 4; ++i)
               Tb[(rb + r * 16 + acc_row(i)) * LDC + cb + c * 16 + acc_col()] =
                   from_f32<Tin>(-acc[i]);
           }
-          // the scratch is rewritten by this wave's next job
-          wave_lds_sync();
+          wave_lds_sync();  // the scratch is rewritten by this wave's next job
         }
         __syncthreads();
       }
     }
 
-    // ---- S5: W = T RHS (row-major [C][VT]) --------------------------------
-    for (int job = wave; job < TB * VB; job += G::NW) {
-      const int tb = job / VB, vb = job % VB;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      Frag<C, Tin> ft, fr;
-      ft.load(Tb + tb * 16 * LDC, LDC);
-      fr.load_kmajor(Rm + vb * 16, LDR);
-      mma(acc, ft, fr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Wm[(tb * 16 + acc_row(i)) * LDR + vb * 16 + acc_col()] = from_f32<Tin>(acc[i]);
-    }
-    __syncthreads();
-
-    // ---- S6: O += P W (store), S = S diag(g) + W^T X' -----------------------
-    if (wave < TB) {
-      const int tb = wave;
-      Frag<C, Tin> fp;
-      fp.load(Pb + tb * 16 * LDC, LDC);
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        Frag<C, Tin> fw;
-        fw.load_kmajor(Wm + vb * 16, LDR);
-        mma(Oacc[vb], fp, fw);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = tb * 16 + acc_row(i);
-          if (rr < valid)
-            o[(t0 + rr) * Dv + v0 + vb * 16 + acc_col()] =
-                from_f32<Tin>(p.scale * Oacc[vb][i]);
+    // ---- Wk = T diag(rs) Y and U = T diag(rs) Z, in place ----------------------
+    // One job = one 16-wide column block of Y (or Z), all row blocks; only the
+    // job's own wave reads that column block, so it is overwritten in place.
+    const size_t uoff = (size_t)n * C * DV;
+    {
+      Frag<C, Tin> ft[TB];
+  #pragma unroll
+      for (int tb = 0; tb < TB; ++tb) ft[tb].load(Tb + tb * 16 * LDC, LDC);
+      for (int job = wave; job < DB + VBT; job += NW) {
+        const bool isU = job >= DB;
+        const int ct = isU ? job - DB : job;
+        Tin* M = isU ? Zs : Ys;
+        const int ld = isU ? LDV : LDK;
+        Frag<C, Tin> fm;
+        fm.load_kmajor(M + ct * 16, ld);
+        f32x4 acc[TB];
+  #pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          mma(acc[tb], ft[tb], fm);
+        }
+  #pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            M[(tb * 16 + acc_row(i)) * ld + ct * 16 + acc_col()] = from_f32<Tin>(acc[tb][i]);
+          if (isU) acc_store(acc[tb], wb.u + uoff + (size_t)(tb * VBT + ct) * 256);
         }
       }
     }
-    // State tiles (vb, db): wave w takes a contiguous run of db for every vb,
-    // so each W^T and X fragment is loaded once per wave; both are read
-    // k-major (token rows) from their row-major tiles. GDN-2 applies the exit
-    // decay after the product: g (S + W^T X) = S diag(g) + W^T X'.
+    __syncthreads();
+
+    // ---- Q' = Q - P Wk (in place) and O' = P U ------------------------------
     {
-      constexpr int DPW = G::DPW;
-      Frag<C, Tin> fw[VB];
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) fw[vb].load_kmajor(Wm + vb * 16, LDR);
-#pragma unroll
-      for (int u = 0; u < DPW; ++u) {
-        const int db = wave * DPW + u;
-        if (db < DB) {
-          Frag<C, Tin> fx;
-          fx.load_kmajor(Xs + db * 16, LDK);
-#pragma unroll
-          for (int vb = 0; vb < VB; ++vb) {
-            f32x4& acc = Sacc[vb * G::DPW + u];
-            mma(acc, fw[vb], fx);
-            if constexpr (kGdn2) {
-              const float gd = gC[db * 16 + acc_col()];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[i] *= gd;
+      Frag<C, Tin> fp[TB];
+  #pragma unroll
+      for (int tb = 0; tb < TB; ++tb) fp[tb].load(Pb + tb * 16 * LDC, LDC);
+      for (int job = wave; job < DB + VBT; job += NW) {
+        const bool isO = job >= DB;
+        const int ct = isO ? job - DB : job;
+        Frag<C, Tin> fm;
+        if (isO)
+          fm.load_kmajor(Zs + ct * 16, LDV);
+        else
+          fm.load_kmajor(Ys + ct * 16, LDK);
+  #pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          mma(acc, fp[tb], fm);
+          if (isO) {
+            acc_store(acc, wb.op + uoff + (size_t)(tb * VBT + ct) * 256);
+          } else {
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              Tin* qe = Qs + (tb * 16 + acc_row(i)) * LDK + ct * 16 + acc_col();
+              *qe = from_f32<Tin>(to_f32(*qe) - acc[i]);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] =
-                  from_f32<Tin>(acc[i]);
           }
         }
       }
     }
     __syncthreads();
+
+    // ---- Wk and Q' as row-block fragments -------------------------------------
+    {
+      const size_t koff = (size_t)n * C * DK;
+      for (int job = wave; job < 2 * TB; job += NW) {
+        const int tb = job % TB;
+        const bool isQ = job >= TB;
+        Frag<DK, Tin> f;
+        f.load((isQ ? Qs : Ys) + tb * 16 * LDK, LDK);
+        f.store_global((isQ ? wb.qp : wb.wk) + koff + (size_t)tb * 16 * DK);
+      }
+    }
+    __syncthreads();  // the next chunk's operands overwrite the tiles
   }
+}
+
+// ---------------------------------------------------------------------------
+// scan
+// ---------------------------------------------------------------------------
+template <int DK, int C, int VT, typename Tin>
+struct ScanCfg {
+  static constexpr int NW = 4, NT = 256;
+  static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
+  static constexpr int LDK = DK + PAD, LDR = VT + PAD;
+  static constexpr int TB = C / 16, VB = VT / 16, DB = DK / 16;
+  static constexpr size_t E = sizeof(Tin);
+  static constexpr size_t oS = 0;
+  static constexpr size_t oW = oS + (size_t)VT * LDK * E;
+  static constexpr size_t bytes = oW + (size_t)C * LDR * E;
+  // State tiles per wave: every value tile times a contiguous run of DPW
+  // channel tiles.
+  static constexpr int DPW = (DB + NW - 1) / NW;
+  static constexpr int NS = VB * DPW;
+  static_assert(TB <= NW, "one row block per wave");
+};
+
+// Accumulator tile in the storage dtype, as fetched (converted at use, so
+// that a prefetch is not waited on when it is issued).
+template <typename Tin>
+struct RawTile;
+template <>
+struct RawTile<__bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ void load(const __bf16* base) {
+    v = *reinterpret_cast<const bf16x4*>(base + (threadIdx.x & 63) * 4);
+  }
+  __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
+};
+template <>
+struct RawTile<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* base) {
+    v = *reinterpret_cast<const f32x4*>(base + (threadIdx.x & 63) * 4);
+  }
+  __device__ __forceinline__ float operator[](int i) const { return v[i]; }
+};
+
+template <bool GDN2, int DK, int C, int VT, typename Tin>
+struct ScanRegs {
+  using G = ScanCfg<DK, C, VT, Tin>;
+  Frag<DK, Tin> wk, qp;
+  RawTile<Tin> u[G::VB], op[G::VB];
+  Frag<C, Tin> x[G::DPW];
+  float gd[G::DPW];
+
+  // Lane-interleaved copy in LDS (16-byte word w of lane l at [w][l]), one
+  // region per wave: the hand-off between the chunk step that fetches the
+  // operands and the step that uses them.
+  template <int K>
+  static constexpr size_t fbytes() {
+    if constexpr (sizeof(Tin) == 2)
+      return (size_t)(K / 32) * 16 + ((K % 32) ? 8 : 0);
+    else
+      return (size_t)K;   // K/4 floats
+  }
+  static constexpr size_t BYTES = 2 * fbytes<DK>() + 2 * G::VB * sizeof(RawTile<Tin>) +
+                                  G::DPW * fbytes<C>() + G::DPW * sizeof(float);
+  static constexpr int WORDS = (int)((BYTES + 15) / 16);
+
+  template <int K>
+  __device__ __forceinline__ static void put(unsigned char* b, size_t& o, const Frag<K, Tin>& f) {
+    __builtin_memcpy(b + o, &f.v, fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0));
+    o += fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0);
+    if constexpr (sizeof(Tin) == 2) {
+      if constexpr (Frag<K, Tin>::R16) { __builtin_memcpy(b + o, &f.t, 8); o += 8; }
+    }
+  }
+  template <int K>
+  __device__ __forceinline__ static void get(const unsigned char* b, size_t& o, Frag<K, Tin>& f) {
+    __builtin_memcpy(&f.v, b + o, fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0));
+    o += fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0);
+    if constexpr (sizeof(Tin) == 2) {
+      if constexpr (Frag<K, Tin>::R16) { __builtin_memcpy(&f.t, b + o, 8); o += 8; }
+    }
+  }
+  __device__ __forceinline__ void stash(uint4* base) const {
+    uint4 w[WORDS];
+    unsigned char* b = reinterpret_cast<unsigned char*>(w);
+    size_t o = 0;
+    put<DK>(b, o, wk);
+    put<DK>(b, o, qp);
+    __builtin_memcpy(b + o, u, sizeof(u)); o += sizeof(u);
+    __builtin_memcpy(b + o, op, sizeof(op)); o += sizeof(op);
+#pragma unroll
+    for (int d = 0; d < G::DPW; ++d) put<C>(b, o, x[d]);
+    __builtin_memcpy(b + o, gd, sizeof(gd)); o += sizeof(gd);
+    for (; o < (size_t)WORDS * 16; ++o) b[o] = 0;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) base[i * 64 + lane] = w[i];
+  }
+  __device__ __forceinline__ void unstash(const uint4* base) {
+    uint4 w[WORDS];
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) w[i] = base[i * 64 + lane];
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(w);
+    size_t o = 0;
+    get<DK>(b, o, wk);
+    get<DK>(b, o, qp);
+    __builtin_memcpy(u, b + o, sizeof(u)); o += sizeof(u);
+    __builtin_memcpy(op, b + o, sizeof(op)); o += sizeof(op);
+#pragma unroll
+    for (int d = 0; d < G::DPW; ++d) get<C>(b, o, x[d]);
+    __builtin_memcpy(gd, b + o, sizeof(gd));
+  }
+
+  // Loads are unconditional (indices of idle waves clamped into range), so
+  // that the compiler can count them and a prefetch is only waited on where
+  // its data is used.
+  __device__ __forceinline__ void load(const WyBufs<Tin>& wb, size_t n, int Dv,
+                                       int vt, int wave) {
+    constexpr int VB = G::VB;
+    const int VBT = Dv / 16;
+    const int tb = min(wave, G::TB - 1);
+    const size_t koff = n * C * DK + (size_t)tb * 16 * DK;
+    wk.load_global(wb.wk + koff);
+    qp.load_global(wb.qp + koff);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      const size_t uo = n * C * Dv + (size_t)(tb * VBT + vt * VB + vb) * 256;
+      u[vb].load(wb.u + uo);
+      op[vb].load(wb.op + uo);
+    }
+#pragma unroll
+    for (int d = 0; d < G::DPW; ++d) {
+      const int db = min(wave * G::DPW + d, G::DB - 1);
+      x[d].load_global(wb.xp + n * C * DK + (size_t)db * 16 * C);
+      if constexpr (GDN2) gd[d] = wb.g[n * DK + db * 16 + (threadIdx.x & 15)];
+    }
+  }
+};
+
+template <bool GDN2, int DK, int C, int VT, typename Tin>
+__global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
+                                                      WyBufs<Tin> wb) {
+  using G = ScanCfg<DK, C, VT, Tin>;
+  using R = ScanRegs<GDN2, DK, C, VT, Tin>;
+  constexpr int LDK = G::LDK, LDR = G::LDR, TB = G::TB, VB = G::VB, DB = G::DB,
+                DPW = G::DPW;
+  // hand-off stage: NW per-wave regions after the state and W tiles. A
+  // wave reads its region at the start of a step and refills it at the end
+  // (LDS operations of one wave complete in order).
+  constexpr size_t kStage = (size_t)R::WORDS * 64 * 16 * G::NW;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes + kStage];
+  Tin* Ss = reinterpret_cast<Tin*>(smem + G::oS);   // state copy [v][dk]
+  Tin* Wm = reinterpret_cast<Tin*>(smem + G::oW);   // W [C][VT]
+  uint4* stage = reinterpret_cast<uint4*>(smem + G::bytes) +
+                 (size_t)(threadIdx.x >> 6) * R::WORDS * 64;
+
+  const int T = p.T, Dv = p.Dv;
+  const int nvt = Dv / VT;
+  // XCD-aware numbering: workgroups go round-robin over the 8 XCDs; keep all
+  // value tiles of one (batch, head) on one XCD so they share its L2.
+  int lin = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int bh = lin / nvt, vt = lin - bh * nvt;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int v0 = vt * VT;
+  Tin* o = (Tin*)p.o;
+
+  // Persistent state slice S[v][dk] (v in this tile), fp32, MFMA layout.
+  // OSDN stores the state [Dv][Dk]; GDN-2 stores it [Dk][Dv].
+  auto sidx = [&](int vv, int kk) -> size_t {
+    return GDN2 ? ((size_t)bh * DK + kk) * Dv + v0 + vv
+                : ((size_t)bh * Dv + v0 + vv) * DK + kk;
+  };
+  f32x4 Sacc[G::NS];
+#pragma unroll
+  for (int vb = 0; vb < VB; ++vb) {
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int db = wave * DPW + d;
+      f32x4& acc = Sacc[vb * DPW + d];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = 0.f;
+        if (db < DB && p.S0) x = p.S0[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())];
+        acc[i] = x;
+      }
+      if (db < DB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] = from_f32<Tin>(acc[i]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // One chunk step; TAIL: the chunk may be partial (rows past T are not
+  // stored). The operands of chunk j wait in the stage; those of chunk j + 1
+  // are fetched at the start and handed to the stage at the end, where their
+  // arrival is awaited. Guards that always hold for the tile
+  // configuration fold away at compile time.
+  constexpr bool kAllRowWaves = TB == G::NW, kAllColWaves = DPW * G::NW == DB;
+  const size_t n0 = (size_t)bh * nchunks;
+  auto step = [&](int j, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const size_t t0 = (size_t)bh * T + (size_t)j * C;
+    const int valid = min(C, T - j * C);
+    R nxt;
+    const bool more = j + 1 < nchunks;
+    if (more) nxt.load(wb, n0 + j + 1, Dv, vt, wave);
+    R cur;
+    cur.unstash(stage);
+    // ---- W = U - Wk S0^T (to LDS), O = O' + Q' S0^T (stored) --------------
+    if (kAllRowWaves || wave < TB) {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        Frag<DK, Tin> fs;
+        fs.load(Ss + vb * 16 * LDK, LDK);
+        f32x4 wa = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+        mma(wa, cur.wk, fs);
+        mma(oa, cur.qp, fs);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = wave * 16 + acc_row(i);
+          Wm[rr * LDR + vb * 16 + acc_col()] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
+          if (!TAIL || rr < valid)
+            o[(t0 + rr) * Dv + v0 + vb * 16 + acc_col()] =
+                from_f32<Tin>(p.scale * (cur.op[vb][i] + oa[i]));
+        }
+      }
+    }
+    __syncthreads();
+    // ---- S = S diag(g) + W^T X' -----------------------------------------------
+    {
+      Frag<C, Tin> fw[VB];
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) fw[vb].load_kmajor(Wm + vb * 16, LDR);
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int db = wave * DPW + d;
+        if (kAllColWaves || db < DB) {
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb) {
+            f32x4& acc = Sacc[vb * DPW + d];
+            if constexpr (GDN2) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[i] *= cur.gd[d];
+            }
+            mma(acc, fw[vb], cur.x[d]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] = from_f32<Tin>(acc[i]);
+          }
+        }
+      }
+    }
+    if (more) nxt.stash(stage);
+    __syncthreads();
+  };
+
+  if (nchunks > 0) {
+    R first;
+    first.load(wb, n0, Dv, vt, wave);
+    first.stash(stage);
+  }
+  __syncthreads();
+  const int nfull = T / C;  // chunks with C valid rows
+  for (int j = 0; j < nfull; ++j) step(j, std::false_type{});
+  if (nfull < nchunks) step(nfull, std::true_type{});
 
   if (p.ST) {
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
 #pragma unroll
-      for (int u = 0; u < G::DPW; ++u) {
-        const int db = wave * G::DPW + u;
+      for (int d = 0; d < DPW; ++d) {
+        const int db = wave * DPW + d;
         if (db < DB) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            p.ST[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())] =
-                Sacc[vb * G::DPW + u][i];
+            p.ST[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())] = Sacc[vb * DPW + d][i];
         }
       }
     }
@@ -636,35 +808,61 @@ __global__ __launch_bounds__(256) void wy_engine_kernel(ChunkArgs p) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
-template <class V, int DK, int C, int VT, typename Tin>
+// Resident prep workgroups per compute unit (LDS-limited).
+template <int DK, int DV, int C, typename Tin>
+constexpr int kPrepWgPerCu() {
+  return (int)(163840 / PrepCfg<DK, DV, C, Tin>::bytes) < 2
+             ? 1
+             : (int)(163840 / PrepCfg<DK, DV, C, Tin>::bytes);
+}
+
+// Value-tile width of the scan: 32 columns when that already gives one
+// workgroup per compute unit (256 CUs), else 16 for more parallelism.
+static int pick_vt(int BH, int Dv) { return (BH * (Dv / 32) >= 256) ? 32 : 16; }
+
+template <class V, int DK, int DV, int C, typename Tin>
 static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
-  if constexpr (!WyCfg<DK, C, VT, Tin>::fits) {
+  if constexpr (!PrepCfg<DK, DV, C, Tin>::fits) {
     return -1;
   } else {
-    const int BH = a.B * a.H;
-    dim3 grid(BH * (a.Dv / VT)), block(256);
-    hipLaunchKernelGGL((wy_engine_kernel<V, DK, C, VT, Tin>), grid, block, 0, s,
-                       a);
+    constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
+    const int BH = a.B * a.H, nch = (a.T + C - 1) / C;
+    if (BH == 0) return 0;
+    const WyBufs<Tin> wb = wy_bufs<Tin>(a.ws, BH, nch, C, DK, DV);
+    if (nch > 0) {
+      // persistent grid: a few workgroups per compute unit at most
+      const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<DK, DV, C, Tin>());
+      hipLaunchKernelGGL((wy_prep_kernel<V, DK, DV, C, Tin>), dim3(grid),
+                         dim3(512), 0, s, a, nch, wb);
+      const int rc = (int)hipGetLastError();
+      if (rc) return rc;
+    }
+    if (pick_vt(BH, DV) == 32)
+      hipLaunchKernelGGL((wy_scan_kernel<kGdn2, DK, C, 32, Tin>),
+                         dim3(BH * (DV / 32)), dim3(256), 0, s, a, nch, wb);
+    else
+      hipLaunchKernelGGL((wy_scan_kernel<kGdn2, DK, C, 16, Tin>),
+                         dim3(BH * (DV / 16)), dim3(256), 0, s, a, nch, wb);
     return (int)hipGetLastError();
   }
 }
 
-// Value-tile width: 32 columns when that already gives one workgroup per
-// compute unit (256 CUs), else 16 for more parallelism.
-static int pick_vt(int BH, int Dv) { return (BH * (Dv / 32) >= 256) ? 32 : 16; }
-
-template <class V, int DK, int C, typename Tin>
-static int launch_c(const ChunkArgs& a, hipStream_t s) {
-  if (pick_vt(a.B * a.H, a.Dv) == 32) return launch_cfg<V, DK, C, 32, Tin>(a, s);
-  return launch_cfg<V, DK, C, 16, Tin>(a, s);
+template <class V, int DK, int DV, typename Tin>
+static int launch_dv(const ChunkArgs& a, hipStream_t s) {
+  switch (a.chunk) {
+    case 16: return launch_cfg<V, DK, DV, 16, Tin>(a, s);
+    case 32: return launch_cfg<V, DK, DV, 32, Tin>(a, s);
+    case 64: return launch_cfg<V, DK, DV, 64, Tin>(a, s);
+  }
+  return -1;
 }
 
 template <class V, int DK, typename Tin>
 static int launch_dk(const ChunkArgs& a, hipStream_t s) {
-  switch (a.chunk) {
-    case 16: return launch_c<V, DK, 16, Tin>(a, s);
-    case 32: return launch_c<V, DK, 32, Tin>(a, s);
-    case 64: return launch_c<V, DK, 64, Tin>(a, s);
+  switch (a.Dv) {
+    case 32: return launch_dv<V, DK, 32, Tin>(a, s);
+    case 64: return launch_dv<V, DK, 64, Tin>(a, s);
+    case 128: return launch_dv<V, DK, 128, Tin>(a, s);
   }
   return -1;
 }
@@ -695,37 +893,47 @@ int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s) {
   return launch_variant<Gdn2Variant>(a, s);
 }
 
-template <int DK, typename Tin>
-static bool fits_dk(int chunk) {
+template <int DK, int DV, typename Tin>
+static bool fits_dv(int chunk) {
   switch (chunk) {
-    case 16: return WyCfg<DK, 16, 32, Tin>::fits && WyCfg<DK, 16, 16, Tin>::fits;
-    case 32: return WyCfg<DK, 32, 32, Tin>::fits && WyCfg<DK, 32, 16, Tin>::fits;
-    case 64: return WyCfg<DK, 64, 32, Tin>::fits && WyCfg<DK, 64, 16, Tin>::fits;
+    case 16: return PrepCfg<DK, DV, 16, Tin>::fits;
+    case 32: return PrepCfg<DK, DV, 32, Tin>::fits;
+    case 64: return PrepCfg<DK, DV, 64, Tin>::fits;
   }
   return false;
 }
 
-bool osdn_chunk_supported(int Dk, int chunk, int bf16) {
+template <int DK, typename Tin>
+static bool fits_dk(int Dv, int chunk) {
+  switch (Dv) {
+    case 32: return fits_dv<DK, 32, Tin>(chunk);
+    case 64: return fits_dv<DK, 64, Tin>(chunk);
+    case 128: return fits_dv<DK, 128, Tin>(chunk);
+  }
+  return false;
+}
+
+bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16) {
   if (bf16) {
     switch (Dk) {
-      case 32: return fits_dk<32, __bf16>(chunk);
-      case 64: return fits_dk<64, __bf16>(chunk);
-      case 128: return fits_dk<128, __bf16>(chunk);
+      case 32: return fits_dk<32, __bf16>(Dv, chunk);
+      case 64: return fits_dk<64, __bf16>(Dv, chunk);
+      case 128: return fits_dk<128, __bf16>(Dv, chunk);
     }
   } else {
     switch (Dk) {
-      case 32: return fits_dk<32, float>(chunk);
-      case 64: return fits_dk<64, float>(chunk);
-      case 128: return fits_dk<128, float>(chunk);
+      case 32: return fits_dk<32, float>(Dv, chunk);
+      case 64: return fits_dk<64, float>(Dv, chunk);
+      case 128: return fits_dk<128, float>(Dv, chunk);
     }
   }
   return false;
 }
 
-// The GDN-2 decay pass splits each chunk's tokens over 256/Dk threads per
+// The GDN-2 decay pass splits each chunk's tokens over 512/Dk threads per
 // channel, so the chunk must hold at least that many tokens.
-bool gdn2_chunk_supported(int Dk, int chunk, int bf16) {
-  return osdn_chunk_supported(Dk, chunk, bf16) && chunk >= 256 / Dk;
+bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16) {
+  return osdn_chunk_supported(Dk, Dv, chunk, bf16) && chunk >= 512 / Dk;
 }
 
 }  // namespace osdn

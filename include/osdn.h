@@ -64,8 +64,9 @@ int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype);
  * Device workspace, in bytes, that osdn_forward needs for these sizes
  * (0 if the sizes are invalid or the call needs none). The workspace holds
  * the preconditioned keys produced by phase 1 ([B,H,T,Dk] in the storage
- * dtype) followed by the phase-1 scratch (osdn_precond_workspace_bytes), and
- * its contents are only meaningful during one call.
+ * dtype) followed by scratch shared by the two phases (the larger of
+ * osdn_precond_workspace_bytes and osdn_chunk_workspace_bytes), and its
+ * contents are only meaningful during one call.
  */
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
@@ -134,13 +135,25 @@ int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
  * ktilde_t^T, o_t = scale * S_t q_t. ktilde is [B,H,T,Dk] in the storage dtype
  * (for OSDN, the output of osdn_precond_scan; ktilde == k gives plain
  * DeltaNet). Other arguments as in osdn_forward; ktilde is an input and must
- * not overlap any output. Needs no workspace.
+ * not overlap any output.
+ * workspace / workspace_bytes: device scratch of at least
+ * osdn_chunk_workspace_bytes(...) bytes, 256-byte aligned, not overlapping
+ * any argument.
  */
 int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
                        int dtype, const void* q, const void* k,
                        const void* ktilde, const void* v, const float* beta,
                        const float* S0, float scale, void* o, float* S_T,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Device scratch, in bytes, that osdn_chunk_forward needs (0 if the sizes
+ * are invalid or T = 0): per chunk and (batch, head), the chunk's operands
+ * that do not depend on the entry state ((3 Dk + 2 Dv) x chunk elements of
+ * the storage dtype and Dk fp32 values).
+ */
+size_t osdn_chunk_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                  int chunk, int dtype);
 
 /* 1 if (Dk, Dv, chunk, dtype) has a GDN-2 kernel instance, else 0. */
 int gdn2_forward_supported(int Dk, int Dv, int chunk, int dtype);
@@ -164,13 +177,21 @@ int gdn2_forward_supported(int Dk, int Dv, int chunk, int dtype);
  * Inside a chunk the decay is absorbed into the keys as k / gamma_t with
  * gamma_t the running product of alpha; the sum of log_alpha over one chunk
  * must stay above about -80 per channel so that 1/gamma_t is finite in fp32.
- * S_T may be exactly S0; no other overlap is allowed. Needs no workspace.
+ * S_T may be exactly S0; no other overlap is allowed.
+ * workspace / workspace_bytes: device scratch of at least
+ * gdn2_forward_workspace_bytes(...) bytes, 256-byte aligned, not overlapping
+ * any argument.
  */
 int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  const void* q, const void* k, const void* v,
                  const float* log_alpha, const void* b, const void* w,
                  const float* S0, float scale, void* o, float* S_T,
-                 void* stream);
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device scratch, in bytes, that gdn2_forward needs (as for
+ * osdn_chunk_workspace_bytes). */
+size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                    int chunk, int dtype);
 
 #ifdef __cplusplus
 }

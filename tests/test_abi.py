@@ -37,7 +37,8 @@ def test_header_declares_entry_points():
     for n in ("osdn_forward", "osdn_forward_workspace_bytes", "osdn_strerror",
               "osdn_forward_supported", "osdn_precond_scan",
               "osdn_precond_workspace_bytes",
-              "osdn_chunk_forward", "gdn2_forward", "gdn2_forward_supported"):
+              "osdn_chunk_forward", "gdn2_forward", "gdn2_forward_supported",
+              "osdn_chunk_workspace_bytes", "gdn2_forward_workspace_bytes"):
         assert n in names
 
 
@@ -80,10 +81,21 @@ def test_supported_and_workspace_sizes():
     assert L.osdn_precond_workspace_bytes(4, 16, 4096, 128, 1) == pre(64, 4096, 128)
     assert L.osdn_precond_workspace_bytes(1, 1, 0, 32, 1) == 0
     assert L.osdn_precond_workspace_bytes(1, 1, 8, 40, 1) == 0
+    # chunk engine: per chunk, Wk, Q', X' (Dk columns), U, O' (Dv columns)
+    # in the storage dtype and the exit decay (Dk fp32)
+    def wy(BH, T, Dk, Dv, C, es):
+        nc = BH * ((T + C - 1) // C)
+        n = nc * C * (3 * Dk + 2 * Dv) * es + nc * Dk * 4
+        return (n + 255) // 256 * 256
+    assert L.osdn_chunk_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
+        wy(64, 4096, 128, 128, 64, 2)
+    assert L.gdn2_forward_workspace_bytes(2, 3, 100, 64, 32, 32, 0) == \
+        wy(6, 100, 64, 32, 32, 4)
     assert L.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
-        4 * 16 * 4096 * 128 * 2 + pre(64, 4096, 128)
+        4 * 16 * 4096 * 128 * 2 + max(pre(64, 4096, 128),
+                                      wy(64, 4096, 128, 128, 64, 2))
     assert L.osdn_forward_workspace_bytes(1, 1, 3, 32, 32, 16, 0) == \
-        512 + pre(1, 3, 32)
+        512 + max(pre(1, 3, 32), wy(1, 3, 32, 32, 16, 4))
     assert L.osdn_forward_workspace_bytes(-1, 1, 3, 32, 32, 16, 0) == 0
 
 
@@ -157,11 +169,13 @@ def test_gdn2_error_paths():
     L = osdn.load_library()
     P = ctypes.c_void_p
     L.gdn2_forward.argtypes = [ctypes.c_int] * 7 + [P] * 7 + [ctypes.c_float,
-                                                              P, P, P]
+                                                              P, P, P,
+                                                              ctypes.c_size_t, P]
 
-    def call(T=64, Dk=32, q=0x10000, la=0x60000, o=0x50000, ST=None, S0=None):
+    def call(T=64, Dk=32, q=0x10000, la=0x60000, o=0x50000, ST=None, S0=None,
+             ws=0x100000, wsb=1 << 20):
         return L.gdn2_forward(1, 1, T, Dk, 32, 16, 1, q, 0x20000, 0x30000, la,
-                              0x70000, 0x80000, S0, 1.0, o, ST, None)
+                              0x70000, 0x80000, S0, 1.0, o, ST, ws, wsb, None)
 
     assert call(q=None) == NULL_ARG
     assert call(la=None) == NULL_ARG
@@ -169,5 +183,8 @@ def test_gdn2_error_paths():
     assert call(Dk=48) == UNSUPPORTED
     assert call(o=0x20000 + 128) == ALIASING
     assert call(S0=0x200000, ST=0x200000 + 8) == ALIASING
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(ws=0x30000) == ALIASING          # workspace over v
     assert L.gdn2_forward_supported(128, 128, 64, 1) == 1
     assert L.gdn2_forward_supported(128, 128, 8, 1) == 0
