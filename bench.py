@@ -2,12 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one full forward (phase 1 preconditioner scan + phase 2 chunked WY
-delta rule) over the workload's synthetic batch, inputs resident in HBM,
-outputs and workspace preallocated. The step issues exactly the two kernel
-launches osdn_forward makes, through their own C-ABI entry points, with HIP
-events recorded around each launch on the launch stream so that per-kernel
-durations are measured live over the timed region.
+One step = one full forward (osdn_forward: phase 1 preconditioner scan and
+phase 2 chunked WY delta rule; or gdn2_forward for --workload gdn2-1.3b) over
+the workload's synthetic batch, inputs resident in HBM, outputs and
+workspace preallocated. Per-kernel durations are measured live over the
+timed region by the library's kernel timing, which records HIP events on the
+launch stream around every kernel.
 
 Prints one JSON line with the throughput (tokens/s = B*T per step time), the
 roofline of the dominant kernel and the CPU-oracle baseline.
@@ -31,10 +31,23 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
 _CSRC = os.path.join(ROOT, "delta_rule_recurrent_scan_amd", "csrc")
 _KERNEL_SOURCES = {
-    "osdn_precond_scan": ["precond_scan.hip"],
-    "osdn_chunk": ["wy_chunk.hip"],
-    "gdn2_chunk": ["wy_chunk.hip"],
+    "precond_prep": ["precond_scan.hip"],
+    "precond_chain": ["precond_scan.hip"],
+    "precond_ktilde": ["precond_scan.hip"],
+    "wy_prep": ["wy_chunk.hip"],
+    "wy_scan": ["wy_chunk.hip"],
+    "gdn2_prep": ["wy_chunk.hip"],
+    "gdn2_scan": ["wy_chunk.hip"],
 }
+PRECOND_CHUNK = 64  # phase-1 chunk length (fixed in the library)
+
+
+def source_sha(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in _KERNEL_SOURCES[kernel] + ["device_common.hpp", "launch.hpp"]:
+        h.update(open(os.path.join(_CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
@@ -42,33 +55,49 @@ def measured_traffic(kernel, workload):
     WRITE_SIZE runs (scaled by the copy-kernel calibration), or None when
     they were taken on another workload or on kernel sources that have
     changed since."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         rec = json.load(open(path))["kernels"][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    h = hashlib.sha256()
-    for f in _KERNEL_SOURCES[kernel] + ["device_common.hpp", "launch.hpp"]:
-        h.update(open(os.path.join(_CSRC, f), "rb").read())
-    if rec.get("source_sha") != h.hexdigest()[:16] or rec.get("workload") != workload:
+    if rec.get("source_sha") != source_sha(kernel) or rec.get("workload") != workload:
         return None
     return rec["bytes"]
 
 
-def bytes_per_token_head(w, apf):
-    """Algorithmic bytes per token-head of each kernel and of the whole path.
-
-    Whole path: q, k (Dk each) and v (Dv) read, o (Dv) written, beta (and r)
-    read. Phase 1 reads k, beta (r) and writes k~ (Dk); phase 2 reads q, k,
-    k~, v, beta and writes o.
-    """
+def path_bytes_per_token_head(w, apf):
+    """Whole OSDN path: q, k (Dk each) and v (Dv) read, o (Dv) written,
+    beta (and r) read."""
     s = 2 if w.dtype == "bf16" else 4
-    g = 4 + (4 if apf else 0)
-    path = (2 * w.Dk + w.Dv) * s + w.Dv * s + g
-    p1 = 2 * w.Dk * s + g
-    p2 = (3 * w.Dk + w.Dv) * s + w.Dv * s + 4
-    return path, p1, p2
+    return (2 * w.Dk + w.Dv) * s + w.Dv * s + 4 + (4 if apf else 0)
+
+
+def kernel_bytes_per_token_head(w, apf=False):
+    """Algorithmic bytes per token-head of each kernel: everything its
+    interface reads and writes once (inputs, outputs and the workspace
+    arrays handed from one kernel to the next)."""
+    s = 2 if w.dtype == "bf16" else 4
+    dk, dv, C, C1 = w.Dk, w.Dv, w.chunk, PRECOND_CHUNK
+    gates = 4 + (4 if apf else 0)
+    rec = (2 * C1 + 4 + C1 * C1) * 4.0 / C1   # phase-1 chunk record
+    dent = dk * 4.0 / C1                       # d at each chunk entry
+    frags = (3 * dk + 2 * dv) * s              # S0-independent chunk operands
+    return {
+        # k, beta, r -> record
+        "precond_prep": dk * s + gates + rec,
+        # k, record -> g, d entries
+        "precond_chain": dk * s + rec + 4 + dent,
+        # k, log gate prefix, g, d entries -> k~
+        "precond_ktilde": 2 * dk * s + 4 * (C1 + 4.0) / C1 + 4 + dent,
+        # q, k, k~, v, beta -> Wk, Q', X', U, O'
+        "wy_prep": (3 * dk + dv) * s + 4 + frags,
+        # Wk, Q', X', U, O' -> o
+        "wy_scan": frags + dv * s,
+        # q, k, b, v, w, log alpha -> Wk, Q', X', U, O', exit decay
+        "gdn2_prep": (3 * dk + 2 * dv) * s + 4 * dk + frags + 4.0 * dk / C,
+        # Wk, Q', X', U, O', exit decay -> o
+        "gdn2_scan": frags + 4.0 * dk / C + dv * s,
+    }
 
 
 def flops_per_token_head(w):
@@ -79,11 +108,36 @@ def flops_per_token_head(w):
     return 6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3.0
 
 
-def gdn2_bytes_per_token_head(w):
-    """q, k, b (Dk) and v, w (Dv) read in the storage dtype, log alpha (Dk)
-    read in fp32, o (Dv) written."""
-    s = 2 if w.dtype == "bf16" else 4
-    return (3 * w.Dk + 2 * w.Dv) * s + 4 * w.Dk + w.Dv * s
+def timed_steps(step, args):
+    """Warm up, then time exactly args.steps steps (synchronised on both
+    sides) with the library's per-kernel event timing on; returns the wall
+    time per step (ms) and {kernel: mean ms}."""
+    import delta_rule_recurrent_scan_amd as osdn
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    osdn.kernel_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    osdn.kernel_timing(False)
+    kt = {n: ms for n, (cnt, ms) in osdn.kernel_times().items()}
+    return wall * 1e3 / args.steps, kt
+
+
+def roofline(w, kt, kb):
+    """Roofline entry of the dominant (longest) kernel: algorithmic bytes per
+    launch over its mean launch duration, against the HBM peak."""
+    th = w.B * w.H * w.T
+    dom = max(kt, key=lambda n: kt[n])
+    alg = kb[dom] * th
+    achieved = alg / (kt[dom] * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": dom, "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(dom, w.name), "alg_bytes": alg,
+            "ms": kt[dom]}
 
 
 def cpu_baseline(w, inp, budget_s=12.0):
@@ -113,45 +167,28 @@ def cpu_baseline(w, inp, budget_s=12.0):
 
 
 def bench_gdn2(args, w, inp, x, dt, dev):
-    """One step = one gdn2_forward launch over the workload."""
+    """One step = one gdn2_forward call over the workload."""
     import delta_rule_recurrent_scan_amd as osdn
     L = osdn.load_library()
     P = osdn._ptr
     o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
     S_T = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
     code = {torch.float32: 0, torch.bfloat16: 1}[dt]
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
+    sp = torch.cuda.current_stream(dev).cuda_stream
     ws_n = L.gdn2_forward_workspace_bytes(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk,
                                           code)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step():
         rc = L.gdn2_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code,
                             P(x["q"]), P(x["k"]), P(x["v"]), P(x["log_alpha"]),
                             P(x["b"]), P(x["w"]), None, 1.0, P(o), P(S_T),
                             P(ws), ws.numel(), sp)
-        if ev is not None:
-            ev[1].record(stream)
         if rc:
             raise RuntimeError("launch failed: %s" % L.osdn_strerror(rc))
 
-    for _ in range(args.warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    th = w.B * w.H * w.T
-    alg = gdn2_bytes_per_token_head(w) * th
-    achieved = alg / (k_ms * 1e-3) / 1e9
+    ms_step, kt = timed_steps(step, args)
+    kb = kernel_bytes_per_token_head(w)
     rec = {
         "metric": "GDN-2 forward tokens/s + % HBM roofline, H=16 d=128 "
                   "T=4096, 1 GPU",
@@ -161,11 +198,8 @@ def bench_gdn2(args, w, inp, x, dt, dev):
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T,
                    "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk},
-        "roofline": {"bound": "hbm", "kernel": "gdn2_chunk",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("gdn2_chunk", w.name)},
-        "kernels_ms": {"gdn2_chunk": k_ms},
+        "roofline": roofline(w, kt, kb),
+        "kernels_ms": kt,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_gdn2(w, inp)
@@ -246,60 +280,27 @@ def main():
     o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
     S_T = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
     d_T = torch.empty((w.B, w.H, w.Dk), dtype=torch.float32, device=dev)
-    ktil = torch.empty((w.B, w.H, w.T, w.Dk), dtype=dt, device=dev)
     L = osdn.load_library()
     code = {torch.float32: 0, torch.bfloat16: 1}[dt]
-    # one scratch buffer serves both entry points (phase-1 scratch is dead
-    # when phase 2 starts)
-    pws_n = max(L.osdn_precond_workspace_bytes(w.B, w.H, w.T, w.Dk, code),
-                L.osdn_chunk_workspace_bytes(w.B, w.H, w.T, w.Dk, w.Dv,
-                                             w.chunk, code))
-    pws = torch.empty(max(pws_n, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
     P = osdn._ptr
+    ws_n = L.osdn_forward_workspace_bytes(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk,
+                                          code)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        rc = L.osdn_precond_scan(w.B, w.H, w.T, w.Dk, code, P(x["k"]),
-                                 P(x["beta"]), P(x["r"]), float(x["eta"]), None,
-                                 P(ktil), P(d_T), P(pws), pws.numel(), sp)
-        if ev is not None:
-            ev[1].record(stream)
-        rc |= L.osdn_chunk_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code,
-                                   P(x["q"]), P(x["k"]), P(ktil), P(x["v"]),
-                                   P(x["beta"]), None, 1.0, P(o), P(S_T),
-                                   P(pws), pws.numel(), sp)
-        if ev is not None:
-            ev[2].record(stream)
+    def step():
+        rc = L.osdn_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code, P(x["q"]),
+                            P(x["k"]), P(x["v"]), P(x["beta"]), P(x["r"]),
+                            float(x["eta"]), None, None, 1.0, P(o), P(S_T),
+                            P(d_T), P(ws), ws.numel(), sp)
         if rc:
             raise RuntimeError("launch failed: %s" % L.osdn_strerror(rc))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))  # ms
-    k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-
+    ms_step, kt = timed_steps(step, args)
     th = w.B * w.H * w.T
     apf = inp["r"] is not None
-    path_b, p1_b, p2_b = bytes_per_token_head(w, apf)
-    kernels = {
-        "osdn_precond_scan": {"ms": k1, "alg_bytes": p1_b * th},
-        "osdn_chunk": {"ms": k2, "alg_bytes": p2_b * th},
-    }
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    achieved = kernels[dom]["alg_bytes"] / (kernels[dom]["ms"] * 1e-3) / 1e9
+    kb = kernel_bytes_per_token_head(w, apf)
+    path_b = path_bytes_per_token_head(w, apf)
     flops = flops_per_token_head(w) * th
     rec = {
         "metric": "OSDN forward tokens/s + % HBM/MFMA roofline, H=16 d=128 "
@@ -318,12 +319,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T,
                    "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk,
                    "forgetting_gate": apf, "eta": w.eta},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(dom, w.name),
-                     "alg_bytes": kernels[dom]["alg_bytes"]},
-        "kernels_ms": {n: kernels[n]["ms"] for n in kernels},
+        "roofline": roofline(w, kt, kb),
+        "kernels_ms": kt,
         "path": {"alg_bytes": path_b * th,
                  "hbm_GBs": path_b * th / (ms_step * 1e-3) / 1e9,
                  "hbm_frac": path_b * th / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -15,6 +15,7 @@ import torch
 __all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
            "gdn2_forward",
            "workspace_bytes", "precond_workspace_bytes", "supported",
+           "kernel_timing", "kernel_times",
            "OsdnError", "library_path", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,8 +73,32 @@ def load_library():
     L.gdn2_forward.argtypes = ([I] * 7 + [P, P, P, P, P, P, P, F, P, P, P, Z,
                                           P])
     L.gdn2_forward.restype = I
+    L.osdn_kernel_timing.argtypes = [I]
+    L.osdn_kernel_timing.restype = None
+    L.osdn_kernel_times.argtypes = [I, P, P, P]
+    L.osdn_kernel_times.restype = I
     _lib = L
     return L
+
+
+def kernel_timing(enable):
+    """Start (clearing earlier records) or stop per-kernel HIP-event timing
+    inside the library."""
+    load_library().osdn_kernel_timing(1 if enable else 0)
+
+
+def kernel_times():
+    """{kernel name: (launches, mean ms)} of the kernels launched while
+    timing was enabled (waits for their events)."""
+    L = load_library()
+    n = 16
+    names = (ctypes.c_char_p * n)()
+    counts = (ctypes.c_int * n)()
+    ms = (ctypes.c_float * n)()
+    k = L.osdn_kernel_times(n, names, counts, ms)
+    if k < 0:
+        raise RuntimeError("osdn_kernel_times: HIP runtime error")
+    return {names[i].decode(): (counts[i], ms[i]) for i in range(min(k, n))}
 
 
 def _ptr(t):

@@ -56,4 +56,9 @@ bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
                           int bf16);
 
+// Kernel timing hooks (no-ops unless enabled through osdn_kernel_timing):
+// an event on stream s before the kernel `name` is launched and one after.
+void ktimer_before(hipStream_t s, const char* name);
+void ktimer_after(hipStream_t s);
+
 }  // namespace osdn

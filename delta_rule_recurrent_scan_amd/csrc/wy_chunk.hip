@@ -832,17 +832,21 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     if (nch > 0) {
       // persistent grid: a few workgroups per compute unit at most
       const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<DK, DV, C, Tin>());
+      ktimer_before(s, kGdn2 ? "gdn2_prep" : "wy_prep");
       hipLaunchKernelGGL((wy_prep_kernel<V, DK, DV, C, Tin>), dim3(grid),
                          dim3(512), 0, s, a, nch, wb);
+      ktimer_after(s);
       const int rc = (int)hipGetLastError();
       if (rc) return rc;
     }
+    ktimer_before(s, kGdn2 ? "gdn2_scan" : "wy_scan");
     if (pick_vt(BH, DV) == 32)
       hipLaunchKernelGGL((wy_scan_kernel<kGdn2, DK, C, 32, Tin>),
                          dim3(BH * (DV / 32)), dim3(256), 0, s, a, nch, wb);
     else
       hipLaunchKernelGGL((wy_scan_kernel<kGdn2, DK, C, 16, Tin>),
                          dim3(BH * (DV / 16)), dim3(256), 0, s, a, nch, wb);
+    ktimer_after(s);
     return (int)hipGetLastError();
   }
 }

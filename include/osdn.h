@@ -193,6 +193,25 @@ int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
 size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
 
+/*
+ * Per-kernel timing for measurement harnesses (not thread-safe). While
+ * enabled, every entry point records a HIP event on its stream before and
+ * after each kernel it launches (two event records per kernel; events are
+ * created on first use and kept). osdn_kernel_timing(1) enables and clears
+ * the record, osdn_kernel_timing(0) disables.
+ */
+void osdn_kernel_timing(int enable);
+
+/*
+ * Waits for the recorded events and reports, for each distinct kernel name
+ * in first-launch order (at most `max`), its name (static storage), launch
+ * count and mean duration in milliseconds; any output pointer may be NULL.
+ * Returns the number of distinct kernels recorded, or -1 if the HIP runtime
+ * fails. Kernel names: precond_prep, precond_chain, precond_ktilde (phase
+ * 1), wy_prep, wy_scan (phase 2), gdn2_prep, gdn2_scan (GDN-2).
+ */
+int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
+
 #ifdef __cplusplus
 }
 #endif

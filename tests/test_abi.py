@@ -157,6 +157,15 @@ def test_precond_scan_error_paths():
     assert pre(B=0, k=None, beta=None, ws=None, wsb=0) == OK
 
 
+@needs_lib
+def test_kernel_timing_host_side():
+    # with nothing launched the record is empty (no HIP call is made)
+    osdn.kernel_timing(True)
+    assert osdn.kernel_times() == {}
+    osdn.kernel_timing(False)
+    assert osdn.load_library().osdn_kernel_times(0, None, None, None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(osdn, "_lib", None)
     monkeypatch.setattr(osdn, "_LIB_PATH", "/nonexistent/libosdn.so")
