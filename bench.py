@@ -35,6 +35,7 @@ _KERNEL_SOURCES = {
     "precond_chain": ["precond_scan.hip"],
     "precond_ktilde": ["precond_scan.hip"],
     "wy_prep": ["wy_chunk.hip"],
+    "wy_prep_fused": ["wy_chunk.hip"],
     "wy_scan": ["wy_chunk.hip"],
     "gdn2_prep": ["wy_chunk.hip"],
     "gdn2_scan": ["wy_chunk.hip"],
@@ -91,6 +92,9 @@ def kernel_bytes_per_token_head(w, apf=False):
         "precond_ktilde": 2 * dk * s + 4 * (C1 + 4.0) / C1 + 4 + dent,
         # q, k, k~, v, beta -> Wk, Q', X', U, O'
         "wy_prep": (3 * dk + dv) * s + 4 + frags,
+        # q, k, v, beta, log gate prefix, g, d entries -> Wk, Q', X', U, O'
+        "wy_prep_fused": (2 * dk + dv) * s + 4 + 4 * (C1 + 4.0) / C1 + 4 + dent
+        + frags,
         # Wk, Q', X', U, O' -> o
         "wy_scan": frags + dv * s,
         # q, k, b, v, w, log alpha -> Wk, Q', X', U, O', exit decay

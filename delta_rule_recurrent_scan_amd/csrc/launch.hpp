@@ -7,6 +7,13 @@
 
 namespace osdn {
 
+// Phase-1 chunk length and the layout of its per-chunk fp32 record
+// {lp_0..lp_C (lp_t = log of the gate product before token t), 3 pad,
+// g (C step sizes), V (C x C)}; the entry values of d follow all records.
+constexpr int kPrecondChunk = 64;
+constexpr int kRecLp = 0, kRecG = kPrecondChunk + 4, kRecV = 2 * kPrecondChunk + 4;
+constexpr int kRecStride = 2 * kPrecondChunk + 4 + kPrecondChunk * kPrecondChunk;
+
 struct PrecondArgs {
   int B, H, T, Dk;
   int bf16;                 // 1: k and ktilde are bf16, 0: fp32
@@ -39,6 +46,10 @@ struct ChunkArgs {
   const void* b;            // GDN-2: [B,H,T,Dk] erase gate
   const void* w;            // GDN-2: [B,H,T,Dv] write gate
   void* ws;                 // wy_workspace_bytes(...) bytes, 16-byte aligned
+  // OSDN with K~ formed inside the engine (chunk == kPrecondChunk): the
+  // phase-1 records and entry values of d (ktilde unused).
+  const float* prec;
+  const float* pdent;
 };
 
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
@@ -48,6 +59,7 @@ int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
 // {log gate prefix, g, V} and the entry value of d.
 size_t precond_workspace_bytes(int B, int H, int T, int Dk, int bf16);
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
+int launch_osdn_fused(const ChunkArgs& a, hipStream_t s);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);

@@ -97,10 +97,12 @@ size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
   if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
       !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
     return 0;
-  // the preconditioned keys, then scratch shared by the two phases (the
-  // phase-1 scratch is dead when phase 2 starts)
   const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
   const size_t p2 = osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  // chunk = 64: phase 2 forms K~ itself from the phase-1 records, so both
+  // scratch regions are live at once; otherwise the preconditioned keys,
+  // then scratch shared by the two phases
+  if (chunk == osdn::kPrecondChunk) return p1 + p2;
   return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
 }
 
@@ -161,18 +163,38 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
   if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
 
   hipStream_t s = (hipStream_t)stream;
-  // workspace: the preconditioned keys, then the phase-1 scratch
-  const size_t kt_bytes = round256(BH * T * Dk * es);
-  void* pws = static_cast<unsigned char*>(workspace) + kt_bytes;
-  osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                       workspace, d_T, pws};
-  int rc = osdn::launch_precond_scan(pa, s);
-  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
-  if (rc != 0) return OSDN_ERR_HIP;
-  osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                     workspace, v, beta, S0, scale, o, S_T,
-                     nullptr, nullptr, nullptr, pws};
-  rc = osdn::launch_osdn_chunk(ca, s);
+  unsigned char* wsb = static_cast<unsigned char*>(workspace);
+  int rc;
+  if (chunk == osdn::kPrecondChunk) {
+    // phase-1 scratch (records, then entry values of d), then the phase-2
+    // operands; K~ is formed inside phase 2
+    const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
+    osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                         nullptr, d_T, wsb};
+    rc = osdn::launch_precond_scan(pa, s);
+    if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+    if (rc != 0) return OSDN_ERR_HIP;
+    const int nch = (T + chunk - 1) / chunk;
+    const float* prec = reinterpret_cast<const float*>(wsb);
+    const float* pdent = prec + BH * (size_t)nch * osdn::kRecStride;
+    osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                       nullptr, v, beta, S0, scale, o, S_T,
+                       nullptr, nullptr, nullptr, wsb + p1, prec, pdent};
+    rc = osdn::launch_osdn_fused(ca, s);
+  } else {
+    // workspace: the preconditioned keys, then scratch shared by the phases
+    const size_t kt_bytes = round256(BH * T * Dk * es);
+    void* pws = wsb + kt_bytes;
+    osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                         workspace, d_T, pws};
+    rc = osdn::launch_precond_scan(pa, s);
+    if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+    if (rc != 0) return OSDN_ERR_HIP;
+    osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                       workspace, v, beta, S0, scale, o, S_T,
+                       nullptr, nullptr, nullptr, pws};
+    rc = osdn::launch_osdn_chunk(ca, s);
+  }
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }

@@ -35,8 +35,6 @@
 
 namespace osdn {
 
-constexpr int kPrecondChunk = 64;
-
 template <int DK, typename Tin>
 struct P1Cfg {
   static constexpr int C = kPrecondChunk, NW = 4, NT = 256, TB = C / 16,
@@ -49,8 +47,8 @@ struct P1Cfg {
   static_assert((C * NCB) % NT == 0, "whole key blocks per thread");
   // chunk record (fp32): lp_0..lp_C (lp_t = log P_t), g (g0 from prep,
   // replaced by g in the chain), V (C x C, zero above the diagonal)
-  static constexpr int R_LP = 0, R_G = C + 4, R_V = 2 * C + 4;
-  static constexpr int RS = 2 * C + 4 + C * C;
+  static constexpr int R_LP = kRecLp, R_G = kRecG, R_V = kRecV;
+  static constexpr int RS = kRecStride;
   // prep: split squares (bf16), then T and the doubling scratch in their place
   static constexpr int LDH = DK + 8;
   static constexpr int LDF = C + 4;
@@ -329,74 +327,39 @@ struct ChainRegs {
   static constexpr int SEG1 = DK / 4;
   static constexpr int NR1 = SEG1 * sizeof(Tin) / 16;
   // d update: wave w owns channels [w DK/4, (w+1) DK/4) as DK/8 pairs; lane l
-  // takes pair l % (DK/8) over the token rows m * NSG + l / (DK/8); it reads
-  // its key pairs from the staged rows.
+  // takes pair l % (DK/8) over the token rows of segment l / (DK/8).
   static constexpr int NP = DK / 8, NSG = 64 / NP, RS3 = C / NSG;
   using Pair = typename KeyPair<Tin>::T;
 
   uint4 kr[NR1];
+  Pair kc[RS3];
   float4 vr[4];
   float g0, lpt1, lpC;
 
-  // GUARD: the chunk may be partial (rows past T read as zero).
-  template <bool GUARD>
   __device__ __forceinline__ void load(const Tin* k, const float* rc, size_t t0,
-                                       int valid, int t, int q) {
+                                       int valid, int t, int q, int c3, int sg) {
 #pragma unroll
     for (int i = 0; i < NR1; ++i) {
       kr[i] = uint4{0u, 0u, 0u, 0u};
-      if (!GUARD || t < valid)
+      if (t < valid)
         kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + t) * DK + q * SEG1 +
                                                 i * (16 / sizeof(Tin)));
     }
-    // V is zero above the diagonal, so every block is read as stored
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + 16 * q + 4 * i);
+    for (int m = 0; m < RS3; ++m) {
+      const int row = sg * RS3 + m;
+      kc[m] = Pair{};
+      if (row < valid) kc[m] = *reinterpret_cast<const Pair*>(k + (t0 + row) * DK + c3);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vr[i] = float4{0.f, 0.f, 0.f, 0.f};
+      if (q <= (t >> 4))
+        vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + 16 * q + 4 * i);
+    }
     g0 = rc[G::R_G + t];
     lpt1 = rc[G::R_LP + t + 1];
     lpC = rc[G::R_LP + C];
-  }
-
-  // Thread-interleaved copy in LDS (16-byte word w of thread i at
-  // [w * SSTR + i], one pad word per row so that the key-pair reads below
-  // spread over the banks): the hand-off between the chunk step that fetches
-  // the operands and the step that uses them, so that a fetch is awaited
-  // only where it is stored. Words 0..NR1-1 are the key rows.
-  static constexpr int SSTR = 257;
-  static constexpr size_t BYTES = sizeof(kr) + sizeof(vr) + 3 * sizeof(float);
-  static constexpr int WORDS = (int)((BYTES + 15) / 16);
-  __device__ __forceinline__ void stash(uint4* base) const {
-    uint4 w[WORDS];
-    unsigned char* b = reinterpret_cast<unsigned char*>(w);
-    size_t o = 0;
-    __builtin_memcpy(b + o, kr, sizeof(kr)); o += sizeof(kr);
-    __builtin_memcpy(b + o, vr, sizeof(vr)); o += sizeof(vr);
-    const float sc[3] = {g0, lpt1, lpC};
-    __builtin_memcpy(b + o, sc, sizeof(sc)); o += sizeof(sc);
-    for (; o < (size_t)WORDS * 16; ++o) b[o] = 0;
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) base[i * SSTR + threadIdx.x] = w[i];
-  }
-  __device__ __forceinline__ void unstash(const uint4* base) {
-    uint4 w[WORDS];
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) w[i] = base[i * SSTR + threadIdx.x];
-    const unsigned char* b = reinterpret_cast<const unsigned char*>(w);
-    size_t o = 0;
-    __builtin_memcpy(kr, b + o, sizeof(kr)); o += sizeof(kr);
-    __builtin_memcpy(vr, b + o, sizeof(vr)); o += sizeof(vr);
-    float sc[3];
-    __builtin_memcpy(sc, b + o, sizeof(sc));
-    g0 = sc[0]; lpt1 = sc[1]; lpC = sc[2];
-  }
-  // Key elements (row, c) and (row, c + 1), c even, from a stage.
-  __device__ __forceinline__ static Pair key_pair(const uint4* base, int row, int c) {
-    constexpr int EPW = 16 / sizeof(Tin);           // elements per word
-    const int qq = c / SEG1, within = c % SEG1;
-    const int word = within / EPW, e = within % EPW;
-    const Tin* wp = reinterpret_cast<const Tin*>(base + word * SSTR + 4 * row + qq);
-    return *reinterpret_cast<const Pair*>(wp + e);
   }
 };
 
@@ -409,38 +372,22 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
   using KP = KeyPair<Tin>;
   constexpr int C = G::C;
   __shared__ float dv[DK], xs[C], cgs[C];
-  // two stages by chunk parity: a step reads stage j&1 (also for the
-  // column-layout key reads) while it fills stage (j+1)&1
-  __shared__ uint4 stage[2][R::WORDS * R::SSTR];
   const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t = tid >> 2, q = tid & 3;
   const int sg = lane / R::NP;
   const int c3 = wave * (DK / 4) + 2 * (lane % R::NP);
 
   for (int c = tid; c < DK; c += G::NT) dv[c] = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
-
-  const int nfull = T / C;  // chunks with C valid rows
-  auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
-  auto fetch = [&](R& r, int jj) {
-    const size_t t0 = (size_t)bh * T + (size_t)jj * C;
-    if (jj < nfull)
-      r.template load<false>(k, recp(jj), t0, C, t, q);
-    else
-      r.template load<true>(k, recp(jj), t0, T - jj * C, t, q);
-  };
-  if (nchunks > 0) {
-    R first;
-    fetch(first, 0);
-    first.stash(stage[0]);
-  }
   __syncthreads();
+
+  auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
+  R cur, nxt;
+  if (nchunks > 0)
+    cur.load(k, recp(0), (size_t)bh * T, min(C, T), t, q, c3, sg);
   for (int jj = 0; jj < nchunks; ++jj) {
-    R nxt;
-    const bool more = jj + 1 < nchunks;
-    if (more) fetch(nxt, jj + 1);
-    const uint4* st = stage[jj & 1];
-    R cur;
-    cur.unstash(st);
+    if (jj + 1 < nchunks)
+      nxt.load(k, recp(jj + 1), (size_t)bh * T + (size_t)(jj + 1) * C,
+               min(C, T - (jj + 1) * C), t, q, c3, sg);
     float* rc = recp(jj);
     if (tid < DK) dent[((size_t)bh * nchunks + jj) * DK + tid] = dv[tid];
     // x_t = <d, a_t>
@@ -477,10 +424,8 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int m = 0; m < R::RS3; ++m) {
-        const int row = m * R::NSG + sg;
-        const float cg = cgs[row];
-        const typename R::Pair kp2 = R::key_pair(st, row, c3);
-        const float x0 = KP::lo(kp2), x1 = KP::hi(kp2);
+        const float cg = cgs[sg * R::RS3 + m];
+        const float x0 = KP::lo(cur.kc[m]), x1 = KP::hi(cur.kc[m]);
         s0 += x0 * x0 * cg;
         s1 += x1 * x1 * cg;
       }
@@ -492,8 +437,8 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
         dv[c3 + 1] = PC * dv[c3 + 1] + s1;
       }
     }
-    if (more) nxt.stash(stage[(jj + 1) & 1]);
     __syncthreads();
+    cur = nxt;
   }
   if (dT && tid < DK) dT[(size_t)bh * DK + tid] = dv[tid];
 }

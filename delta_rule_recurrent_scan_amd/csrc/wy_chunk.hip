@@ -34,8 +34,8 @@
 // * scan: one workgroup (4 waves) per (batch, head, VT-wide value tile) walks
 //   the chunks in order with the VT x Dk state slice in fp32 MFMA
 //   accumulators: two products into W and O, one into the state, two
-//   barriers per chunk; the next chunk's operands are loaded into registers
-//   while the current one computes.
+//   barriers per chunk; operands are fetched into registers two chunks ahead
+//   and handed over through an LDS stage.
 #include <algorithm>
 #include <type_traits>
 
@@ -46,6 +46,11 @@ namespace osdn {
 
 struct OsdnVariant {};
 struct Gdn2Variant {};
+// OSDN with the preconditioned keys formed in the engine from the raw keys,
+// the phase-1 chunk records (gate prefix, step sizes) and the entry values
+// of d: K~ = (P d^T + L A) * K, L[t][i] = (P_t / P_{i+1}) g_i for i < t,
+// A = K * K ([OSDN-it] 2.2). Requires chunk == the phase-1 chunk.
+struct OsdnFusedVariant {};
 
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
 // storage dtype (g in fp32): Wk and Q' as 16-row A fragments (row block tb
@@ -101,7 +106,14 @@ struct PrepCfg {
   static constexpr size_t oA = oPb + (size_t)C * LDC * E;
   static constexpr size_t oYs = oA + (size_t)TB * 16 * LDD * 4;
   static constexpr size_t oG = oYs + (size_t)NW * (C / 2) * LDS16 * E;
-  static constexpr size_t bytes = oG + (size_t)DK * 4;
+  // fused OSDN: squares of the keys, gate prefix (C + 4), step sizes, entry
+  // d, gate products P_t
+  static constexpr size_t oAs = oG + (size_t)DK * 4;
+  static constexpr size_t oLp = oAs + (size_t)C * LDK * E;
+  static constexpr size_t oGs = oLp + (size_t)(C + 4) * 4;
+  static constexpr size_t oDs = oGs + (size_t)C * 4;
+  static constexpr size_t oPv = oDs + (size_t)DK * 4;
+  static constexpr size_t bytes = oPv + (size_t)C * 4;
   static constexpr bool fits = bytes <= 163840;
   // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
   static constexpr int TPC = NT / DK;
@@ -114,13 +126,15 @@ template <class V, int DK, int DV, int C, typename Tin>
 struct PrepRegs {
   using G = PrepCfg<DK, DV, C, Tin>;
   static constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
+  static constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
   static constexpr int VEC = G::VEC;
   static constexpr int NKB = C * (DK / VEC), NVB = C * (DV / VEC);
   static constexpr int NLK = (NKB + G::NT - 1) / G::NT;
   static constexpr int NLV = (NVB + G::NT - 1) / G::NT;
-  uint4 k[NLK], q[NLK], x[NLK], v[NLV], w[kGdn2 ? NLV : 1];
+  uint4 k[NLK], q[NLK], x[kFused ? 1 : NLK], v[NLV], w[kGdn2 ? NLV : 1];
   float bk[NLK], bv[NLV];          // OSDN: beta of the row
   float la[kGdn2 ? G::TPT : 1];    // GDN-2: log alpha of the decay pass
+  float plp, pg, pd;               // fused OSDN: record entries, entry d
 
   __device__ __forceinline__ void load(const ChunkArgs& p, int n, int nchunks) {
     const int bh = n / nchunks, j = n - bh * nchunks;
@@ -133,14 +147,22 @@ struct PrepRegs {
     for (int i = 0; i < NLK; ++i) {
       const int e = tid + i * G::NT;
       const int rr = e / (DK / VEC), cc = (e % (DK / VEC)) * VEC;
-      k[i] = z; q[i] = z; x[i] = z; bk[i] = 0.f;
+      k[i] = z; q[i] = z; bk[i] = 0.f;
+      if constexpr (!kFused) x[i] = z;
       if (e < NKB && rr < valid) {
         const size_t gi = (t0 + rr) * DK + cc;
         k[i] = *reinterpret_cast<const uint4*>((const Tin*)p.k + gi);
         q[i] = *reinterpret_cast<const uint4*>((const Tin*)p.q + gi);
-        x[i] = *reinterpret_cast<const uint4*>(xs + gi);
+        if constexpr (!kFused) x[i] = *reinterpret_cast<const uint4*>(xs + gi);
         if constexpr (!kGdn2) bk[i] = p.beta[t0 + rr];
       }
+    }
+    if constexpr (kFused) {
+      // the phase-1 chunk of this engine chunk has the same index
+      const float* rc = p.prec + (size_t)n * kRecStride;
+      plp = tid <= C ? rc[kRecLp + tid] : 0.f;
+      pg = tid < C ? rc[kRecG + tid] : 0.f;
+      pd = tid < DK ? p.pdent[(size_t)n * DK + tid] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
@@ -170,8 +192,10 @@ struct PrepRegs {
   }
 
   // OSDN: Y = beta*k, X = k~, Q = q, Z = beta*v. GDN-2: raw k, b, q and
-  // Z = w*v (the decay pass forms X, Y and Q in place).
-  __device__ __forceinline__ void store(Tin* Ys, Tin* Xs, Tin* Qs, Tin* Zs) const {
+  // Z = w*v (the decay pass forms X, Y and Q in place). Fused OSDN: X = raw
+  // k (turned into K~ in place), the squares of k, and the record entries.
+  __device__ __forceinline__ void store(Tin* Ys, Tin* Xs, Tin* Qs, Tin* Zs,
+                                        unsigned char* smem) const {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < NLK; ++i) {
@@ -188,9 +212,29 @@ struct PrepRegs {
 #pragma unroll
           for (int u = 0; u < VEC; ++u) y[u] = from_f32<Tin>(bk[i] * to_f32(kv[u]));
           *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(y);
-          *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = x[i];
+          if constexpr (kFused) {
+            *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = k[i];
+            Tin a[VEC];
+#pragma unroll
+            for (int u = 0; u < VEC; ++u) {
+              const float xk = to_f32(kv[u]);
+              a[u] = from_f32<Tin>(xk * xk);
+            }
+            Tin* As = reinterpret_cast<Tin*>(smem + G::oAs);
+            *reinterpret_cast<uint4*>(As + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(a);
+          } else {
+            *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = x[i];
+          }
         }
       }
+    }
+    if constexpr (kFused) {
+      float* lps = reinterpret_cast<float*>(smem + G::oLp);
+      float* gs = reinterpret_cast<float*>(smem + G::oGs);
+      float* ds = reinterpret_cast<float*>(smem + G::oDs);
+      if (tid <= C) lps[tid] = plp;
+      if (tid < C) gs[tid] = pg;
+      if (tid < DK) ds[tid] = pd;
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
@@ -220,6 +264,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
                                                       WyBufs<Tin> wb) {
   using G = PrepCfg<DK, DV, C, Tin>;
   constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
+  constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDS16 = G::LDS16,
                 TB = G::TB, DB = G::DB, VBT = G::VBT, NW = G::NW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
@@ -250,7 +295,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   PrepRegs<V, DK, DV, C, Tin> regs;
   if ((int)blockIdx.x < total) regs.load(p, blockIdx.x, nchunks);
   for (int n = blockIdx.x; n < total; n += gridDim.x) {
-    regs.store(Ys, Xs, Qs, Zs);
+    regs.store(Ys, Xs, Qs, Zs, smem);
     if constexpr (kGdn2) {
       // Decay pass: TPC threads per channel c (lanes l and l + 64/TPC of one
       // wave), each over TPT consecutive tokens. Cumulative log decay within
@@ -298,13 +343,51 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
     if (n + (int)gridDim.x < total) regs.load(p, n + gridDim.x, nchunks);
     __syncthreads();
+    if constexpr (kFused) {
+      // ---- K~ = (P d^T + L A) * K in place over the raw keys --------------
+      const float* lps = reinterpret_cast<const float*>(smem + G::oLp);
+      const float* gs = reinterpret_cast<const float*>(smem + G::oGs);
+      const float* ds = reinterpret_cast<const float*>(smem + G::oDs);
+      float* Pv = reinterpret_cast<float*>(smem + G::oPv);
+      const Tin* As = reinterpret_cast<const Tin*>(smem + G::oAs);
+      Tin* Lb = Ab;  // L lives in the Gram buffer until the Gram step
+      for (int e = tid; e < C * C; e += G::NT) {
+        const int t = e / C, i = e % C;
+        Lb[t * LDC + i] = from_f32<Tin>(i < t ? __expf(lps[t] - lps[i + 1]) * gs[i] : 0.f);
+      }
+      if (tid < C) Pv[tid] = expf(lps[tid]);
+      __syncthreads();
+      // one job = (16-token block tb, 16-channel block db), db-major so a
+      // wave keeps its squares fragment
+      for (int job = wave; job < TB * DB; job += NW) {
+        const int db = job % DB, tb = job / DB;
+        Frag<C, Tin> fl, fa;
+        fl.load(Lb + tb * 16 * LDC, LDC);
+        fa.load_kmajor(As + db * 16, LDK);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma(acc, fl, fa);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb * 16 + acc_row(i), c = db * 16 + acc_col();
+          Tin* xe = Xs + t * LDK + c;
+          *xe = from_f32<Tin>((Pv[t] * ds[c] + acc[i]) * to_f32(*xe));
+        }
+      }
+      __syncthreads();
+    }
 
     // ---- Gram A, scores P, diagonal blocks of T; X' fragments ---------------
-    // Jobs: the TB diagonal tiles first (job b on wave b, which then inverts
-    // its block), then the off-diagonal lower tiles in row-major order.
+    // Jobs: diagonal tile b on wave b, which then inverts its block; the
+    // off-diagonal lower tiles (row-major order) on the other waves, so that
+    // they run beside the serial inversions.
     {
       constexpr int NL = TB * (TB + 1) / 2;
-      for (int job = wave; job < NL; job += NW) {
+      constexpr int NOFF = NL - TB;
+      static_assert(NW > TB, "waves left for the off-diagonal tiles");
+      constexpr int OW = NW - TB;
+      const int njobs = wave < TB ? 1 : (NOFF - (wave - TB) + OW - 1) / OW;
+      for (int it = 0; it < njobs; ++it) {
+        const int job = wave < TB ? wave : TB + (wave - TB) + OW * it;
         int a, b;
         if (job < TB) {
           a = b = job;
@@ -716,19 +799,18 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   __syncthreads();
 
   // One chunk step; TAIL: the chunk may be partial (rows past T are not
-  // stored). The operands of chunk j wait in the stage; those of chunk j + 1
-  // are fetched at the start and handed to the stage at the end, where their
-  // arrival is awaited. Guards that always hold for the tile
-  // configuration fold away at compile time.
+  // stored). On entry the stage holds chunk j and `give` holds chunk j + 1
+  // (fetched during the previous step); chunk j + 2 is fetched into `fetch`
+  // at the start, and `give` is handed to the stage at the end, where its
+  // arrival (one step after it was issued) is awaited. Guards that always
+  // hold for the tile configuration fold away at compile time.
   constexpr bool kAllRowWaves = TB == G::NW, kAllColWaves = DPW * G::NW == DB;
   const size_t n0 = (size_t)bh * nchunks;
-  auto step = [&](int j, auto tail) {
+  auto step = [&](int j, auto tail, R& fetch, const R& give) {
     constexpr bool TAIL = decltype(tail)::value;
     const size_t t0 = (size_t)bh * T + (size_t)j * C;
     const int valid = min(C, T - j * C);
-    R nxt;
-    const bool more = j + 1 < nchunks;
-    if (more) nxt.load(wb, n0 + j + 1, Dv, vt, wave);
+    if (j + 2 < nchunks) fetch.load(wb, n0 + j + 2, Dv, vt, wave);
     R cur;
     cur.unstash(stage);
     // ---- W = U - Wk S0^T (to LDS), O = O' + Q' S0^T (stored) --------------
@@ -775,19 +857,38 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
         }
       }
     }
-    if (more) nxt.stash(stage);
+    if (j + 1 < nchunks) give.stash(stage);
     __syncthreads();
   };
 
+  // Two register sets in turn (even steps fetch into rb and hand over ra,
+  // odd steps the reverse), unrolled so that each set is a fixed object.
+  R ra, rb;
   if (nchunks > 0) {
     R first;
     first.load(wb, n0, Dv, vt, wave);
     first.stash(stage);
   }
+  if (nchunks > 1) ra.load(wb, n0 + 1, Dv, vt, wave);
   __syncthreads();
+  using Full = std::false_type;
+  using Tail = std::true_type;
   const int nfull = T / C;  // chunks with C valid rows
-  for (int j = 0; j < nfull; ++j) step(j, std::false_type{});
-  if (nfull < nchunks) step(nfull, std::true_type{});
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    step(j, Full{}, rb, ra);
+    step(j + 1, Full{}, ra, rb);
+  }
+  if (j < nfull) {
+    step(j, Full{}, rb, ra);  // j even
+    ++j;
+  }
+  if (j < nchunks) {
+    if ((j & 1) == 0)
+      step(j, Tail{}, rb, ra);
+    else
+      step(j, Tail{}, ra, rb);
+  }
 
   if (p.ST) {
 #pragma unroll
@@ -832,7 +933,9 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     if (nch > 0) {
       // persistent grid: a few workgroups per compute unit at most
       const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<DK, DV, C, Tin>());
-      ktimer_before(s, kGdn2 ? "gdn2_prep" : "wy_prep");
+      ktimer_before(s, kGdn2 ? "gdn2_prep"
+                             : std::is_same<V, OsdnFusedVariant>::value ? "wy_prep_fused"
+                                                                       : "wy_prep");
       hipLaunchKernelGGL((wy_prep_kernel<V, DK, DV, C, Tin>), dim3(grid),
                          dim3(512), 0, s, a, nch, wb);
       ktimer_after(s);
@@ -853,6 +956,10 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
 
 template <class V, int DK, int DV, typename Tin>
 static int launch_dv(const ChunkArgs& a, hipStream_t s) {
+  if constexpr (std::is_same<V, OsdnFusedVariant>::value) {
+    return a.chunk == kPrecondChunk ? launch_cfg<V, DK, DV, kPrecondChunk, Tin>(a, s)
+                                    : -1;
+  }
   switch (a.chunk) {
     case 16: return launch_cfg<V, DK, DV, 16, Tin>(a, s);
     case 32: return launch_cfg<V, DK, DV, 32, Tin>(a, s);
@@ -895,6 +1002,11 @@ int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s) {
 
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s) {
   return launch_variant<Gdn2Variant>(a, s);
+}
+
+int launch_osdn_fused(const ChunkArgs& a, hipStream_t s) {
+  if (a.chunk != kPrecondChunk) return -1;
+  return launch_variant<OsdnFusedVariant>(a, s);
 }
 
 template <int DK, int DV, typename Tin>

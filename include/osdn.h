@@ -62,11 +62,13 @@ int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype);
 
 /*
  * Device workspace, in bytes, that osdn_forward needs for these sizes
- * (0 if the sizes are invalid or the call needs none). The workspace holds
- * the preconditioned keys produced by phase 1 ([B,H,T,Dk] in the storage
- * dtype) followed by scratch shared by the two phases (the larger of
- * osdn_precond_workspace_bytes and osdn_chunk_workspace_bytes), and its
- * contents are only meaningful during one call.
+ * (0 if the sizes are invalid or the call needs none); its contents are only
+ * meaningful during one call. chunk = 64: the phase-1 scratch
+ * (osdn_precond_workspace_bytes) followed by the phase-2 scratch
+ * (osdn_chunk_workspace_bytes), since phase 2 then forms the preconditioned
+ * keys itself. Other chunks: the preconditioned keys ([B,H,T,Dk] in the
+ * storage dtype, rounded up to 256 bytes) followed by scratch shared by the
+ * two phases (the larger of the two).
  */
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);

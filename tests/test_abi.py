@@ -91,9 +91,10 @@ def test_supported_and_workspace_sizes():
         wy(64, 4096, 128, 128, 64, 2)
     assert L.gdn2_forward_workspace_bytes(2, 3, 100, 64, 32, 32, 0) == \
         wy(6, 100, 64, 32, 32, 4)
+    # chunk 64: both scratch regions (phase 2 forms K~ from the records);
+    # other chunks: K~ plus the larger of the two
     assert L.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
-        4 * 16 * 4096 * 128 * 2 + max(pre(64, 4096, 128),
-                                      wy(64, 4096, 128, 128, 64, 2))
+        pre(64, 4096, 128) + wy(64, 4096, 128, 128, 64, 2)
     assert L.osdn_forward_workspace_bytes(1, 1, 3, 32, 32, 16, 0) == \
         512 + max(pre(1, 3, 32), wy(1, 3, 32, 32, 16, 4))
     assert L.osdn_forward_workspace_bytes(-1, 1, 3, 32, 32, 16, 0) == 0
