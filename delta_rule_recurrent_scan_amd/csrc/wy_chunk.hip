@@ -113,7 +113,14 @@ struct PrepCfg {
   static constexpr size_t oGs = oLp + (size_t)(C + 4) * 4;
   static constexpr size_t oDs = oGs + (size_t)C * 4;
   static constexpr size_t oPv = oDs + (size_t)DK * 4;
-  static constexpr size_t bytes = oPv + (size_t)C * 4;
+  static constexpr size_t oEnd = oPv + (size_t)C * 4;
+  // GDN-2: log alpha staged as fp32 rows, over the Gram/inverse buffers
+  // (not in use yet during the decay pass) when they are large enough
+  static constexpr int LDA = DK + 4;
+  static constexpr size_t kLaBytes = (size_t)C * LDA * 4;
+  static constexpr bool kLaInGram = oAb + kLaBytes <= oG;
+  static constexpr size_t oLa = kLaInGram ? oAb : oEnd;
+  static constexpr size_t bytes = oEnd + (kLaInGram ? 0 : kLaBytes);
   static constexpr bool fits = bytes <= 163840;
   // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
   static constexpr int TPC = NT / DK;
@@ -133,7 +140,8 @@ struct PrepRegs {
   static constexpr int NLV = (NVB + G::NT - 1) / G::NT;
   uint4 k[NLK], q[NLK], x[kFused ? 1 : NLK], v[NLV], w[kGdn2 ? NLV : 1];
   float bk[NLK], bv[NLV];          // OSDN: beta of the row
-  float la[kGdn2 ? G::TPT : 1];    // GDN-2: log alpha of the decay pass
+  static constexpr int NLA = (C * DK / 4 + G::NT - 1) / G::NT;
+  uint4 la4[kGdn2 ? NLA : 1];      // GDN-2: log alpha, 4 channels per load
   float plp, pg, pd;               // fused OSDN: record entries, entry d
 
   __device__ __forceinline__ void load(const ChunkArgs& p, int n, int nchunks) {
@@ -180,13 +188,13 @@ struct PrepRegs {
       }
     }
     if constexpr (kGdn2) {
-      constexpr int CPW = 64 / G::TPC;
-      const int lane = tid & 63, wave = tid >> 6;
-      const int c = wave * CPW + lane % CPW, part = lane / CPW;
 #pragma unroll
-      for (int m = 0; m < G::TPT; ++m) {
-        const int t = part * G::TPT + m;
-        la[m] = (t < valid) ? p.log_alpha[(t0 + t) * DK + c] : 0.f;
+      for (int i = 0; i < NLA; ++i) {
+        const int e = tid + i * G::NT;
+        const int rr = e / (DK / 4), cc = (e % (DK / 4)) * 4;
+        la4[i] = z;
+        if (e < C * DK / 4 && rr < valid)
+          la4[i] = *reinterpret_cast<const uint4*>(p.log_alpha + (t0 + rr) * DK + cc);
       }
     }
   }
@@ -225,6 +233,17 @@ struct PrepRegs {
           } else {
             *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = x[i];
           }
+        }
+      }
+    }
+    if constexpr (kGdn2) {
+      float* La = reinterpret_cast<float*>(smem + G::oLa);
+#pragma unroll
+      for (int i = 0; i < NLA; ++i) {
+        const int e = tid + i * G::NT;
+        if (e < C * DK / 4) {
+          const int rr = e / (DK / 4), cc = (e % (DK / 4)) * 4;
+          *reinterpret_cast<uint4*>(La + rr * G::LDA + cc) = la4[i];
         }
       }
     }
@@ -283,7 +302,8 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   const int total = p.B * p.H * nchunks;
   const Tin zero = from_f32<Tin>(0.f);
 
-  // Blocks above the diagonal of T and P are zero (and never written).
+  // Blocks above the diagonal of T and P are zero (never written by the
+  // chunk steps; GDN-2 restores them after its decay pass).
   for (int e = tid; e < C * C; e += G::NT) {
     const int rr = e / C, cc = e % C;
     if ((cc >> 4) > (rr >> 4)) {
@@ -297,51 +317,72 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   for (int n = blockIdx.x; n < total; n += gridDim.x) {
     regs.store(Ys, Xs, Qs, Zs, smem);
     if constexpr (kGdn2) {
-      // Decay pass: TPC threads per channel c (lanes l and l + 64/TPC of one
-      // wave), each over TPT consecutive tokens. Cumulative log decay within
-      // the chunk, then X = k/gamma, Y = gamma*b*k, Q = gamma*q in place and
-      // the exit decay g = gamma_C.
-      constexpr int TPC = G::TPC, TPT = G::TPT, CPW = 64 / TPC;
-      const int c = wave * CPW + lane % CPW, part = lane / CPW;
+      // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
+      // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
+      // staged log alpha into the inclusive prefix lambda in place and give
+      // the exit decay g = gamma_C. (2) Row pass: X = k/gamma, Y = gamma*b*k,
+      // Q = gamma*q with gamma = exp(lambda), VEC channels per access.
+      constexpr int TPC = G::TPC, TPT = G::TPT, CPW = 64 / TPC, LDA = G::LDA;
+      float* La = reinterpret_cast<float*>(smem + G::oLa);
       __syncthreads();
-      float lam[TPT];
-      float run = 0.f;
-  #pragma unroll
-      for (int m = 0; m < TPT; ++m) {
-        run += regs.la[m];
-        lam[m] = run;
-      }
-      float incl = run;
-  #pragma unroll
-      for (int d = 1; d < TPC; d <<= 1) {
-        const float y = __shfl_up(incl, d * CPW, 64);
-        if (part >= d) incl += y;
-      }
-      const float excl = incl - run;
-      const float total_la = __shfl(incl, (TPC - 1) * CPW + lane % CPW, 64);
-      constexpr int BT = TPT >= 8 ? 8 : TPT;
-  #pragma unroll
-      for (int m0 = 0; m0 < TPT; m0 += BT) {
-        const int tb0 = part * TPT + m0;
-        float kk[BT], bb[BT], qq[BT];
-  #pragma unroll
-        for (int u = 0; u < BT; ++u) {
-          kk[u] = to_f32(Xs[(tb0 + u) * LDK + c]);
-          bb[u] = to_f32(Ys[(tb0 + u) * LDK + c]);
-          qq[u] = to_f32(Qs[(tb0 + u) * LDK + c]);
+      {
+        const int c = wave * CPW + lane % CPW, part = lane / CPW;
+        float lam[TPT];
+        float run = 0.f;
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+          run += La[(part * TPT + m) * LDA + c];
+          lam[m] = run;
         }
-  #pragma unroll
-        for (int u = 0; u < BT; ++u) {
-          const float gam = __expf(excl + lam[m0 + u]);
+        float incl = run;
+#pragma unroll
+        for (int d = 1; d < TPC; d <<= 1) {
+          const float y = __shfl_up(incl, d * CPW, 64);
+          if (part >= d) incl += y;
+        }
+        const float excl = incl - run;
+        const float total_la = __shfl(incl, (TPC - 1) * CPW + lane % CPW, 64);
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) La[(part * TPT + m) * LDA + c] = excl + lam[m];
+        if (part == 0) gC[c] = __expf(total_la);
+      }
+      __syncthreads();
+      constexpr int VEC = G::VEC;
+      for (int item = tid; item < C * (DK / VEC); item += G::NT) {
+        const int t = item / (DK / VEC), c0 = (item % (DK / VEC)) * VEC;
+        uint4 k4 = *reinterpret_cast<const uint4*>(Xs + t * LDK + c0);
+        uint4 b4 = *reinterpret_cast<const uint4*>(Ys + t * LDK + c0);
+        uint4 q4 = *reinterpret_cast<const uint4*>(Qs + t * LDK + c0);
+        const Tin* kv = reinterpret_cast<const Tin*>(&k4);
+        const Tin* bv = reinterpret_cast<const Tin*>(&b4);
+        const Tin* qv = reinterpret_cast<const Tin*>(&q4);
+        Tin xo[VEC], yo[VEC], qo[VEC];
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          const float gam = __expf(La[t * LDA + c0 + u]);
           const float igam = __builtin_amdgcn_rcpf(gam);
-          Xs[(tb0 + u) * LDK + c] = from_f32<Tin>(kk[u] * igam);
-          Ys[(tb0 + u) * LDK + c] = from_f32<Tin>(gam * bb[u] * kk[u]);
-          Qs[(tb0 + u) * LDK + c] = from_f32<Tin>(gam * qq[u]);
+          const float kk = to_f32(kv[u]);
+          xo[u] = from_f32<Tin>(kk * igam);
+          yo[u] = from_f32<Tin>(gam * to_f32(bv[u]) * kk);
+          qo[u] = from_f32<Tin>(gam * to_f32(qv[u]));
+        }
+        *reinterpret_cast<uint4*>(Xs + t * LDK + c0) = *reinterpret_cast<const uint4*>(xo);
+        *reinterpret_cast<uint4*>(Ys + t * LDK + c0) = *reinterpret_cast<const uint4*>(yo);
+        *reinterpret_cast<uint4*>(Qs + t * LDK + c0) = *reinterpret_cast<const uint4*>(qo);
+      }
+      if constexpr (G::kLaInGram) {
+        __syncthreads();
+        // the staging overlapped T and P: their blocks above the diagonal
+        // are zero again
+        for (int e = tid; e < C * C; e += G::NT) {
+          const int rr = e / C, cc = e % C;
+          if ((cc >> 4) > (rr >> 4)) {
+            Tb[rr * LDC + cc] = zero;
+            Pb[rr * LDC + cc] = zero;
+          }
         }
       }
-      if (part == 0) gC[c] = __expf(total_la);
     }
-    if (n + (int)gridDim.x < total) regs.load(p, n + gridDim.x, nchunks);
     __syncthreads();
     if constexpr (kFused) {
       // ---- K~ = (P d^T + L A) * K in place over the raw keys --------------
@@ -405,7 +446,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         mma(aa, fy, fx);
         mma(pa, fq, fx);
         if (a > b) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = a * 16 + acc_row(i), cc = b * 16 + acc_col();
             Ab[rr * LDC + cc] = from_f32<Tin>(aa[i]);
@@ -420,7 +461,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
           col.w = acc_row(3) > acc_col() ? aa[3] : 0.f;
           float* Ad = Am + a * 16 * G::LDD;
           *reinterpret_cast<float4*>(Ad + acc_col() * G::LDD + acc_row(0)) = col;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = a * 16 + acc_row(i), cc = a * 16 + acc_col();
             Pb[rr * LDC + cc] = from_f32<Tin>(cc <= rr ? pa[i] : 0.f);
@@ -431,22 +472,22 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
           if (lane < 16) {
             const int c = lane;
             float x[16], sv[16];
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) sv[i] = (i == c) ? 1.f : 0.f;
-  #pragma unroll
+#pragma unroll
             for (int m = 0; m < 16; ++m) {
               x[m] = sv[m];
               float cv[16];
-  #pragma unroll
+#pragma unroll
               for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 v4 = *reinterpret_cast<const float4*>(Ad + m * G::LDD + 4 * q4);
                 cv[4 * q4] = v4.x; cv[4 * q4 + 1] = v4.y;
                 cv[4 * q4 + 2] = v4.z; cv[4 * q4 + 3] = v4.w;
               }
-  #pragma unroll
+#pragma unroll
               for (int i = m + 1; i < 16; ++i) sv[i] -= cv[i] * x[m];
             }
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i)
               Tb[(a * 16 + i) * LDC + a * 16 + c] = from_f32<Tin>(x[i]);
           }
@@ -460,16 +501,16 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         if constexpr (kGdn2) {
           const float gd = gC[db * 16 + (lane & 15)];
           if constexpr (sizeof(Tin) == 2) {
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < Frag<C, Tin>::N32; ++i)
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 8; ++e) fx.v[i][e] = (__bf16)((float)fx.v[i][e] * gd);
             if constexpr (Frag<C, Tin>::R16) {
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 4; ++e) fx.t[e] = (__bf16)((float)fx.t[e] * gd);
             }
           } else {
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < C / 4; ++i) fx.v[i] *= gd;
           }
         }
@@ -481,13 +522,17 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
     __syncthreads();
 
+    // The next chunk's raw operands are fetched from here on (issuing them
+    // earlier makes the compiler wait for them inside the job loops above).
+    if (n + (int)gridDim.x < total) regs.load(p, n + gridDim.x, nchunks);
+
     // ---- recursive doubling, T21 = -T22 (A21 T11) ----------------------------
     // One job = one 16-wide column of T21 in one pair: that column of
     // Y = A21 T11 goes to the wave's own scratch (row-major), then the same
     // column of T21 = -T22 Y; the right operands are read k-major.
     {
       Tin* ys = Ysc + wave * (C / 2) * LDS16;
-  #pragma unroll
+#pragma unroll
       for (int s = 16; s < C; s *= 2) {
         const int nt = s / 16;
         const int jobs = (C / (2 * s)) * nt;
@@ -502,7 +547,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
               fb.load_kmajor(Tb + (cb + kk) * LDC + cb + c * 16, LDC);
               mma(acc, fa, fb);
             }
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i)
               ys[(r * 16 + acc_row(i)) * LDS16 + acc_col()] = from_f32<Tin>(acc[i]);
           }
@@ -515,7 +560,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
               fb.load_kmajor(ys + kk * LDS16, LDS16);
               mma(acc, fa, fb);
             }
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i)
               Tb[(rb + r * 16 + acc_row(i)) * LDC + cb + c * 16 + acc_col()] =
                   from_f32<Tin>(-acc[i]);
@@ -532,7 +577,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     const size_t uoff = (size_t)n * C * DV;
     {
       Frag<C, Tin> ft[TB];
-  #pragma unroll
+#pragma unroll
       for (int tb = 0; tb < TB; ++tb) ft[tb].load(Tb + tb * 16 * LDC, LDC);
       for (int job = wave; job < DB + VBT; job += NW) {
         const bool isU = job >= DB;
@@ -542,14 +587,14 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         Frag<C, Tin> fm;
         fm.load_kmajor(M + ct * 16, ld);
         f32x4 acc[TB];
-  #pragma unroll
+#pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
           acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
           mma(acc[tb], ft[tb], fm);
         }
-  #pragma unroll
+#pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i)
             M[(tb * 16 + acc_row(i)) * ld + ct * 16 + acc_col()] = from_f32<Tin>(acc[tb][i]);
           if (isU) acc_store(acc[tb], wb.u + uoff + (size_t)(tb * VBT + ct) * 256);
@@ -561,7 +606,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     // ---- Q' = Q - P Wk (in place) and O' = P U ------------------------------
     {
       Frag<C, Tin> fp[TB];
-  #pragma unroll
+#pragma unroll
       for (int tb = 0; tb < TB; ++tb) fp[tb].load(Pb + tb * 16 * LDC, LDC);
       for (int job = wave; job < DB + VBT; job += NW) {
         const bool isO = job >= DB;
@@ -571,14 +616,14 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
           fm.load_kmajor(Zs + ct * 16, LDV);
         else
           fm.load_kmajor(Ys + ct * 16, LDK);
-  #pragma unroll
+#pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           mma(acc, fp[tb], fm);
           if (isO) {
             acc_store(acc, wb.op + uoff + (size_t)(tb * VBT + ct) * 256);
           } else {
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
               Tin* qe = Qs + (tb * 16 + acc_row(i)) * LDK + ct * 16 + acc_col();
               *qe = from_f32<Tin>(to_f32(*qe) - acc[i]);
