@@ -17,8 +17,9 @@
 //   d_C = P_C d0 + A^T (c * g),   c_i = P_C / P_{i+1},
 //   K~  = (P d0^T + L A) * K,     L[t][i] = (P_t / P_{i+1}) g_i  (i < t).
 // Only the middle line links the chunks. Three kernels:
-//   prep    one workgroup per chunk, all chunks at once: the Gram matrix of
-//           a, M, T, and the chunk record {log P prefix, g0, V};
+//   prep    persistent workgroups over all chunks at once (the next chunk
+//           fetched during the current one): the Gram matrix of a, M, T,
+//           and the chunk record {log P prefix, g0, V};
 //   chain   one workgroup per (batch, head): the serial part, three
 //           matrix-vector products per chunk (x = A d, g = g0 - V x,
 //           d <- P_C d + A^T (c*g)); records d at each chunk entry and g;
@@ -78,10 +79,13 @@ __device__ __forceinline__ void split_bf16(float a, __bf16& hi, __bf16& lo) {
 // ---------------------------------------------------------------------------
 // prep: everything of a chunk that does not depend on d
 // ---------------------------------------------------------------------------
+// Persistent: workgroup g takes chunks g, g + gridDim.x, ... and fetches the
+// next chunk's keys and gates while the current one computes.
 template <int DK, typename Tin>
 __global__ __launch_bounds__(256) void precond_prep_kernel(
-    int T, int nchunks, const Tin* __restrict__ k, const float* __restrict__ beta,
-    const float* __restrict__ r, float eta, float* __restrict__ rec) {
+    int T, int nchunks, int total, const Tin* __restrict__ k,
+    const float* __restrict__ beta, const float* __restrict__ r, float eta,
+    float* __restrict__ rec) {
   using G = P1Cfg<DK, Tin>;
   constexpr int C = G::C, LDH = G::LDH, LDF = G::LDF, LDYS = G::LDYS,
                 TB = G::TB, VEC = G::VEC, NCB = G::NCB;
@@ -97,206 +101,225 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
   float* ev = nv + C;     // eta beta / n
   float* rho = ev + C;    // eta beta^2 / n
   float* hv = rho + C;    // rho P
-
-  const int bh = blockIdx.x / nchunks, j = blockIdx.x - bh * nchunks;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int valid = min(C, T - j * C);
-  const size_t t0 = (size_t)bh * T + (size_t)j * C;
-  float* out = rec + (size_t)blockIdx.x * G::RS;
 
-  // ---- keys: split squares and row norms; gates --------------------------
+  // next chunk's keys (row e / NCB, 16-byte block e % NCB) and, on wave 0,
+  // its gates (token = lane); padding tokens read as zero keys, r = 1, beta = 0
+  uint4 kr[G::NLK];
+  float rt = 1.f, bt = 0.f;
+  auto fetch = [&](int n) {
+    const int bh = n / nchunks, j = n - bh * nchunks;
+    const int valid = min(C, T - j * C);
+    const size_t t0 = (size_t)bh * T + (size_t)j * C;
 #pragma unroll
-  for (int i = 0; i < G::NLK; ++i) {
-    const int e = tid + i * G::NT;
-    const int rr = e / NCB, cc = (e % NCB) * VEC;
-    uint4 kr = {0u, 0u, 0u, 0u};
-    if (rr < valid) kr = *reinterpret_cast<const uint4*>(k + (t0 + rr) * DK + cc);
-    const Tin* kv = reinterpret_cast<const Tin*>(&kr);
-    __bf16 hi[VEC], lo[VEC];
-    float part = 0.f;
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) {
-      const float x = to_f32(kv[u]);
-      const float a = x * x;
-      part += a;
-      split_bf16(a, hi[u], lo[u]);
+    for (int i = 0; i < G::NLK; ++i) {
+      const int e = tid + i * G::NT;
+      const int rr = e / NCB, cc = (e % NCB) * VEC;
+      kr[i] = uint4{0u, 0u, 0u, 0u};
+      if (rr < valid) kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + rr) * DK + cc);
     }
-    if constexpr (VEC == 8) {
-      *reinterpret_cast<uint4*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint4*>(hi);
-      *reinterpret_cast<uint4*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint4*>(lo);
-    } else {
-      *reinterpret_cast<uint2*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint2*>(hi);
-      *reinterpret_cast<uint2*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint2*>(lo);
+    if (wave == 0) {
+      rt = (lane < valid && r) ? r[t0 + lane] : 1.f;
+      bt = (lane < valid) ? beta[t0 + lane] : 0.f;
     }
-    // the NCB lanes of one row are consecutive and aligned
-    part = group_sum<NCB>(part);
-    if (e % NCB == 0) nv[rr] = part;
-  }
-  if (wave == 0) {
-    // exclusive prefix of log r (r clamped away from 0 so that ratios of
-    // prefixes stay finite); padding tokens have r = 1, beta = 0
-    const float rt = (lane < valid && r) ? r[t0 + lane] : 1.f;
-    const float bt = (lane < valid) ? beta[t0 + lane] : 0.f;
-    const float lr = logf(fmaxf(rt, 1e-30f));
-    const float inc = wave_prefix_sum(lr);
-    lpv[lane] = inc - lr;
-    if (lane == C - 1) lpv[C] = inc;
-    bev[lane] = bt;
-  }
-  __syncthreads();
+  };
+  if ((int)blockIdx.x < total) fetch(blockIdx.x);
 
-  // ---- per-token scalars; Gram of a (split bf16 MFMA) ----------------------
-  if (wave == 0) {
-    const int t = lane;
-    const float n = nv[t], bt = bev[t];
-    const float e = n > 0.f ? eta * bt / n : 0.f;
-    ev[t] = e;
-    rho[t] = e * bt;
-    hv[t] = e * bt * expf(lpv[t]);
-  }
-  // Tile list: wave w owns the diagonal tile (w, w) and a share of the
-  // off-diagonal lower tiles, and keeps its accumulators in registers.
-  constexpr int NL = TB * (TB + 1) / 2;
-  constexpr int NJ = 1 + (NL - TB + G::NW - 1) / G::NW;
-  f32x4 gacc[NJ];
-  int gja[NJ], gjb[NJ];
+  for (int n = blockIdx.x; n < total; n += gridDim.x) {
+    float* out = rec + (size_t)n * G::RS;
+
+    // ---- keys: split squares and row norms; gates --------------------------
 #pragma unroll
-  for (int s2 = 0; s2 < NJ; ++s2) {
-    int a = -1, b = -1;
-    const int job = wave + G::NW * s2;
-    if (s2 == 0) {
-      if (wave < TB) { a = wave; b = wave; }
-    } else {
-      // off-diagonal tiles in row-major order, dealt round-robin
-      int l = job - G::NW, aa = 1;
-      if (l >= 0) {
-        while (l >= aa) { l -= aa; ++aa; }
-        if (aa < TB) { a = aa; b = l; }
+    for (int i = 0; i < G::NLK; ++i) {
+      const int e = tid + i * G::NT;
+      const int rr = e / NCB, cc = (e % NCB) * VEC;
+      const Tin* kv = reinterpret_cast<const Tin*>(&kr[i]);
+      __bf16 hi[VEC], lo[VEC];
+      float part = 0.f;
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) {
+        const float x = to_f32(kv[u]);
+        const float a = x * x;
+        part += a;
+        split_bf16(a, hi[u], lo[u]);
       }
-    }
-    gja[s2] = a;
-    gjb[s2] = b;
-    gacc[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (a >= 0) {
-      Frag<DK, __bf16> ah, al, bh_, bl;
-      ah.load(Ah + a * 16 * LDH, LDH);
-      al.load(Al + a * 16 * LDH, LDH);
-      bh_.load(Ah + b * 16 * LDH, LDH);
-      bl.load(Al + b * 16 * LDH, LDH);
-      mma(gacc[s2], ah, bh_);
-      mma(gacc[s2], ah, bl);
-      mma(gacc[s2], al, bh_);
-    }
-  }
-  __syncthreads();  // the split squares are dead from here on (T reuses them)
-  // M[t][i] = rho_t (P_t / P_{i+1}) <a_i, a_t> for i < t
-#pragma unroll
-  for (int s2 = 0; s2 < NJ; ++s2) {
-    const int a = gja[s2], b = gjb[s2];
-    if (a >= 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = a * 16 + acc_row(i), c = b * 16 + acc_col();
-        Mf[t * LDF + c] =
-            c < t ? rho[t] * __expf(lpv[t] - lpv[c + 1]) * gacc[s2][i] : 0.f;
+      if constexpr (VEC == 8) {
+        *reinterpret_cast<uint4*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint4*>(hi);
+        *reinterpret_cast<uint4*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint4*>(lo);
+      } else {
+        *reinterpret_cast<uint2*>(Ah + rr * LDH + cc) = *reinterpret_cast<const uint2*>(hi);
+        *reinterpret_cast<uint2*>(Al + rr * LDH + cc) = *reinterpret_cast<const uint2*>(lo);
       }
+      // the NCB lanes of one row are consecutive and aligned
+      part = group_sum<NCB>(part);
+      if (e % NCB == 0) nv[rr] = part;
     }
-  }
-  // Blocks of T above the diagonal are zero.
-  for (int e = tid; e < C * C; e += G::NT) {
-    const int rr = e / C, cc = e % C;
-    if ((cc >> 4) > (rr >> 4)) Tf[rr * LDF + cc] = 0.f;
-  }
-
-  // ---- diagonal 16x16 blocks of T = (I + M)^-1 ----------------------------
-  // Wave b wrote diagonal tile (b, b) of M itself; lane c < 16 owns column c.
-  if (wave < TB) {
-    wave_lds_sync();
-    if (lane < 16) {
-      const int b = wave, c = lane;
-      const float* Mblk = Mf + b * 16 * LDF + b * 16;
-      float x[16], s[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        x[m] = s[m];
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) s[i] -= Mblk[i * LDF + m] * x[m];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Tf[(b * 16 + i) * LDF + b * 16 + c] = x[i];
+    if (wave == 0) {
+      // exclusive prefix of log r (r clamped away from 0 so that ratios of
+      // prefixes stay finite)
+      const float lr = logf(fmaxf(rt, 1e-30f));
+      const float inc = wave_prefix_sum(lr);
+      lpv[lane] = inc - lr;
+      if (lane == C - 1) lpv[C] = inc;
+      bev[lane] = bt;
     }
-  }
-  __syncthreads();
+    if (n + (int)gridDim.x < total) fetch(n + gridDim.x);
+    __syncthreads();
 
-  // ---- recursive doubling in fp32, T21 = -T22 (M21 T11) --------------------
-  // One job = one 16-wide column of T21 in one pair: that column of
-  // Y = M21 T11 goes to the wave's own scratch, then the same column of
-  // T21 = -T22 Y; the right operands are read k-major.
-  {
-    float* ys = Ysc + wave * (C / 2) * LDYS;
+    // ---- per-token scalars; Gram of a (split bf16 MFMA) ----------------------
+    if (wave == 0) {
+      const int t = lane;
+      const float n = nv[t], bt = bev[t];
+      const float e = n > 0.f ? eta * bt / n : 0.f;
+      ev[t] = e;
+      rho[t] = e * bt;
+      hv[t] = e * bt * expf(lpv[t]);
+    }
+    // Tile list: wave w owns the diagonal tile (w, w) and a share of the
+    // off-diagonal lower tiles, and keeps its accumulators in registers.
+    constexpr int NL = TB * (TB + 1) / 2;
+    constexpr int NJ = 1 + (NL - TB + G::NW - 1) / G::NW;
+    f32x4 gacc[NJ];
+    int gja[NJ], gjb[NJ];
 #pragma unroll
-    for (int s = 16; s < C; s *= 2) {
-      const int nt = s / 16, jobs = (C / (2 * s)) * nt;
-      for (int job = wave; job < jobs; job += G::NW) {
-        const int pp = job / nt, c = job % nt;
-        const int rb = 2 * s * pp + s, cb = 2 * s * pp;
-        for (int rt = 0; rt < nt; ++rt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          for (int kk = 0; kk < s; kk += 16) {
-            Frag<16, float> fa, fb;
-            fa.load(Mf + (rb + rt * 16) * LDF + cb + kk, LDF);
-            fb.load_kmajor(Tf + (cb + kk) * LDF + cb + c * 16, LDF);
-            mma(acc, fa, fb);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ys[(rt * 16 + acc_row(i)) * LDYS + acc_col()] = acc[i];
+    for (int s2 = 0; s2 < NJ; ++s2) {
+      int a = -1, b = -1;
+      const int job = wave + G::NW * s2;
+      if (s2 == 0) {
+        if (wave < TB) { a = wave; b = wave; }
+      } else {
+        // off-diagonal tiles in row-major order, dealt round-robin
+        int l = job - G::NW, aa = 1;
+        if (l >= 0) {
+          while (l >= aa) { l -= aa; ++aa; }
+          if (aa < TB) { a = aa; b = l; }
         }
-        wave_lds_sync();
-        for (int rt = 0; rt < nt; ++rt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          for (int kk = 0; kk < s; kk += 16) {
-            Frag<16, float> fa, fb;
-            fa.load(Tf + (rb + rt * 16) * LDF + rb + kk, LDF);
-            fb.load_kmajor(ys + kk * LDYS, LDYS);
-            mma(acc, fa, fb);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            Tf[(rb + rt * 16 + acc_row(i)) * LDF + cb + c * 16 + acc_col()] = -acc[i];
-        }
-        wave_lds_sync();  // the scratch is rewritten by this wave's next job
       }
-      __syncthreads();
+      gja[s2] = a;
+      gjb[s2] = b;
+      gacc[s2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (a >= 0) {
+        Frag<DK, __bf16> ah, al, bh_, bl;
+        ah.load(Ah + a * 16 * LDH, LDH);
+        al.load(Al + a * 16 * LDH, LDH);
+        bh_.load(Ah + b * 16 * LDH, LDH);
+        bl.load(Al + b * 16 * LDH, LDH);
+        mma(gacc[s2], ah, bh_);
+        mma(gacc[s2], ah, bl);
+        mma(gacc[s2], al, bh_);
+      }
     }
-  }
-
-  // ---- chunk record: lp, g0 = T e, V = T diag(h) ---------------------------
-  for (int e = tid; e <= C; e += G::NT) out[G::R_LP + e] = lpv[e];
-  {
-    // four threads per row, one 16-wide block each (zero above the diagonal)
-    const int t = tid >> 2, q = tid & 3;
-    float s = 0.f;
-    if (q <= (t >> 4)) {
+    __syncthreads();  // the split squares are dead from here on (T reuses them)
+    // M[t][i] = rho_t (P_t / P_{i+1}) <a_i, a_t> for i < t
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s += Tf[t * LDF + 16 * q + i] * ev[16 * q + i];
+    for (int s2 = 0; s2 < NJ; ++s2) {
+      const int a = gja[s2], b = gjb[s2];
+      if (a >= 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = a * 16 + acc_row(i), c = b * 16 + acc_col();
+          Mf[t * LDF + c] =
+              c < t ? rho[t] * __expf(lpv[t] - lpv[c + 1]) * gacc[s2][i] : 0.f;
+        }
+      }
     }
-    s = group_sum<4>(s);
-    if (q == 0) out[G::R_G + t] = s;
-  }
-  for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
-    const int t = e4 / (C / 4), c0 = (e4 % (C / 4)) * 4;
-    float4 v = {0.f, 0.f, 0.f, 0.f};
-    if ((c0 >> 4) <= (t >> 4)) {
-      const float* tr = Tf + t * LDF + c0;
-      v.x = tr[0] * hv[c0];
-      v.y = tr[1] * hv[c0 + 1];
-      v.z = tr[2] * hv[c0 + 2];
-      v.w = tr[3] * hv[c0 + 3];
+    // Blocks of T above the diagonal are zero.
+    for (int e = tid; e < C * C; e += G::NT) {
+      const int rr = e / C, cc = e % C;
+      if ((cc >> 4) > (rr >> 4)) Tf[rr * LDF + cc] = 0.f;
     }
-    *reinterpret_cast<float4*>(out + G::R_V + t * C + c0) = v;
+
+    // ---- diagonal 16x16 blocks of T = (I + M)^-1 ----------------------------
+    // Wave b wrote diagonal tile (b, b) of M itself; lane c < 16 owns column c.
+    if (wave < TB) {
+      wave_lds_sync();
+      if (lane < 16) {
+        const int b = wave, c = lane;
+        const float* Mblk = Mf + b * 16 * LDF + b * 16;
+        float x[16], s[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = (i == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          x[m] = s[m];
+#pragma unroll
+          for (int i = m + 1; i < 16; ++i) s[i] -= Mblk[i * LDF + m] * x[m];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Tf[(b * 16 + i) * LDF + b * 16 + c] = x[i];
+      }
+    }
+    __syncthreads();
+
+    // ---- recursive doubling in fp32, T21 = -T22 (M21 T11) --------------------
+    // One job = one 16-wide column of T21 in one pair: that column of
+    // Y = M21 T11 goes to the wave's own scratch, then the same column of
+    // T21 = -T22 Y; the right operands are read k-major.
+    {
+      float* ys = Ysc + wave * (C / 2) * LDYS;
+#pragma unroll
+      for (int s = 16; s < C; s *= 2) {
+        const int nt = s / 16, jobs = (C / (2 * s)) * nt;
+        for (int job = wave; job < jobs; job += G::NW) {
+          const int pp = job / nt, c = job % nt;
+          const int rb = 2 * s * pp + s, cb = 2 * s * pp;
+          for (int rt = 0; rt < nt; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < s; kk += 16) {
+              Frag<16, float> fa, fb;
+              fa.load(Mf + (rb + rt * 16) * LDF + cb + kk, LDF);
+              fb.load_kmajor(Tf + (cb + kk) * LDF + cb + c * 16, LDF);
+              mma(acc, fa, fb);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              ys[(rt * 16 + acc_row(i)) * LDYS + acc_col()] = acc[i];
+          }
+          wave_lds_sync();
+          for (int rt = 0; rt < nt; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < s; kk += 16) {
+              Frag<16, float> fa, fb;
+              fa.load(Tf + (rb + rt * 16) * LDF + rb + kk, LDF);
+              fb.load_kmajor(ys + kk * LDYS, LDYS);
+              mma(acc, fa, fb);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              Tf[(rb + rt * 16 + acc_row(i)) * LDF + cb + c * 16 + acc_col()] = -acc[i];
+          }
+          wave_lds_sync();  // the scratch is rewritten by this wave's next job
+        }
+        __syncthreads();
+      }
+    }
+
+    // ---- chunk record: lp, g0 = T e, V = T diag(h) ---------------------------
+    for (int e = tid; e <= C; e += G::NT) out[G::R_LP + e] = lpv[e];
+    {
+      // four threads per row, one 16-wide block each (zero above the diagonal)
+      const int t = tid >> 2, q = tid & 3;
+      float s = 0.f;
+      if (q <= (t >> 4)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += Tf[t * LDF + 16 * q + i] * ev[16 * q + i];
+      }
+      s = group_sum<4>(s);
+      if (q == 0) out[G::R_G + t] = s;
+    }
+    for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
+      const int t = e4 / (C / 4), c0 = (e4 % (C / 4)) * 4;
+      float4 v = {0.f, 0.f, 0.f, 0.f};
+      if ((c0 >> 4) <= (t >> 4)) {
+        const float* tr = Tf + t * LDF + c0;
+        v.x = tr[0] * hv[c0];
+        v.y = tr[1] * hv[c0 + 1];
+        v.z = tr[2] * hv[c0 + 2];
+        v.w = tr[3] * hv[c0 + 3];
+      }
+      *reinterpret_cast<float4*>(out + G::R_V + t * C + c0) = v;
+    }
+    __syncthreads();  // the next chunk's split squares overwrite T
   }
 }
 
@@ -545,8 +568,12 @@ static int launch_dk(const PrecondArgs& a, hipStream_t s) {
   const dim3 block(256);
   if (nch > 0) {
     ktimer_before(s, "precond_prep");
-    hipLaunchKernelGGL((precond_prep_kernel<DK, Tin>), dim3(BH * nch), block, 0, s,
-                       a.T, nch, (const Tin*)a.k, a.beta, a.r, a.eta, rec);
+    // persistent grid: as many workgroups as fit on the 256 compute units
+    constexpr int per_cu = (int)(163840 / G::prep_bytes);
+    const int total = BH * nch;
+    const int grid = total < 256 * per_cu ? total : 256 * per_cu;
+    hipLaunchKernelGGL((precond_prep_kernel<DK, Tin>), dim3(grid), block, 0, s,
+                       a.T, nch, total, (const Tin*)a.k, a.beta, a.r, a.eta, rec);
     ktimer_after(s);
     const int rc = (int)hipGetLastError();
     if (rc) return rc;
