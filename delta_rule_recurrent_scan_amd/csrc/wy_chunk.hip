@@ -34,8 +34,8 @@
 // * scan: one workgroup (4 waves) per (batch, head, VT-wide value tile) walks
 //   the chunks in order with the VT x Dk state slice in fp32 MFMA
 //   accumulators: two products into W and O, one into the state, two
-//   barriers per chunk; operands are fetched into registers two chunks ahead
-//   and handed over through an LDS stage.
+//   barriers per chunk; each chunk's operands are fetched into registers
+//   during the step before (two register sets used in turn).
 #include <algorithm>
 #include <type_traits>
 
@@ -656,12 +656,13 @@ template <int DK, int C, int VT, typename Tin>
 struct ScanCfg {
   static constexpr int NW = 4, NT = 256;
   static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
-  static constexpr int LDK = DK + PAD, LDR = VT + PAD;
+  static constexpr int LDK = DK + PAD, LDW = C + PAD, LDO = VT + PAD;
   static constexpr int TB = C / 16, VB = VT / 16, DB = DK / 16;
   static constexpr size_t E = sizeof(Tin);
-  static constexpr size_t oS = 0;
-  static constexpr size_t oW = oS + (size_t)VT * LDK * E;
-  static constexpr size_t bytes = oW + (size_t)C * LDR * E;
+  static constexpr size_t oS = 0;                                 // state copy [VT][Dk]
+  static constexpr size_t oW = oS + (size_t)VT * LDK * E;        // W^T [VT][C]
+  static constexpr size_t oO = oW + (size_t)VT * LDW * E;        // output rows [C][VT]
+  static constexpr size_t bytes = oO + (size_t)C * LDO * E;
   // State tiles per wave: every value tile times a contiguous run of DPW
   // channel tiles.
   static constexpr int DPW = (DB + NW - 1) / NW;
@@ -698,68 +699,6 @@ struct ScanRegs {
   Frag<C, Tin> x[G::DPW];
   float gd[G::DPW];
 
-  // Lane-interleaved copy in LDS (16-byte word w of lane l at [w][l]), one
-  // region per wave: the hand-off between the chunk step that fetches the
-  // operands and the step that uses them.
-  template <int K>
-  static constexpr size_t fbytes() {
-    if constexpr (sizeof(Tin) == 2)
-      return (size_t)(K / 32) * 16 + ((K % 32) ? 8 : 0);
-    else
-      return (size_t)K;   // K/4 floats
-  }
-  static constexpr size_t BYTES = 2 * fbytes<DK>() + 2 * G::VB * sizeof(RawTile<Tin>) +
-                                  G::DPW * fbytes<C>() + G::DPW * sizeof(float);
-  static constexpr int WORDS = (int)((BYTES + 15) / 16);
-
-  template <int K>
-  __device__ __forceinline__ static void put(unsigned char* b, size_t& o, const Frag<K, Tin>& f) {
-    __builtin_memcpy(b + o, &f.v, fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0));
-    o += fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0);
-    if constexpr (sizeof(Tin) == 2) {
-      if constexpr (Frag<K, Tin>::R16) { __builtin_memcpy(b + o, &f.t, 8); o += 8; }
-    }
-  }
-  template <int K>
-  __device__ __forceinline__ static void get(const unsigned char* b, size_t& o, Frag<K, Tin>& f) {
-    __builtin_memcpy(&f.v, b + o, fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0));
-    o += fbytes<K>() - ((sizeof(Tin) == 2 && (K % 32)) ? 8 : 0);
-    if constexpr (sizeof(Tin) == 2) {
-      if constexpr (Frag<K, Tin>::R16) { __builtin_memcpy(&f.t, b + o, 8); o += 8; }
-    }
-  }
-  __device__ __forceinline__ void stash(uint4* base) const {
-    uint4 w[WORDS];
-    unsigned char* b = reinterpret_cast<unsigned char*>(w);
-    size_t o = 0;
-    put<DK>(b, o, wk);
-    put<DK>(b, o, qp);
-    __builtin_memcpy(b + o, u, sizeof(u)); o += sizeof(u);
-    __builtin_memcpy(b + o, op, sizeof(op)); o += sizeof(op);
-#pragma unroll
-    for (int d = 0; d < G::DPW; ++d) put<C>(b, o, x[d]);
-    __builtin_memcpy(b + o, gd, sizeof(gd)); o += sizeof(gd);
-    for (; o < (size_t)WORDS * 16; ++o) b[o] = 0;
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) base[i * 64 + lane] = w[i];
-  }
-  __device__ __forceinline__ void unstash(const uint4* base) {
-    uint4 w[WORDS];
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) w[i] = base[i * 64 + lane];
-    const unsigned char* b = reinterpret_cast<const unsigned char*>(w);
-    size_t o = 0;
-    get<DK>(b, o, wk);
-    get<DK>(b, o, qp);
-    __builtin_memcpy(u, b + o, sizeof(u)); o += sizeof(u);
-    __builtin_memcpy(op, b + o, sizeof(op)); o += sizeof(op);
-#pragma unroll
-    for (int d = 0; d < G::DPW; ++d) get<C>(b, o, x[d]);
-    __builtin_memcpy(gd, b + o, sizeof(gd));
-  }
-
   // Loads are unconditional (indices of idle waves clamped into range), so
   // that the compiler can count them and a prefetch is only waited on where
   // its data is used.
@@ -791,17 +730,12 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
                                                       WyBufs<Tin> wb) {
   using G = ScanCfg<DK, C, VT, Tin>;
   using R = ScanRegs<GDN2, DK, C, VT, Tin>;
-  constexpr int LDK = G::LDK, LDR = G::LDR, TB = G::TB, VB = G::VB, DB = G::DB,
-                DPW = G::DPW;
-  // hand-off stage: NW per-wave regions after the state and W tiles. A
-  // wave reads its region at the start of a step and refills it at the end
-  // (LDS operations of one wave complete in order).
-  constexpr size_t kStage = (size_t)R::WORDS * 64 * 16 * G::NW;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes + kStage];
+  constexpr int LDK = G::LDK, LDW = G::LDW, LDO = G::LDO, TB = G::TB, VB = G::VB,
+                DB = G::DB, DPW = G::DPW;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
   Tin* Ss = reinterpret_cast<Tin*>(smem + G::oS);   // state copy [v][dk]
-  Tin* Wm = reinterpret_cast<Tin*>(smem + G::oW);   // W [C][VT]
-  uint4* stage = reinterpret_cast<uint4*>(smem + G::bytes) +
-                 (size_t)(threadIdx.x >> 6) * R::WORDS * 64;
+  Tin* Wt = reinterpret_cast<Tin*>(smem + G::oW);   // W^T [v][t]
+  Tin* Os = reinterpret_cast<Tin*>(smem + G::oO);   // output rows [t][v]
 
   const int T = p.T, Dv = p.Dv;
   const int nvt = Dv / VT;
@@ -844,21 +778,21 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   __syncthreads();
 
   // One chunk step; TAIL: the chunk may be partial (rows past T are not
-  // stored). On entry the stage holds chunk j and `give` holds chunk j + 1
-  // (fetched during the previous step); chunk j + 2 is fetched into `fetch`
-  // at the start, and `give` is handed to the stage at the end, where its
-  // arrival (one step after it was issued) is awaited. Guards that always
-  // hold for the tile configuration fold away at compile time.
+  // stored). `cur` holds chunk j (fetched during the previous step); chunk
+  // j + 1 is fetched into `fetch` at the start (the last chunk again on the
+  // final step, so that every step issues the same loads). Guards that
+  // always hold for the tile configuration fold away at compile time.
   constexpr bool kAllRowWaves = TB == G::NW, kAllColWaves = DPW * G::NW == DB;
   const size_t n0 = (size_t)bh * nchunks;
-  auto step = [&](int j, auto tail, R& fetch, const R& give) {
+  auto step = [&](int j, auto tail, R& fetch, const R& cur) {
     constexpr bool TAIL = decltype(tail)::value;
     const size_t t0 = (size_t)bh * T + (size_t)j * C;
     const int valid = min(C, T - j * C);
-    if (j + 2 < nchunks) fetch.load(wb, n0 + j + 2, Dv, vt, wave);
-    R cur;
-    cur.unstash(stage);
-    // ---- W = U - Wk S0^T (to LDS), O = O' + Q' S0^T (stored) --------------
+    fetch.load(wb, n0 + min(j + 1, nchunks - 1), Dv, vt, wave);
+    // ---- W = U - Wk S0^T (to LDS, transposed), O = O' + Q' S0^T -----------
+    // A lane's four W values (tokens 4g..4g+3 of one column) are contiguous
+    // in W^T; the wave's 16 output rows are staged in LDS and stored as one
+    // 16-byte access per lane.
     if (kAllRowWaves || wave < TB) {
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
@@ -867,14 +801,33 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
         f32x4 wa = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
         mma(wa, cur.wk, fs);
         mma(oa, cur.qp, fs);
+        Tin w4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = wave * 16 + acc_row(i);
-          Wm[rr * LDR + vb * 16 + acc_col()] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
-          if (!TAIL || rr < valid)
-            o[(t0 + rr) * Dv + v0 + vb * 16 + acc_col()] =
-                from_f32<Tin>(p.scale * (cur.op[vb][i] + oa[i]));
+          w4[i] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
+          Os[(wave * 16 + acc_row(i)) * LDO + vb * 16 + acc_col()] =
+              from_f32<Tin>(p.scale * (cur.op[vb][i] + oa[i]));
         }
+        typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
+        if constexpr (sizeof(Tin) == 2)
+          *reinterpret_cast<u16x4*>(Wt + (vb * 16 + acc_col()) * LDW + wave * 16 + acc_row(0)) =
+              *reinterpret_cast<const u16x4*>(w4);
+        else
+          *reinterpret_cast<float4*>(Wt + (vb * 16 + acc_col()) * LDW + wave * 16 + acc_row(0)) =
+              *reinterpret_cast<const float4*>(w4);
+      }
+      // the wave's output rows (written by this wave only)
+      wave_lds_sync();
+      constexpr int VPL = 16 / (int)sizeof(Tin);           // elements per lane access
+      constexpr int LPR = VT / VPL;                        // lanes per row
+      constexpr int RPI = 64 / LPR;                        // rows per access
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += RPI) {
+        const int rr = wave * 16 + r0 + (threadIdx.x & 63) / LPR;
+        const int cc = ((threadIdx.x & 63) % LPR) * VPL;
+        if (r0 + (threadIdx.x & 63) / LPR < 16 && (!TAIL || rr < valid))
+          *reinterpret_cast<uint4*>(o + (t0 + rr) * Dv + v0 + cc) =
+              *reinterpret_cast<const uint4*>(Os + rr * LDO + cc);
       }
     }
     __syncthreads();
@@ -882,7 +835,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
     {
       Frag<C, Tin> fw[VB];
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) fw[vb].load_kmajor(Wm + vb * 16, LDR);
+      for (int vb = 0; vb < VB; ++vb) fw[vb].load(Wt + vb * 16 * LDW, LDW);
 #pragma unroll
       for (int d = 0; d < DPW; ++d) {
         const int db = wave * DPW + d;
@@ -902,20 +855,13 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
         }
       }
     }
-    if (j + 1 < nchunks) give.stash(stage);
     __syncthreads();
   };
 
-  // Two register sets in turn (even steps fetch into rb and hand over ra,
-  // odd steps the reverse), unrolled so that each set is a fixed object.
+  // Two register sets in turn (even steps fetch into rb and use ra, odd
+  // steps the reverse), unrolled so that each set is a fixed object.
   R ra, rb;
-  if (nchunks > 0) {
-    R first;
-    first.load(wb, n0, Dv, vt, wave);
-    first.stash(stage);
-  }
-  if (nchunks > 1) ra.load(wb, n0 + 1, Dv, vt, wave);
-  __syncthreads();
+  if (nchunks > 0) ra.load(wb, n0, Dv, vt, wave);
   using Full = std::false_type;
   using Tail = std::true_type;
   const int nfull = T / C;  // chunks with C valid rows
