@@ -82,7 +82,10 @@ def kernel_bytes_per_token_head(w, apf=False):
     gates = 4 + (4 if apf else 0)
     rec = (2 * C1 + 4 + C1 * C1) * 4.0 / C1   # phase-1 chunk record
     dent = dk * 4.0 / C1                       # d at each chunk entry
-    frags = (3 * dk + 2 * dv) * s              # S0-independent chunk operands
+    # S0-independent chunk operands: Wk, X', U and the scores P; GDN-2 adds
+    # its decayed queries and exit decays
+    frags = (2 * dk + dv + C) * s
+    frags_g = frags + dk * s + 4.0 * dk / C
     return {
         # k, beta, r -> record
         "precond_prep": dk * s + gates + rec,
@@ -90,17 +93,17 @@ def kernel_bytes_per_token_head(w, apf=False):
         "precond_chain": dk * s + rec + 4 + dent,
         # k, log gate prefix, g, d entries -> k~
         "precond_ktilde": 2 * dk * s + 4 * (C1 + 4.0) / C1 + 4 + dent,
-        # q, k, k~, v, beta -> Wk, Q', X', U, O'
+        # q, k, k~, v, beta -> Wk, X', U, P
         "wy_prep": (3 * dk + dv) * s + 4 + frags,
-        # q, k, v, beta, log gate prefix, g, d entries -> Wk, Q', X', U, O'
+        # q, k, v, beta, log gate prefix, g, d entries -> Wk, X', U, P
         "wy_prep_fused": (2 * dk + dv) * s + 4 + 4 * (C1 + 4.0) / C1 + 4 + dent
         + frags,
-        # Wk, Q', X', U, O' -> o
-        "wy_scan": frags + dv * s,
-        # q, k, b, v, w, log alpha -> Wk, Q', X', U, O', exit decay
-        "gdn2_prep": (3 * dk + 2 * dv) * s + 4 * dk + frags + 4.0 * dk / C,
-        # Wk, Q', X', U, O', exit decay -> o
-        "gdn2_scan": frags + 4.0 * dk / C + dv * s,
+        # Wk, X', U, P, q -> o
+        "wy_scan": frags + dk * s + dv * s,
+        # q, k, b, v, w, log alpha -> Wk, X', U, P, Q^, exit decay
+        "gdn2_prep": (3 * dk + 2 * dv) * s + 4 * dk + frags_g,
+        # Wk, X', U, P, Q^, exit decay -> o
+        "gdn2_scan": frags_g + dv * s,
     }
 
 
@@ -114,18 +117,23 @@ def flops_per_token_head(w):
 
 def timed_steps(step, args):
     """Warm up, then time exactly args.steps steps (synchronised on both
-    sides) with the library's per-kernel event timing on; returns the wall
-    time per step (ms) and {kernel: mean ms}."""
+    sides); returns the wall time per step (ms) and {kernel: mean ms}. The
+    per-kernel durations come from a second pass of the same steps with the
+    library's event timing on, so that the events do not weigh on the wall
+    time."""
     import delta_rule_recurrent_scan_amd as osdn
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    osdn.kernel_timing(True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    osdn.kernel_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     osdn.kernel_timing(False)
     kt = {n: ms for n, (cnt, ms) in osdn.kernel_times().items()}
     return wall * 1e3 / args.steps, kt

@@ -88,13 +88,15 @@ struct Frag<KEXT, __bf16> {
   bf16x8 v[N32 > 0 ? N32 : 1];
   bf16x4 t;
   __device__ __forceinline__ void load(const __bf16* base, int ld) {
-    const int lane = threadIdx.x & 63;
-    const __bf16* p = base + (lane & 15) * ld;
-    const int g = lane >> 4;
+    load_row(base + (threadIdx.x & 15) * ld);
+  }
+  // `row` points at the start of this lane's row (row lane % 16 of the tile).
+  __device__ __forceinline__ void load_row(const __bf16* row) {
+    const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int i = 0; i < N32; ++i)
-      v[i] = *reinterpret_cast<const bf16x8*>(p + 32 * i + g * 8);
-    if constexpr (R16) t = *reinterpret_cast<const bf16x4*>(p + 32 * N32 + g * 4);
+      v[i] = *reinterpret_cast<const bf16x8*>(row + 32 * i + g * 8);
+    if constexpr (R16) t = *reinterpret_cast<const bf16x4*>(row + 32 * N32 + g * 4);
   }
   // The same fragment of the transpose of a KEXT x 16 block stored k-major
   // (row k holds 16 consecutive n), by the gfx950 LDS transpose read: within
@@ -144,8 +146,10 @@ template <int KEXT>
 struct Frag<KEXT, float> {
   float v[KEXT / 4];
   __device__ __forceinline__ void load(const float* base, int ld) {
-    const int lane = threadIdx.x & 63;
-    const float* p = base + (lane & 15) * ld + (lane >> 4);
+    load_row(base + (threadIdx.x & 15) * ld);
+  }
+  __device__ __forceinline__ void load_row(const float* row) {
+    const float* p = row + ((threadIdx.x & 63) >> 4);
 #pragma unroll
     for (int i = 0; i < KEXT / 4; ++i) v[i] = p[4 * i];
   }

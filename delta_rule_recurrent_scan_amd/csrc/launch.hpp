@@ -64,9 +64,9 @@ int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 // Device scratch of the chunk engine: per chunk, the S0-independent operands
-// of the chunk step.
+// of the chunk step (GDN-2 has two more: its decayed queries and decays).
 size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
-                          int bf16);
+                          int bf16, int gdn2);
 
 // Kernel timing hooks (no-ops unless enabled through osdn_kernel_timing):
 // an event on stream s before the kernel `name` is launched and one after.

@@ -78,18 +78,23 @@ size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype) {
   return round256(osdn::precond_workspace_bytes(B, H, T, Dk, dtype == OSDN_BF16));
 }
 
-size_t osdn_chunk_workspace_bytes(int B, int H, int T, int Dk, int Dv,
-                                  int chunk, int dtype) {
+static size_t chunk_ws_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
+                             int dtype, int gdn2) {
   if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
       !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
     return 0;
   return round256(osdn::wy_workspace_bytes(B, H, T, Dk, Dv, chunk,
-                                           dtype == OSDN_BF16));
+                                           dtype == OSDN_BF16, gdn2));
+}
+
+size_t osdn_chunk_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                  int chunk, int dtype) {
+  return chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 0);
 }
 
 size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype) {
-  return osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  return chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 1);
 }
 
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,

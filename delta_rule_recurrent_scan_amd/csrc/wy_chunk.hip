@@ -23,19 +23,20 @@
 // decay g = gamma_C; rs = 1.
 //
 // Split by dependence on S0. With P = Q X^T masked to i <= t,
-//   Wk = T diag(rs) Y,  U = T diag(rs) Z,  Q' = Q - P Wk,  O' = P U,
+//   Wk = T diag(rs) Y,  U = T diag(rs) Z,
 // the chunk step is
-//   W = U - Wk S0^T,    O = O' + Q' S0^T,   S1 = S0 diag(g) + W^T X'.
+//   W = U - Wk S0^T,    O = Q S0^T + P W,   S1 = S0 diag(g) + W^T X'.
 // * prep: persistent workgroups of 8 waves over all chunks at once (the next
-//   chunk is fetched while the current one computes) form Wk, U, Q', O' and
-//   X' and write them to the workspace in MFMA operand order.
+//   chunk is fetched while the current one computes) form Wk, U, P and X'
+//   (GDN-2 also its decayed queries and exit decays) and write them to the
+//   workspace in MFMA operand order.
 //   T comes from 16x16 diagonal blocks by fp32 forward substitution (one lane
 //   per column) and recursive doubling, T21 = -T22 A21 T11, on MFMA.
 // * scan: one workgroup (4 waves) per (batch, head, VT-wide value tile) walks
 //   the chunks in order with the VT x Dk state slice in fp32 MFMA
-//   accumulators: two products into W and O, one into the state, two
-//   barriers per chunk; each chunk's operands are fetched into registers
-//   during the step before (two register sets used in turn).
+//   accumulators: W and Q S0^T from the state, then P W and the state update
+//   from W, two barriers per chunk; each chunk's operands are fetched into
+//   registers during the step before (two register sets used in turn).
 #include <algorithm>
 #include <type_traits>
 
@@ -53,34 +54,38 @@ struct Gdn2Variant {};
 struct OsdnFusedVariant {};
 
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
-// storage dtype (g in fp32): Wk and Q' as 16-row A fragments (row block tb
-// at tb*16*Dk), X' as k-major B fragments (channel block db at db*16*C), U
-// and O' as accumulator tiles ((tb, vb) at (tb*Dv/16 + vb)*256).
+// storage dtype: Wk and the scores P as 16-row A fragments (row block tb at
+// tb*16*Dk, resp. tb*16*C), X' as k-major B fragments (channel block db at
+// db*16*C), U as accumulator tiles ((tb, vb) at (tb*Dv/16 + vb)*256). GDN-2
+// adds the decayed queries Q^ (like Wk) and the exit decays g (fp32, Dk per
+// chunk); OSDN's scan reads the queries themselves.
 template <typename Tin>
 struct WyBufs {
-  Tin *wk, *qp, *xp, *u, *op;
+  Tin *wk, *xp, *u, *pp, *qh;
   float* g;
 };
 
 template <typename Tin>
-static WyBufs<Tin> wy_bufs(void* ws, int BH, int nchunks, int C, int Dk, int Dv) {
+static WyBufs<Tin> wy_bufs(void* ws, int BH, int nchunks, int C, int Dk, int Dv,
+                           bool gdn2) {
   const size_t n = (size_t)BH * nchunks * C;
   Tin* b = static_cast<Tin*>(ws);
   WyBufs<Tin> w;
   w.wk = b;
-  w.qp = w.wk + n * Dk;
-  w.xp = w.qp + n * Dk;
+  w.xp = w.wk + n * Dk;
   w.u = w.xp + n * Dk;
-  w.op = w.u + n * Dv;
-  w.g = reinterpret_cast<float*>(w.op + n * Dv);
+  w.pp = w.u + n * Dv;
+  w.qh = gdn2 ? w.pp + n * C : nullptr;
+  w.g = gdn2 ? reinterpret_cast<float*>(w.qh + n * Dk) : nullptr;
   return w;
 }
 
 size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
-                          int bf16) {
+                          int bf16, int gdn2) {
   const size_t n = (size_t)B * H * ((T + chunk - 1) / chunk);
   const size_t e = bf16 ? 2 : 4;
-  return n * chunk * (3 * (size_t)Dk + 2 * (size_t)Dv) * e + n * Dk * 4;
+  const size_t per = n * chunk * (2 * (size_t)Dk + (size_t)Dv + (size_t)chunk) * e;
+  return gdn2 ? per + n * chunk * (size_t)Dk * e + n * Dk * 4 : per;
 }
 
 // ---------------------------------------------------------------------------
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
   Tin* Ys = reinterpret_cast<Tin*>(smem + G::oY);   // diag(rs) Y, then Wk
   Tin* Xs = reinterpret_cast<Tin*>(smem + G::oX);
-  Tin* Qs = reinterpret_cast<Tin*>(smem + G::oQ);   // Q, then Q'
+  Tin* Qs = reinterpret_cast<Tin*>(smem + G::oQ);   // Q (GDN-2: Q^ = gamma q)
   Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);   // diag(rs) Z, then U
   Tin* Ab = reinterpret_cast<Tin*>(smem + G::oAb);
   Tin* Tb = reinterpret_cast<Tin*>(smem + G::oTb);
@@ -603,46 +608,20 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
     __syncthreads();
 
-    // ---- Q' = Q - P Wk (in place) and O' = P U ------------------------------
+    // ---- Wk, P (and GDN-2's Q^) as row-block fragments ----------------------
     {
-      Frag<C, Tin> fp[TB];
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) fp[tb].load(Pb + tb * 16 * LDC, LDC);
-      for (int job = wave; job < DB + VBT; job += NW) {
-        const bool isO = job >= DB;
-        const int ct = isO ? job - DB : job;
-        Frag<C, Tin> fm;
-        if (isO)
-          fm.load_kmajor(Zs + ct * 16, LDV);
-        else
-          fm.load_kmajor(Ys + ct * 16, LDK);
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          mma(acc, fp[tb], fm);
-          if (isO) {
-            acc_store(acc, wb.op + uoff + (size_t)(tb * VBT + ct) * 256);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              Tin* qe = Qs + (tb * 16 + acc_row(i)) * LDK + ct * 16 + acc_col();
-              *qe = from_f32<Tin>(to_f32(*qe) - acc[i]);
-            }
-          }
+      const size_t koff = (size_t)n * C * DK, poff = (size_t)n * C * C;
+      for (int job = wave; job < (kGdn2 ? 3 : 2) * TB; job += NW) {
+        const int tb = job % TB, kind = job / TB;
+        if (kind == 1) {
+          Frag<C, Tin> f;
+          f.load(Pb + tb * 16 * LDC, LDC);
+          f.store_global(wb.pp + poff + (size_t)tb * 16 * C);
+        } else {
+          Frag<DK, Tin> f;
+          f.load((kind == 2 ? Qs : Ys) + tb * 16 * LDK, LDK);
+          f.store_global((kind == 2 ? wb.qh : wb.wk) + koff + (size_t)tb * 16 * DK);
         }
-      }
-    }
-    __syncthreads();
-
-    // ---- Wk and Q' as row-block fragments -------------------------------------
-    {
-      const size_t koff = (size_t)n * C * DK;
-      for (int job = wave; job < 2 * TB; job += NW) {
-        const int tb = job % TB;
-        const bool isQ = job >= TB;
-        Frag<DK, Tin> f;
-        f.load((isQ ? Qs : Ys) + tb * 16 * LDK, LDK);
-        f.store_global((isQ ? wb.qp : wb.wk) + koff + (size_t)tb * 16 * DK);
       }
     }
     __syncthreads();  // the next chunk's operands overwrite the tiles
@@ -694,28 +673,35 @@ struct RawTile<float> {
 template <bool GDN2, int DK, int C, int VT, typename Tin>
 struct ScanRegs {
   using G = ScanCfg<DK, C, VT, Tin>;
-  Frag<DK, Tin> wk, qp;
-  RawTile<Tin> u[G::VB], op[G::VB];
+  Frag<DK, Tin> wk, qh;      // the wave's 16 rows of Wk and of the queries
+  Frag<C, Tin> pr;           // the same rows of the scores P
+  RawTile<Tin> u[G::VB];
   Frag<C, Tin> x[G::DPW];
   float gd[G::DPW];
 
-  // Loads are unconditional (indices of idle waves clamped into range), so
-  // that the compiler can count them and a prefetch is only waited on where
-  // its data is used.
-  __device__ __forceinline__ void load(const WyBufs<Tin>& wb, size_t n, int Dv,
-                                       int vt, int wave) {
+  // Chunk j of (batch, head) bh. Loads are unconditional (indices of idle
+  // waves and rows past the sequence end clamped into range), so that the
+  // compiler can count them and a prefetch is only waited on where its data
+  // is used.
+  __device__ __forceinline__ void load(const WyBufs<Tin>& wb, const Tin* q, int bh,
+                                       int j, int nchunks, int T, int Dv, int vt,
+                                       int wave) {
     constexpr int VB = G::VB;
     const int VBT = Dv / 16;
     const int tb = min(wave, G::TB - 1);
+    const size_t n = (size_t)bh * nchunks + j;
     const size_t koff = n * C * DK + (size_t)tb * 16 * DK;
     wk.load_global(wb.wk + koff);
-    qp.load_global(wb.qp + koff);
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      const size_t uo = n * C * Dv + (size_t)(tb * VBT + vt * VB + vb) * 256;
-      u[vb].load(wb.u + uo);
-      op[vb].load(wb.op + uo);
+    if constexpr (GDN2) {
+      qh.load_global(wb.qh + koff);
+    } else {
+      const int row = min(tb * 16 + (int)(threadIdx.x & 15), min(C, T - j * C) - 1);
+      qh.load_row(q + ((size_t)bh * T + (size_t)j * C + row) * DK);
     }
+    pr.load_global(wb.pp + n * C * C + (size_t)tb * 16 * C);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb)
+      u[vb].load(wb.u + n * C * Dv + (size_t)(tb * VBT + vt * VB + vb) * 256);
 #pragma unroll
     for (int d = 0; d < G::DPW; ++d) {
       const int db = min(wave * G::DPW + d, G::DB - 1);
@@ -748,6 +734,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   const int tid = threadIdx.x, wave = tid >> 6;
   const int v0 = vt * VT;
   Tin* o = (Tin*)p.o;
+  const Tin* q = (const Tin*)p.q;
 
   // Persistent state slice S[v][dk] (v in this tile), fp32, MFMA layout.
   // OSDN stores the state [Dv][Dk]; GDN-2 stores it [Dk][Dv].
@@ -783,31 +770,27 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   // final step, so that every step issues the same loads). Guards that
   // always hold for the tile configuration fold away at compile time.
   constexpr bool kAllRowWaves = TB == G::NW, kAllColWaves = DPW * G::NW == DB;
-  const size_t n0 = (size_t)bh * nchunks;
   auto step = [&](int j, auto tail, R& fetch, const R& cur) {
     constexpr bool TAIL = decltype(tail)::value;
     const size_t t0 = (size_t)bh * T + (size_t)j * C;
     const int valid = min(C, T - j * C);
-    fetch.load(wb, n0 + min(j + 1, nchunks - 1), Dv, vt, wave);
-    // ---- W = U - Wk S0^T (to LDS, transposed), O = O' + Q' S0^T -----------
+    fetch.load(wb, q, bh, min(j + 1, nchunks - 1), nchunks, T, Dv, vt, wave);
+    // ---- W = U - Wk S0^T (to LDS, transposed) and Q S0^T ------------------
     // A lane's four W values (tokens 4g..4g+3 of one column) are contiguous
-    // in W^T; the wave's 16 output rows are staged in LDS and stored as one
-    // 16-byte access per lane.
+    // in W^T.
+    f32x4 oacc[VB];
     if (kAllRowWaves || wave < TB) {
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         Frag<DK, Tin> fs;
         fs.load(Ss + vb * 16 * LDK, LDK);
-        f32x4 wa = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+        f32x4 wa = {0.f, 0.f, 0.f, 0.f};
+        oacc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
         mma(wa, cur.wk, fs);
-        mma(oa, cur.qp, fs);
+        mma(oacc[vb], cur.qh, fs);
         Tin w4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w4[i] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
-          Os[(wave * 16 + acc_row(i)) * LDO + vb * 16 + acc_col()] =
-              from_f32<Tin>(p.scale * (cur.op[vb][i] + oa[i]));
-        }
+        for (int i = 0; i < 4; ++i) w4[i] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
         typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
         if constexpr (sizeof(Tin) == 2)
           *reinterpret_cast<u16x4*>(Wt + (vb * 16 + acc_col()) * LDW + wave * 16 + acc_row(0)) =
@@ -816,26 +799,37 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
           *reinterpret_cast<float4*>(Wt + (vb * 16 + acc_col()) * LDW + wave * 16 + acc_row(0)) =
               *reinterpret_cast<const float4*>(w4);
       }
-      // the wave's output rows (written by this wave only)
-      wave_lds_sync();
-      constexpr int VPL = 16 / (int)sizeof(Tin);           // elements per lane access
-      constexpr int LPR = VT / VPL;                        // lanes per row
-      constexpr int RPI = 64 / LPR;                        // rows per access
-#pragma unroll
-      for (int r0 = 0; r0 < 16; r0 += RPI) {
-        const int rr = wave * 16 + r0 + (threadIdx.x & 63) / LPR;
-        const int cc = ((threadIdx.x & 63) % LPR) * VPL;
-        if (r0 + (threadIdx.x & 63) / LPR < 16 && (!TAIL || rr < valid))
-          *reinterpret_cast<uint4*>(o + (t0 + rr) * Dv + v0 + cc) =
-              *reinterpret_cast<const uint4*>(Os + rr * LDO + cc);
-      }
     }
     __syncthreads();
-    // ---- S = S diag(g) + W^T X' -----------------------------------------------
+    // ---- O = scale (Q S0^T + P W); S = S diag(g) + W^T X' -------------------
     {
       Frag<C, Tin> fw[VB];
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) fw[vb].load(Wt + vb * 16 * LDW, LDW);
+      if (kAllRowWaves || wave < TB) {
+        // the wave's 16 output rows go through LDS (rows of this wave only)
+        // and out as one 16-byte store per lane
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+          mma(oacc[vb], cur.pr, fw[vb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Os[(wave * 16 + acc_row(i)) * LDO + vb * 16 + acc_col()] =
+                from_f32<Tin>(p.scale * oacc[vb][i]);
+        }
+        wave_lds_sync();
+        constexpr int VPL = 16 / (int)sizeof(Tin);           // elements per lane access
+        constexpr int LPR = VT / VPL;                        // lanes per row
+        constexpr int RPI = 64 / LPR;                        // rows per access
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += RPI) {
+          const int rr = wave * 16 + r0 + (threadIdx.x & 63) / LPR;
+          const int cc = ((threadIdx.x & 63) % LPR) * VPL;
+          if (r0 + (threadIdx.x & 63) / LPR < 16 && (!TAIL || rr < valid))
+            *reinterpret_cast<uint4*>(o + (t0 + rr) * Dv + v0 + cc) =
+                *reinterpret_cast<const uint4*>(Os + rr * LDO + cc);
+        }
+      }
 #pragma unroll
       for (int d = 0; d < DPW; ++d) {
         const int db = wave * DPW + d;
@@ -861,7 +855,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   // Two register sets in turn (even steps fetch into rb and use ra, odd
   // steps the reverse), unrolled so that each set is a fixed object.
   R ra, rb;
-  if (nchunks > 0) ra.load(wb, n0, Dv, vt, wave);
+  if (nchunks > 0) ra.load(wb, q, bh, 0, nchunks, T, Dv, vt, wave);
   using Full = std::false_type;
   using Tail = std::true_type;
   const int nfull = T / C;  // chunks with C valid rows
@@ -920,7 +914,7 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
     const int BH = a.B * a.H, nch = (a.T + C - 1) / C;
     if (BH == 0) return 0;
-    const WyBufs<Tin> wb = wy_bufs<Tin>(a.ws, BH, nch, C, DK, DV);
+    const WyBufs<Tin> wb = wy_bufs<Tin>(a.ws, BH, nch, C, DK, DV, kGdn2);
     if (nch > 0) {
       // persistent grid: a few workgroups per compute unit at most
       const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<DK, DV, C, Tin>());

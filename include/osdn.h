@@ -151,8 +151,8 @@ int osdn_chunk_forward(int B, int H, int T, int Dk, int Dv, int chunk,
 /*
  * Device scratch, in bytes, that osdn_chunk_forward needs (0 if the sizes
  * are invalid or T = 0): per chunk and (batch, head), the chunk's operands
- * that do not depend on the entry state ((3 Dk + 2 Dv) x chunk elements of
- * the storage dtype and Dk fp32 values).
+ * that do not depend on the entry state ((2 Dk + Dv + chunk) x chunk
+ * elements of the storage dtype).
  */
 size_t osdn_chunk_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                   int chunk, int dtype);
@@ -190,8 +190,10 @@ int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  const float* S0, float scale, void* o, float* S_T,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device scratch, in bytes, that gdn2_forward needs (as for
- * osdn_chunk_workspace_bytes). */
+/* Device scratch, in bytes, that gdn2_forward needs (0 if the sizes are
+ * invalid or T = 0): as for osdn_chunk_workspace_bytes plus, per chunk, the
+ * decayed queries (Dk x chunk elements of the storage dtype) and the exit
+ * decays (Dk fp32 values). */
 size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
 
@@ -210,7 +212,8 @@ void osdn_kernel_timing(int enable);
  * count and mean duration in milliseconds; any output pointer may be NULL.
  * Returns the number of distinct kernels recorded, or -1 if the HIP runtime
  * fails. Kernel names: precond_prep, precond_chain, precond_ktilde (phase
- * 1), wy_prep, wy_scan (phase 2), gdn2_prep, gdn2_scan (GDN-2).
+ * 1), wy_prep, wy_prep_fused (phase 2 forming the preconditioned keys
+ * itself), wy_scan (phase 2), gdn2_prep, gdn2_scan (GDN-2).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

@@ -81,16 +81,19 @@ def test_supported_and_workspace_sizes():
     assert L.osdn_precond_workspace_bytes(4, 16, 4096, 128, 1) == pre(64, 4096, 128)
     assert L.osdn_precond_workspace_bytes(1, 1, 0, 32, 1) == 0
     assert L.osdn_precond_workspace_bytes(1, 1, 8, 40, 1) == 0
-    # chunk engine: per chunk, Wk, Q', X' (Dk columns), U, O' (Dv columns)
-    # in the storage dtype and the exit decay (Dk fp32)
-    def wy(BH, T, Dk, Dv, C, es):
+    # chunk engine: per chunk, Wk, X' (Dk columns), U (Dv columns) and the
+    # scores P (C columns) in the storage dtype; GDN-2 adds its decayed
+    # queries (Dk columns) and the exit decay (Dk fp32)
+    def wy(BH, T, Dk, Dv, C, es, gdn2=False):
         nc = BH * ((T + C - 1) // C)
-        n = nc * C * (3 * Dk + 2 * Dv) * es + nc * Dk * 4
+        n = nc * C * ((3 if gdn2 else 2) * Dk + Dv + C) * es
+        if gdn2:
+            n += nc * Dk * 4
         return (n + 255) // 256 * 256
     assert L.osdn_chunk_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
         wy(64, 4096, 128, 128, 64, 2)
     assert L.gdn2_forward_workspace_bytes(2, 3, 100, 64, 32, 32, 0) == \
-        wy(6, 100, 64, 32, 32, 4)
+        wy(6, 100, 64, 32, 32, 4, gdn2=True)
     # chunk 64: both scratch regions (phase 2 forms K~ from the records);
     # other chunks: K~ plus the larger of the two
     assert L.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) == \
