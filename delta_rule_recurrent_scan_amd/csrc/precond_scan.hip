@@ -359,27 +359,25 @@ struct ChainRegs {
   float4 vr[4];
   float g0, lpt1, lpC;
 
+  // Loads are unconditional, so that the compiler can count them and a
+  // prefetch is only waited on where its data is used: rows past the end of
+  // the sequence read the last valid row instead (their g is zero, so they
+  // add nothing), and V is stored in full (zero above the diagonal blocks).
   __device__ __forceinline__ void load(const Tin* k, const float* rc, size_t t0,
                                        int valid, int t, int q, int c3, int sg) {
+    const int tr = min(t, valid - 1);
 #pragma unroll
-    for (int i = 0; i < NR1; ++i) {
-      kr[i] = uint4{0u, 0u, 0u, 0u};
-      if (t < valid)
-        kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + t) * DK + q * SEG1 +
-                                                i * (16 / sizeof(Tin)));
-    }
+    for (int i = 0; i < NR1; ++i)
+      kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + tr) * DK + q * SEG1 +
+                                              i * (16 / sizeof(Tin)));
 #pragma unroll
     for (int m = 0; m < RS3; ++m) {
-      const int row = sg * RS3 + m;
-      kc[m] = Pair{};
-      if (row < valid) kc[m] = *reinterpret_cast<const Pair*>(k + (t0 + row) * DK + c3);
+      const int row = min(sg * RS3 + m, valid - 1);
+      kc[m] = *reinterpret_cast<const Pair*>(k + (t0 + row) * DK + c3);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vr[i] = float4{0.f, 0.f, 0.f, 0.f};
-      if (q <= (t >> 4))
-        vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + 16 * q + 4 * i);
-    }
+    for (int i = 0; i < 4; ++i)
+      vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + 16 * q + 4 * i);
     g0 = rc[G::R_G + t];
     lpt1 = rc[G::R_LP + t + 1];
     lpC = rc[G::R_LP + C];
@@ -404,13 +402,13 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
   __syncthreads();
 
   auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
-  R cur, nxt;
-  if (nchunks > 0)
-    cur.load(k, recp(0), (size_t)bh * T, min(C, T), t, q, c3, sg);
-  for (int jj = 0; jj < nchunks; ++jj) {
-    if (jj + 1 < nchunks)
-      nxt.load(k, recp(jj + 1), (size_t)bh * T + (size_t)(jj + 1) * C,
-               min(C, T - (jj + 1) * C), t, q, c3, sg);
+  auto fetch_chunk = [&](R& r, int jj) {
+    r.load(k, recp(jj), (size_t)bh * T + (size_t)jj * C, min(C, T - jj * C), t, q, c3, sg);
+  };
+  // One chunk: `cur` holds chunk jj (fetched two chunks before); chunk jj + 2
+  // is fetched into `fetch` at the start (the last chunk again near the end).
+  auto step = [&](int jj, R& fetch, const R& cur) {
+    fetch_chunk(fetch, min(jj + 2, nchunks - 1));
     float* rc = recp(jj);
     if (tid < DK) dent[((size_t)bh * nchunks + jj) * DK + tid] = dv[tid];
     // x_t = <d, a_t>
@@ -461,8 +459,22 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
       }
     }
     __syncthreads();
-    cur = nxt;
+  };
+  // Three register sets in turn (chunk jj uses set jj % 3), unrolled so that
+  // each set is a fixed object.
+  R ra, rb, rc3;
+  if (nchunks > 0) {
+    fetch_chunk(ra, 0);
+    fetch_chunk(rb, min(1, nchunks - 1));
   }
+  int jj = 0;
+  for (; jj + 2 < nchunks; jj += 3) {
+    step(jj, rc3, ra);
+    step(jj + 1, ra, rb);
+    step(jj + 2, rb, rc3);
+  }
+  if (jj < nchunks) step(jj++, rc3, ra);
+  if (jj < nchunks) step(jj++, ra, rb);
   if (dT && tid < DK) dT[(size_t)bh * DK + tid] = dv[tid];
 }
 
