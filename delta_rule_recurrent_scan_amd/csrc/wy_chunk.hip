@@ -132,6 +132,12 @@ struct PrepCfg {
   static constexpr int TPT = C / TPC > 0 ? C / TPC : 1;
 };
 
+// v, or zeros when !keep (per component, so that the register arrays it reads
+// are not forced into memory).
+__device__ __forceinline__ uint4 keep_or_zero(const uint4& v, bool keep) {
+  return uint4{keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u};
+}
+
 // Raw operands of one chunk, fetched into registers while the previous chunk
 // computes (padding rows are zero).
 template <class V, int DK, int DV, int C, typename Tin>
@@ -148,58 +154,52 @@ struct PrepRegs {
   static constexpr int NLA = (C * DK / 4 + G::NT - 1) / G::NT;
   uint4 la4[kGdn2 ? NLA : 1];      // GDN-2: log alpha, 4 channels per load
   float plp, pg, pd;               // fused OSDN: record entries, entry d
+  int vrows;                       // valid rows of the fetched chunk
 
+  // Loads are unconditional (rows past the sequence end read the last valid
+  // row and are zeroed when staged), so that the compiler can count them and
+  // the fetch is only waited on where the staging uses it.
   __device__ __forceinline__ void load(const ChunkArgs& p, int n, int nchunks) {
     const int bh = n / nchunks, j = n - bh * nchunks;
     const int T = p.T, Dv = p.Dv, tid = threadIdx.x;
     const int valid = min(C, T - j * C);
+    vrows = valid;
     const size_t t0 = (size_t)bh * T + (size_t)j * C;
     const Tin* xs = kGdn2 ? (const Tin*)p.b : (const Tin*)p.ktilde;
-    const uint4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < NLK; ++i) {
-      const int e = tid + i * G::NT;
-      const int rr = e / (DK / VEC), cc = (e % (DK / VEC)) * VEC;
-      k[i] = z; q[i] = z; bk[i] = 0.f;
-      if constexpr (!kFused) x[i] = z;
-      if (e < NKB && rr < valid) {
-        const size_t gi = (t0 + rr) * DK + cc;
-        k[i] = *reinterpret_cast<const uint4*>((const Tin*)p.k + gi);
-        q[i] = *reinterpret_cast<const uint4*>((const Tin*)p.q + gi);
-        if constexpr (!kFused) x[i] = *reinterpret_cast<const uint4*>(xs + gi);
-        if constexpr (!kGdn2) bk[i] = p.beta[t0 + rr];
-      }
+      const int e = min(tid + i * G::NT, NKB - 1);
+      const int rr = min(e / (DK / VEC), valid - 1), cc = (e % (DK / VEC)) * VEC;
+      const size_t gi = (t0 + rr) * DK + cc;
+      k[i] = *reinterpret_cast<const uint4*>((const Tin*)p.k + gi);
+      q[i] = *reinterpret_cast<const uint4*>((const Tin*)p.q + gi);
+      if constexpr (!kFused) x[i] = *reinterpret_cast<const uint4*>(xs + gi);
+      if constexpr (!kGdn2) bk[i] = p.beta[t0 + rr];
     }
     if constexpr (kFused) {
       // the phase-1 chunk of this engine chunk has the same index
       const float* rc = p.prec + (size_t)n * kRecStride;
-      plp = tid <= C ? rc[kRecLp + tid] : 0.f;
-      pg = tid < C ? rc[kRecG + tid] : 0.f;
-      pd = tid < DK ? p.pdent[(size_t)n * DK + tid] : 0.f;
+      plp = rc[kRecLp + min(tid, C)];
+      pg = rc[kRecG + min(tid, C - 1)];
+      pd = p.pdent[(size_t)n * DK + min(tid, DK - 1)];
     }
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
-      const int e = tid + i * G::NT;
-      const int rr = e / (DV / VEC), cc = (e % (DV / VEC)) * VEC;
-      v[i] = z; bv[i] = 0.f;
-      if constexpr (kGdn2) w[i] = z;
-      if (e < NVB && rr < valid) {
-        const size_t gi = (t0 + rr) * Dv + cc;
-        v[i] = *reinterpret_cast<const uint4*>((const Tin*)p.v + gi);
-        if constexpr (kGdn2)
-          w[i] = *reinterpret_cast<const uint4*>((const Tin*)p.w + gi);
-        else
-          bv[i] = p.beta[t0 + rr];
-      }
+      const int e = min(tid + i * G::NT, NVB - 1);
+      const int rr = min(e / (DV / VEC), valid - 1), cc = (e % (DV / VEC)) * VEC;
+      const size_t gi = (t0 + rr) * Dv + cc;
+      v[i] = *reinterpret_cast<const uint4*>((const Tin*)p.v + gi);
+      if constexpr (kGdn2)
+        w[i] = *reinterpret_cast<const uint4*>((const Tin*)p.w + gi);
+      else
+        bv[i] = p.beta[t0 + rr];
     }
     if constexpr (kGdn2) {
 #pragma unroll
       for (int i = 0; i < NLA; ++i) {
-        const int e = tid + i * G::NT;
-        const int rr = e / (DK / 4), cc = (e % (DK / 4)) * 4;
-        la4[i] = z;
-        if (e < C * DK / 4 && rr < valid)
-          la4[i] = *reinterpret_cast<const uint4*>(p.log_alpha + (t0 + rr) * DK + cc);
+        const int e = min(tid + i * G::NT, C * DK / 4 - 1);
+        const int rr = min(e / (DK / 4), valid - 1), cc = (e % (DK / 4)) * 4;
+        la4[i] = *reinterpret_cast<const uint4*>(p.log_alpha + (t0 + rr) * DK + cc);
       }
     }
   }
@@ -215,18 +215,20 @@ struct PrepRegs {
       const int e = tid + i * G::NT;
       if (e < NKB) {
         const int rr = e / (DK / VEC), cc = (e % (DK / VEC)) * VEC;
-        *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = q[i];
+        const bool live = rr < vrows;
+        const uint4 kk = keep_or_zero(k[i], live);
+        *reinterpret_cast<uint4*>(Qs + rr * G::LDK + cc) = keep_or_zero(q[i], live);
         if constexpr (kGdn2) {
-          *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = k[i];
-          *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = x[i];
+          *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = kk;
+          *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = keep_or_zero(x[i], live);
         } else {
-          const Tin* kv = reinterpret_cast<const Tin*>(&k[i]);
+          const Tin* kv = reinterpret_cast<const Tin*>(&kk);
           Tin y[VEC];
 #pragma unroll
           for (int u = 0; u < VEC; ++u) y[u] = from_f32<Tin>(bk[i] * to_f32(kv[u]));
           *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(y);
           if constexpr (kFused) {
-            *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = k[i];
+            *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = kk;
             Tin a[VEC];
 #pragma unroll
             for (int u = 0; u < VEC; ++u) {
@@ -236,7 +238,7 @@ struct PrepRegs {
             Tin* As = reinterpret_cast<Tin*>(smem + G::oAs);
             *reinterpret_cast<uint4*>(As + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(a);
           } else {
-            *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = x[i];
+            *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = keep_or_zero(x[i], live);
           }
         }
       }
@@ -248,7 +250,7 @@ struct PrepRegs {
         const int e = tid + i * G::NT;
         if (e < C * DK / 4) {
           const int rr = e / (DK / 4), cc = (e % (DK / 4)) * 4;
-          *reinterpret_cast<uint4*>(La + rr * G::LDA + cc) = la4[i];
+          *reinterpret_cast<uint4*>(La + rr * G::LDA + cc) = keep_or_zero(la4[i], rr < vrows);
         }
       }
     }
@@ -265,7 +267,8 @@ struct PrepRegs {
       const int e = tid + i * G::NT;
       if (e < NVB) {
         const int rr = e / (DV / VEC), cc = (e % (DV / VEC)) * VEC;
-        const Tin* vv = reinterpret_cast<const Tin*>(&v[i]);
+        const uint4 vz = keep_or_zero(v[i], rr < vrows);
+        const Tin* vv = reinterpret_cast<const Tin*>(&vz);
         Tin zz[VEC];
         if constexpr (kGdn2) {
           const Tin* ww = reinterpret_cast<const Tin*>(&w[i]);
@@ -321,6 +324,8 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   if ((int)blockIdx.x < total) regs.load(p, blockIdx.x, nchunks);
   for (int n = blockIdx.x; n < total; n += gridDim.x) {
     regs.store(Ys, Xs, Qs, Zs, smem);
+    // the next chunk's raw operands (the last chunk again at the end)
+    regs.load(p, min(n + (int)gridDim.x, total - 1), nchunks);
     if constexpr (kGdn2) {
       // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
       // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
@@ -499,8 +504,13 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         }
       }
       // X' = X diag(g) as k-major fragments, one channel block per job
+      // (loops that store have a static trip count, so that the compiler can
+      // count the stores and the next chunk's fetch is not waited on early)
       const size_t xoff = (size_t)n * C * DK;
-      for (int db = wave; db < DB; db += NW) {
+#pragma unroll
+      for (int it = 0; it < (DB + NW - 1) / NW; ++it) {
+        const int db = wave + it * NW;
+        if (db >= DB) break;
         Frag<C, Tin> fx;
         fx.load_kmajor(Xs + db * 16, LDK);
         if constexpr (kGdn2) {
@@ -527,9 +537,6 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
     __syncthreads();
 
-    // The next chunk's raw operands are fetched from here on (issuing them
-    // earlier makes the compiler wait for them inside the job loops above).
-    if (n + (int)gridDim.x < total) regs.load(p, n + gridDim.x, nchunks);
 
     // ---- recursive doubling, T21 = -T22 (A21 T11) ----------------------------
     // One job = one 16-wide column of T21 in one pair: that column of
@@ -584,7 +591,10 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       Frag<C, Tin> ft[TB];
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) ft[tb].load(Tb + tb * 16 * LDC, LDC);
-      for (int job = wave; job < DB + VBT; job += NW) {
+#pragma unroll
+      for (int it = 0; it < (DB + VBT + NW - 1) / NW; ++it) {
+        const int job = wave + it * NW;
+        if (job >= DB + VBT) break;
         const bool isU = job >= DB;
         const int ct = isU ? job - DB : job;
         Tin* M = isU ? Zs : Ys;
@@ -611,7 +621,11 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     // ---- Wk, P (and GDN-2's Q^) as row-block fragments ----------------------
     {
       const size_t koff = (size_t)n * C * DK, poff = (size_t)n * C * C;
-      for (int job = wave; job < (kGdn2 ? 3 : 2) * TB; job += NW) {
+      constexpr int NJ = (kGdn2 ? 3 : 2) * TB;
+#pragma unroll
+      for (int it = 0; it < (NJ + NW - 1) / NW; ++it) {
+        const int job = wave + it * NW;
+        if (job >= NJ) break;
         const int tb = job % TB, kind = job / TB;
         if (kind == 1) {
           Frag<C, Tin> f;
