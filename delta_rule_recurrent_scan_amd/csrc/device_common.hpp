@@ -220,6 +220,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// v, or zeros when !keep. Selected per component: a select of the whole
+// struct becomes a select of addresses, which forces the register arrays it
+// reads into scratch memory.
+__device__ __forceinline__ uint4 keep_or_zero(const uint4& v, bool keep) {
+  return uint4{keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u};
+}
+
 // Row (within a 16x16 output tile) of element i held by this lane.
 __device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }

@@ -132,12 +132,6 @@ struct PrepCfg {
   static constexpr int TPT = C / TPC > 0 ? C / TPC : 1;
 };
 
-// v, or zeros when !keep (per component, so that the register arrays it reads
-// are not forced into memory).
-__device__ __forceinline__ uint4 keep_or_zero(const uint4& v, bool keep) {
-  return uint4{keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u};
-}
-
 // Raw operands of one chunk, fetched into registers while the previous chunk
 // computes (padding rows are zero).
 template <class V, int DK, int DV, int C, typename Tin>
