@@ -314,12 +314,22 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
   }
 
+  // Chunks are taken position-major, from the last position of every
+  // (batch, head) down to the first: the scan that follows walks the chunks
+  // from the first position up, so its first reads find the most recently
+  // written operands still in the memory-side cache.
+  const int BHn = total / nchunks;
+  auto chunk_of = [&](int i) {
+    const int jr = i / BHn, bh = i - jr * BHn;
+    return bh * nchunks + (nchunks - 1 - jr);
+  };
   PrepRegs<V, DK, DV, C, Tin> regs;
-  if ((int)blockIdx.x < total) regs.load(p, blockIdx.x, nchunks);
-  for (int n = blockIdx.x; n < total; n += gridDim.x) {
+  if ((int)blockIdx.x < total) regs.load(p, chunk_of(blockIdx.x), nchunks);
+  for (int pos = blockIdx.x; pos < total; pos += gridDim.x) {
+    const int n = chunk_of(pos);
     regs.store(Ys, Xs, Qs, Zs, smem);
     // the next chunk's raw operands (the last chunk again at the end)
-    regs.load(p, min(n + (int)gridDim.x, total - 1), nchunks);
+    regs.load(p, chunk_of(min(pos + (int)gridDim.x, total - 1)), nchunks);
     if constexpr (kGdn2) {
       // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
       // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
@@ -834,8 +844,10 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
           const int rr = wave * 16 + r0 + (threadIdx.x & 63) / LPR;
           const int cc = ((threadIdx.x & 63) % LPR) * VPL;
           if (r0 + (threadIdx.x & 63) / LPR < 16 && (!TAIL || rr < valid))
-            *reinterpret_cast<uint4*>(o + (t0 + rr) * Dv + v0 + cc) =
-                *reinterpret_cast<const uint4*>(Os + rr * LDO + cc);
+            // non-temporal: the output is not read again here, and it
+            // should not push the operands of later chunks out of the caches
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Os + rr * LDO + cc),
+                                        reinterpret_cast<u32x4*>(o + (t0 + rr) * Dv + v0 + cc));
         }
       }
 #pragma unroll
