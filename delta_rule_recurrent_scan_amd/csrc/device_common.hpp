@@ -122,9 +122,52 @@ struct Frag<KEXT, __bf16> {
       t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
           (lds_bf16x4*)(p + (32 * N32 + 4 * g) * ld));
   }
+  // The same fragments in the permuted k order that accumulator tiles give
+  // directly: in 32-wide step i, lane group g holds k = 32i + 4g + {0..3}
+  // and 32i + 16 + 4g + {0..3} (the rows an accumulator lane holds in two
+  // adjacent 16x16 tiles). Any k order serves a contraction as long as both
+  // operands use it. Row-major source (row lane % 16, k along the row):
+  __device__ __forceinline__ void load_perm(const __bf16* base, int ld) {
+    const int lane = threadIdx.x & 63;
+    const __bf16* p = base + (lane & 15) * ld + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < N32; ++i) {
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p + 32 * i);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 32 * i + 16);
+      v[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if constexpr (R16) t = *reinterpret_cast<const bf16x4*>(p + 32 * N32);
+  }
+  // k-major source (as load_kmajor), permuted k order.
+  __device__ __forceinline__ void load_kmajor_perm(const __bf16* base, int ld) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, s = lane & 15;
+    const __bf16* p = base + (s >> 2) * ld + 4 * (s & 3) + 4 * g * ld;
+#pragma unroll
+    for (int i = 0; i < N32; ++i) {
+      const __bf16* q = p + 32 * i * ld;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)q);
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(q + 16 * ld));
+      v[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if constexpr (R16)
+      t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 32 * N32 * ld));
+  }
   // Fragment-major global storage (ELEMS elements): slot s of lane l at
   // [s][l], so that a wave moves each slot as one contiguous block.
   static constexpr int ELEMS = 16 * KEXT;
+  // Accumulator tile b (16 k values) of a permuted-order fragment, stored
+  // in place: tiles 2i and 2i + 1 fill the low and high halves of step i.
+  __device__ __forceinline__ static void store_acc_tile(__bf16* base, int b, const f32x4& a) {
+    bf16x4 h;
+    h[0] = (__bf16)a[0]; h[1] = (__bf16)a[1]; h[2] = (__bf16)a[2]; h[3] = (__bf16)a[3];
+    const int lane = threadIdx.x & 63;
+    __bf16* d = (b >> 1) < N32 ? base + ((b >> 1) * 64 + lane) * 8 + 4 * (b & 1)
+                               : base + N32 * 512 + lane * 4;
+    *reinterpret_cast<bf16x4*>(d) = h;
+  }
   __device__ __forceinline__ void store_global(__bf16* base) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -162,7 +205,31 @@ struct Frag<KEXT, float> {
 #pragma unroll
     for (int i = 0; i < KEXT / 4; ++i) v[i] = p[4 * i * ld];
   }
+  // Permuted k order (see the bf16 fragment): step 4b + i, lane group g
+  // holds k = 16b + 4g + i, i.e. accumulator value i of tile b.
+  __device__ __forceinline__ void load_perm(const float* base, int ld) {
+    const int lane = threadIdx.x & 63;
+    const float* p = base + (lane & 15) * ld + 4 * (lane >> 4);
+#pragma unroll
+    for (int b = 0; b < KEXT / 16; ++b) {
+      const float4 x = *reinterpret_cast<const float4*>(p + 16 * b);
+      v[4 * b] = x.x; v[4 * b + 1] = x.y; v[4 * b + 2] = x.z; v[4 * b + 3] = x.w;
+    }
+  }
+  __device__ __forceinline__ void load_kmajor_perm(const float* base, int ld) {
+    const int lane = threadIdx.x & 63;
+    const float* p = base + 4 * (lane >> 4) * ld + (lane & 15);
+#pragma unroll
+    for (int b = 0; b < KEXT / 16; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * b + i] = p[(16 * b + i) * ld];
+  }
   static constexpr int ELEMS = 16 * KEXT;
+  __device__ __forceinline__ static void store_acc_tile(float* base, int b, const f32x4& a) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) base[(4 * b + i) * 64 + lane] = a[i];
+  }
   __device__ __forceinline__ void store_global(float* base) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll

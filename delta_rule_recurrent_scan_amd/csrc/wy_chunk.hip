@@ -54,9 +54,11 @@ struct Gdn2Variant {};
 struct OsdnFusedVariant {};
 
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
-// storage dtype: Wk and the scores P as 16-row A fragments (row block tb at
-// tb*16*Dk, resp. tb*16*C), X' as k-major B fragments (channel block db at
-// db*16*C), U as accumulator tiles ((tb, vb) at (tb*Dv/16 + vb)*256). GDN-2
+// storage dtype: Wk as 16-row A fragments (row block tb at tb*16*Dk); the
+// scores P as 16-row A fragments (row block tb at tb*16*C) and X' as k-major
+// B fragments (channel block db at db*16*C), both over the tokens in the
+// permuted order of Frag::load_perm, which P's accumulator tiles give
+// directly; U as accumulator tiles ((tb, vb) at (tb*Dv/16 + vb)*256). GDN-2
 // adds the decayed queries Q^ (like Wk) and the exit decays g (fp32, Dk per
 // chunk); OSDN's scan reads the queries themselves.
 template <typename Tin>
@@ -107,8 +109,7 @@ struct PrepCfg {
   static constexpr size_t oZ = oQ + (size_t)C * LDK * E;
   static constexpr size_t oAb = oZ + (size_t)C * LDV * E;
   static constexpr size_t oTb = oAb + (size_t)C * LDC * E;
-  static constexpr size_t oPb = oTb + (size_t)C * LDC * E;
-  static constexpr size_t oA = oPb + (size_t)C * LDC * E;
+  static constexpr size_t oA = oTb + (size_t)C * LDC * E;
   static constexpr size_t oYs = oA + (size_t)TB * 16 * LDD * 4;
   static constexpr size_t oG = oYs + (size_t)NW * (C / 2) * LDS16 * E;
   // fused OSDN: squares of the keys, gate prefix (C + 4), step sizes, entry
@@ -295,7 +296,6 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);   // diag(rs) Z, then U
   Tin* Ab = reinterpret_cast<Tin*>(smem + G::oAb);
   Tin* Tb = reinterpret_cast<Tin*>(smem + G::oTb);
-  Tin* Pb = reinterpret_cast<Tin*>(smem + G::oPb);
   float* Am = reinterpret_cast<float*>(smem + G::oA);
   Tin* Ysc = reinterpret_cast<Tin*>(smem + G::oYs);
   float* gC = reinterpret_cast<float*>(smem + G::oG);
@@ -304,14 +304,11 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   const int total = p.B * p.H * nchunks;
   const Tin zero = from_f32<Tin>(0.f);
 
-  // Blocks above the diagonal of T and P are zero (never written by the
-  // chunk steps; GDN-2 restores them after its decay pass).
+  // Blocks above the diagonal of T are zero (never written by the chunk
+  // steps; GDN-2 restores them after its decay pass).
   for (int e = tid; e < C * C; e += G::NT) {
     const int rr = e / C, cc = e % C;
-    if ((cc >> 4) > (rr >> 4)) {
-      Tb[rr * LDC + cc] = zero;
-      Pb[rr * LDC + cc] = zero;
-    }
+    if ((cc >> 4) > (rr >> 4)) Tb[rr * LDC + cc] = zero;
   }
 
   // Chunks are taken position-major, from the last position of every
@@ -386,14 +383,11 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       }
       if constexpr (G::kLaInGram) {
         __syncthreads();
-        // the staging overlapped T and P: their blocks above the diagonal
-        // are zero again
+        // the staging overlapped T: its blocks above the diagonal are zero
+        // again
         for (int e = tid; e < C * C; e += G::NT) {
           const int rr = e / C, cc = e % C;
-          if ((cc >> 4) > (rr >> 4)) {
-            Tb[rr * LDC + cc] = zero;
-            Pb[rr * LDC + cc] = zero;
-          }
+          if ((cc >> 4) > (rr >> 4)) Tb[rr * LDC + cc] = zero;
         }
       }
     }
@@ -456,16 +450,24 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         fy.load(Ys + a * 16 * LDK, LDK);
         fq.load(Qs + a * 16 * LDK, LDK);
         fx.load(Xs + b * 16 * LDK, LDK);
+        // A tile (a, b); the scores as their transpose, tile (b, a) of
+        // P^T = X Q^T, whose accumulator lanes hold exactly the scan's
+        // permuted-order fragment of P's row block a, step b (stored
+        // straight to the workspace; the mirrored tile above the diagonal
+        // is stored as zeros)
         f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
         mma(aa, fy, fx);
-        mma(pa, fq, fx);
+        mma(pa, fx, fq);
+        Tin* prow = wb.pp + (size_t)n * C * C;
         if (a > b) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = a * 16 + acc_row(i), cc = b * 16 + acc_col();
             Ab[rr * LDC + cc] = from_f32<Tin>(aa[i]);
-            Pb[rr * LDC + cc] = from_f32<Tin>(pa[i]);
           }
+          Frag<C, Tin>::store_acc_tile(prow + (size_t)a * 16 * C, b, pa);
+          Frag<C, Tin>::store_acc_tile(prow + (size_t)b * 16 * C, a,
+                                       f32x4{0.f, 0.f, 0.f, 0.f});
         } else {
           // diagonal tile: A in fp32, transposed, strictly lower part only
           float4 col;
@@ -475,11 +477,11 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
           col.w = acc_row(3) > acc_col() ? aa[3] : 0.f;
           float* Ad = Am + a * 16 * G::LDD;
           *reinterpret_cast<float4*>(Ad + acc_col() * G::LDD + acc_row(0)) = col;
+          // P^T element (t' = row, t = column) kept where t' <= t
+          f32x4 pm;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = a * 16 + acc_row(i), cc = a * 16 + acc_col();
-            Pb[rr * LDC + cc] = from_f32<Tin>(cc <= rr ? pa[i] : 0.f);
-          }
+          for (int i = 0; i < 4; ++i) pm[i] = acc_row(i) <= acc_col() ? pa[i] : 0.f;
+          Frag<C, Tin>::store_acc_tile(prow + (size_t)a * 16 * C, a, pm);
           // T's diagonal block by forward substitution: lane c < 16 owns
           // column c; pending sums are updated as soon as each entry is final.
           wave_lds_sync();
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         const int db = wave + it * NW;
         if (db >= DB) break;
         Frag<C, Tin> fx;
-        fx.load_kmajor(Xs + db * 16, LDK);
+        fx.load_kmajor_perm(Xs + db * 16, LDK);  // the scan's k order
         if constexpr (kGdn2) {
           const float gd = gC[db * 16 + (lane & 15)];
           if constexpr (sizeof(Tin) == 2) {
@@ -622,24 +624,18 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
     __syncthreads();
 
-    // ---- Wk, P (and GDN-2's Q^) as row-block fragments ----------------------
+    // ---- Wk (and GDN-2's Q^) as row-block fragments -------------------------
     {
-      const size_t koff = (size_t)n * C * DK, poff = (size_t)n * C * C;
-      constexpr int NJ = (kGdn2 ? 3 : 2) * TB;
+      const size_t koff = (size_t)n * C * DK;
+      constexpr int NJ = (kGdn2 ? 2 : 1) * TB;
 #pragma unroll
       for (int it = 0; it < (NJ + NW - 1) / NW; ++it) {
         const int job = wave + it * NW;
         if (job >= NJ) break;
         const int tb = job % TB, kind = job / TB;
-        if (kind == 1) {
-          Frag<C, Tin> f;
-          f.load(Pb + tb * 16 * LDC, LDC);
-          f.store_global(wb.pp + poff + (size_t)tb * 16 * C);
-        } else {
-          Frag<DK, Tin> f;
-          f.load((kind == 2 ? Qs : Ys) + tb * 16 * LDK, LDK);
-          f.store_global((kind == 2 ? wb.qh : wb.wk) + koff + (size_t)tb * 16 * DK);
-        }
+        Frag<DK, Tin> f;
+        f.load((kind == 1 ? Qs : Ys) + tb * 16 * LDK, LDK);
+        f.store_global((kind == 1 ? wb.qh : wb.wk) + koff + (size_t)tb * 16 * DK);
       }
     }
     __syncthreads();  // the next chunk's operands overwrite the tiles
@@ -823,7 +819,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
     {
       Frag<C, Tin> fw[VB];
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) fw[vb].load(Wt + vb * 16 * LDW, LDW);
+      for (int vb = 0; vb < VB; ++vb) fw[vb].load_perm(Wt + vb * 16 * LDW, LDW);
       if (kAllRowWaves || wave < TB) {
         // the wave's 16 output rows go through LDS (rows of this wave only)
         // and out as one 16-byte store per lane
