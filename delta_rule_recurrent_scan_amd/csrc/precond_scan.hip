@@ -341,22 +341,32 @@ struct KeyPair<float> {
   __device__ static float hi(T p) { return p.y; }
 };
 
+// Waves of the chain workgroup: 8 where every section still has whole
+// 16-byte key loads and a supported lane reduction, else 4.
+template <int DK>
+constexpr int chain_waves() { return DK >= 64 ? 8 : 4; }
+
 template <int DK, typename Tin>
 struct ChainRegs {
   using G = P1Cfg<DK, Tin>;
-  static constexpr int C = G::C;
-  // x and g: four threads per token row t = tid/4, quarter q = tid%4 holds
-  // channels [q DK/4, (q+1) DK/4) of the key and the 16-wide block q of V.
-  static constexpr int SEG1 = DK / 4;
+  static constexpr int C = G::C, NW = chain_waves<DK>(), NT = 64 * NW;
+  // x and g: TPR threads per token row t = tid / TPR; part q = tid % TPR
+  // holds channels [q SEG1, (q+1) SEG1) of the key and block q (NV wide) of
+  // the row of V.
+  static constexpr int TPR = NT / C;
+  static constexpr int SEG1 = DK / TPR;
   static constexpr int NR1 = SEG1 * sizeof(Tin) / 16;
-  // d update: wave w owns channels [w DK/4, (w+1) DK/4) as DK/8 pairs; lane l
-  // takes pair l % (DK/8) over the token rows of segment l / (DK/8).
-  static constexpr int NP = DK / 8, NSG = 64 / NP, RS3 = C / NSG;
+  static constexpr int NV = C / TPR;
+  static_assert(NR1 >= 1 && NV % 4 == 0, "whole 16-byte loads");
+  // d update: wave w owns channels [w DK/NW, (w+1) DK/NW) as NP pairs; lane l
+  // takes pair l % NP over the token rows of segment l / NP.
+  static constexpr int NP = DK / (2 * NW), NSG = 64 / NP, RS3 = C / NSG;
+  static_assert(NP == 4 || NP == 8 || NP == 16, "strided lane reduction");
   using Pair = typename KeyPair<Tin>::T;
 
   uint4 kr[NR1];
   Pair kc[RS3];
-  float4 vr[4];
+  float4 vr[NV / 4];
   float g0, lpt1, lpC;
 
   // Loads are unconditional, so that the compiler can count them and a
@@ -376,8 +386,8 @@ struct ChainRegs {
       kc[m] = *reinterpret_cast<const Pair*>(k + (t0 + row) * DK + c3);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + 16 * q + 4 * i);
+    for (int i = 0; i < NV / 4; ++i)
+      vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + NV * q + 4 * i);
     g0 = rc[G::R_G + t];
     lpt1 = rc[G::R_LP + t + 1];
     lpC = rc[G::R_LP + C];
@@ -385,20 +395,20 @@ struct ChainRegs {
 };
 
 template <int DK, typename Tin>
-__global__ __launch_bounds__(256) void precond_chain_kernel(
+__global__ __launch_bounds__(64 * chain_waves<DK>()) void precond_chain_kernel(
     int T, int nchunks, const Tin* __restrict__ k, const float* __restrict__ d0in,
     float* __restrict__ rec, float* __restrict__ dent, float* __restrict__ dT) {
   using G = P1Cfg<DK, Tin>;
   using R = ChainRegs<DK, Tin>;
   using KP = KeyPair<Tin>;
-  constexpr int C = G::C;
+  constexpr int C = G::C, NT = R::NT, TPR = R::TPR;
   __shared__ float dv[DK], xs[C], cgs[C];
   const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t = tid >> 2, q = tid & 3;
+  const int t = tid / TPR, q = tid % TPR;
   const int sg = lane / R::NP;
-  const int c3 = wave * (DK / 4) + 2 * (lane % R::NP);
+  const int c3 = wave * (DK / R::NW) + 2 * (lane % R::NP);
 
-  for (int c = tid; c < DK; c += G::NT) dv[c] = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
+  for (int c = tid; c < DK; c += NT) dv[c] = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
   __syncthreads();
 
   auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
@@ -422,7 +432,7 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
         s0 += x0 * x0 * dq[c];
         s1 += x1 * x1 * dq[c + 1];
       }
-      const float s = group_sum<4>(s0 + s1);
+      const float s = group_sum<TPR>(s0 + s1);
       if (q == 0) xs[t] = s;
     }
     __syncthreads();
@@ -431,8 +441,8 @@ __global__ __launch_bounds__(256) void precond_chain_kernel(
       const float* vv = reinterpret_cast<const float*>(cur.vr);
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s += vv[i] * xs[16 * q + i];
-      s = group_sum<4>(s);
+      for (int i = 0; i < R::NV; ++i) s += vv[i] * xs[R::NV * q + i];
+      s = group_sum<TPR>(s);
       const float g = cur.g0 - s;
       if (q == 0) {
         rc[G::R_G + t] = g;
@@ -591,7 +601,7 @@ static int launch_dk(const PrecondArgs& a, hipStream_t s) {
     if (rc) return rc;
   }
   ktimer_before(s, "precond_chain");
-  hipLaunchKernelGGL((precond_chain_kernel<DK, Tin>), dim3(BH), block, 0, s, a.T,
+  hipLaunchKernelGGL((precond_chain_kernel<DK, Tin>), dim3(BH), dim3(64 * chain_waves<DK>()), 0, s, a.T,
                      nch, (const Tin*)a.k, a.d0, rec, dent, a.dT);
   ktimer_after(s);
   int rc = (int)hipGetLastError();
