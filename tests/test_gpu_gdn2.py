@@ -54,6 +54,10 @@ SMALL = [
     BASE.scaled(B=1, H=2, T=90, Dk=64, Dv=32, chunk=32),
     BASE.scaled(B=1, H=2, T=120, dtype="f32", Dk=32, Dv=32, chunk=16),
     BASE.scaled(B=1, H=2, T=70, dtype="f32", Dk=64, Dv=32, chunk=32),
+    # around one chunk: a single token, exactly one chunk, one token past it
+    BASE.scaled(B=1, H=2, T=1),
+    BASE.scaled(B=1, H=2, T=64),
+    BASE.scaled(B=1, H=2, T=65),
 ]
 
 

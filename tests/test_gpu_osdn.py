@@ -218,6 +218,35 @@ def test_precond_scan_alone_and_decoupling():
     assert np.array_equal(d1, f(dT)) and np.array_equal(d1, d2)
 
 
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_zero_key_rows(chunk):
+    """Tokens whose key is exactly zero (||k||^2 = 0): the gradient step is
+    taken as zero there and the write vanishes, in the chunked phase 1 and
+    in the engine alike (a zero row inside a chunk, at a chunk's first and
+    last position, and a whole zero chunk)."""
+    w = small("osdn-1.3b-apf", B=1, H=2, T=64 * 3 + 20)
+    inp = W.make_inputs(w)
+    k = inp["k"].clone()
+    for t in (5, 64, 127, 130):
+        k[:, :, t] = 0
+    k[:, 1, 128:192] = 0
+    inp["k"] = k
+    got = gpu_forward(inp, chunk=chunk)
+    check(got, oracle(inp), "bf16", "zero keys C=%d" % chunk)
+
+
+@pytest.mark.parametrize("T,chunk,dtype", [(1, 64, "bf16"), (63, 64, "bf16"),
+                                           (64, 64, "bf16"), (65, 64, "bf16"),
+                                           (1, 16, "f32"), (17, 16, "f32")])
+def test_short_sequences(T, chunk, dtype):
+    """Sequences around one chunk: a single token, one token short of a
+    chunk, exactly one chunk, one token past it."""
+    name = "osdn-1.3b-apf" if dtype == "bf16" else "tiny-fp32"
+    w = small(name, B=1, H=2, T=T, chunk=chunk)
+    inp = W.make_inputs(w)
+    check(gpu_forward(inp), oracle(inp), dtype, "T=%d C=%d" % (T, chunk))
+
+
 def test_deterministic():
     w = small("osdn-1.3b-apf", B=1, H=4, T=256)
     inp = W.make_inputs(w)
