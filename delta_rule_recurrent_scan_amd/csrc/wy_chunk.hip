@@ -734,7 +734,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
                 DB = G::DB, DPW = G::DPW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
   Tin* Ss = reinterpret_cast<Tin*>(smem + G::oS);   // state copy [v][dk]
-  Tin* Wt = reinterpret_cast<Tin*>(smem + G::oW);   // W^T [v][t]
+  Tin* Wt = reinterpret_cast<Tin*>(smem + G::oW);   // W^T [v][token]
   Tin* Os = reinterpret_cast<Tin*>(smem + G::oO);   // output rows [t][v]
 
   const int T = p.T, Dv = p.Dv;
@@ -806,10 +806,16 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
 #pragma unroll
         for (int i = 0; i < 4; ++i) w4[i] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
         typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
-        if constexpr (sizeof(Tin) == 2)
-          *reinterpret_cast<u16x4*>(Wt + (vb * 16 + acc_col()) * LDW + wave * 16 + acc_row(0)) =
+        if constexpr (sizeof(Tin) == 2) {
+          // bf16: the four tokens go to their slots of the permuted order
+          // (tile tb fills half tb % 2 of 32-wide step tb / 2), so that the
+          // fragments below are plain 16-byte row reads
+          const int g = (threadIdx.x & 63) >> 4;
+          const int slot = (wave >> 1) < C / 32 ? 32 * (wave >> 1) + 8 * g + 4 * (wave & 1)
+                                                : 32 * (C / 32) + 4 * g;
+          *reinterpret_cast<u16x4*>(Wt + (vb * 16 + acc_col()) * LDW + slot) =
               *reinterpret_cast<const u16x4*>(w4);
-        else
+        } else
           *reinterpret_cast<float4*>(Wt + (vb * 16 + acc_col()) * LDW + wave * 16 + acc_row(0)) =
               *reinterpret_cast<const float4*>(w4);
       }
@@ -819,7 +825,12 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
     {
       Frag<C, Tin> fw[VB];
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb) fw[vb].load_perm(Wt + vb * 16 * LDW, LDW);
+      for (int vb = 0; vb < VB; ++vb) {
+        if constexpr (sizeof(Tin) == 2)
+          fw[vb].load(Wt + vb * 16 * LDW, LDW);       // stored in slot order
+        else
+          fw[vb].load_perm(Wt + vb * 16 * LDW, LDW);
+      }
       if (kAllRowWaves || wave < TB) {
         // the wave's 16 output rows go through LDS (rows of this wave only)
         // and out as one 16-byte store per lane
