@@ -58,7 +58,8 @@ struct OsdnFusedVariant {};
 // scores P as 16-row A fragments (row block tb at tb*16*C) and X' as k-major
 // B fragments (channel block db at db*16*C), both over the tokens in the
 // permuted order of Frag::load_perm, which P's accumulator tiles give
-// directly; U as accumulator tiles ((tb, vb) at (tb*Dv/16 + vb)*256). GDN-2
+// directly; U as accumulator tiles, adjacent value tiles interleaved in
+// pairs (u_tile). GDN-2
 // adds the decayed queries Q^ (like Wk) and the exit decays g (fp32, Dk per
 // chunk); OSDN's scan reads the queries themselves.
 template <typename Tin>
@@ -89,6 +90,52 @@ size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
   const size_t per = n * chunk * (2 * (size_t)Dk + (size_t)Dv + (size_t)chunk) * e;
   return gdn2 ? per + n * chunk * (size_t)Dk * e + n * Dk * 4 : per;
 }
+
+// Accumulator tile in the storage dtype, as fetched (converted at use, so
+// that a prefetch is not waited on when it is issued).
+template <typename Tin>
+struct RawTile;
+// U tiles are stored in pairs of adjacent value tiles, interleaved per lane:
+// lane l's four values of tile (tb, ct) at u_tile(tb, ct) + 8 l, so that a
+// wave fetches both tiles of a pair with one 16-byte access per lane (bf16).
+__device__ __forceinline__ size_t u_tile(int tb, int ct, int VBT) {
+  return (size_t)(tb * (VBT / 2) + (ct >> 1)) * 512 + (ct & 1) * 4;
+}
+template <>
+struct RawTile<__bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ void load(const __bf16* tile) {
+    v = *reinterpret_cast<const bf16x4*>(tile + (threadIdx.x & 63) * 8);
+  }
+  __device__ __forceinline__ static void load_pair(const __bf16* tile, RawTile& a,
+                                                   RawTile& b) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(tile + (threadIdx.x & 63) * 8);
+    a.v = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    b.v = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ static void store(const f32x4& a, __bf16* tile) {
+    bf16x4 h;
+    h[0] = (__bf16)a[0]; h[1] = (__bf16)a[1]; h[2] = (__bf16)a[2]; h[3] = (__bf16)a[3];
+    *reinterpret_cast<bf16x4*>(tile + (threadIdx.x & 63) * 8) = h;
+  }
+  __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
+};
+template <>
+struct RawTile<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* tile) {
+    v = *reinterpret_cast<const f32x4*>(tile + (threadIdx.x & 63) * 8);
+  }
+  __device__ __forceinline__ static void load_pair(const float* tile, RawTile& a,
+                                                   RawTile& b) {
+    a.load(tile);
+    b.load(tile + 4);
+  }
+  __device__ __forceinline__ static void store(const f32x4& a, float* tile) {
+    *reinterpret_cast<f32x4*>(tile + (threadIdx.x & 63) * 8) = a;
+  }
+  __device__ __forceinline__ float operator[](int i) const { return v[i]; }
+};
 
 // ---------------------------------------------------------------------------
 // prep
@@ -618,7 +665,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             M[(tb * 16 + acc_row(i)) * ld + ct * 16 + acc_col()] = from_f32<Tin>(acc[tb][i]);
-          if (isU) acc_store(acc[tb], wb.u + uoff + (size_t)(tb * VBT + ct) * 256);
+          if (isU) RawTile<Tin>::store(acc[tb], wb.u + uoff + u_tile(tb, ct, VBT));
         }
       }
     }
@@ -663,27 +710,6 @@ struct ScanCfg {
   static_assert(TB <= NW, "one row block per wave");
 };
 
-// Accumulator tile in the storage dtype, as fetched (converted at use, so
-// that a prefetch is not waited on when it is issued).
-template <typename Tin>
-struct RawTile;
-template <>
-struct RawTile<__bf16> {
-  bf16x4 v;
-  __device__ __forceinline__ void load(const __bf16* base) {
-    v = *reinterpret_cast<const bf16x4*>(base + (threadIdx.x & 63) * 4);
-  }
-  __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
-};
-template <>
-struct RawTile<float> {
-  f32x4 v;
-  __device__ __forceinline__ void load(const float* base) {
-    v = *reinterpret_cast<const f32x4*>(base + (threadIdx.x & 63) * 4);
-  }
-  __device__ __forceinline__ float operator[](int i) const { return v[i]; }
-};
-
 template <bool GDN2, int DK, int C, int VT, typename Tin>
 struct ScanRegs {
   using G = ScanCfg<DK, C, VT, Tin>;
@@ -713,9 +739,16 @@ struct ScanRegs {
       qh.load_row(q + ((size_t)bh * T + (size_t)j * C + row) * DK);
     }
     pr.load_global(wb.pp + n * C * C + (size_t)tb * 16 * C);
+    const Tin* ub = wb.u + n * C * Dv;
+    if constexpr (VB % 2 == 0) {
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-      u[vb].load(wb.u + n * C * Dv + (size_t)(tb * VBT + vt * VB + vb) * 256);
+      for (int pr2 = 0; pr2 < VB / 2; ++pr2)
+        RawTile<Tin>::load_pair(ub + u_tile(tb, vt * VB + 2 * pr2, VBT), u[2 * pr2],
+                                u[2 * pr2 + 1]);
+    } else {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) u[vb].load(ub + u_tile(tb, vt * VB + vb, VBT));
+    }
 #pragma unroll
     for (int d = 0; d < G::DPW; ++d) {
       const int db = min(wave * G::DPW + d, G::DB - 1);
