@@ -884,10 +884,8 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
           const int rr = wave * 16 + r0 + (threadIdx.x & 63) / LPR;
           const int cc = ((threadIdx.x & 63) % LPR) * VPL;
           if (r0 + (threadIdx.x & 63) / LPR < 16 && (!TAIL || rr < valid))
-            // non-temporal: the output is not read again here, and it
-            // should not push the operands of later chunks out of the caches
-            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Os + rr * LDO + cc),
-                                        reinterpret_cast<u32x4*>(o + (t0 + rr) * Dv + v0 + cc));
+            *reinterpret_cast<u32x4*>(o + (t0 + rr) * Dv + v0 + cc) =
+                *reinterpret_cast<const u32x4*>(Os + rr * LDO + cc);
         }
       }
 #pragma unroll
