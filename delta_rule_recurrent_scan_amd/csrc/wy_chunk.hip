@@ -140,8 +140,10 @@ struct RawTile<float> {
 // ---------------------------------------------------------------------------
 // prep
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int C, typename Tin>
+template <class V, int DK, int DV, int C, typename Tin>
 struct PrepCfg {
+  static constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
+  static constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
   static constexpr int NW = 8, NT = 512;
   static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
   static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD;
@@ -159,22 +161,24 @@ struct PrepCfg {
   static constexpr size_t oA = oTb + (size_t)C * LDC * E;
   static constexpr size_t oYs = oA + (size_t)TB * 16 * LDD * 4;
   static constexpr size_t oG = oYs + (size_t)NW * (C / 2) * LDS16 * E;
-  // fused OSDN: squares of the keys, gate prefix (C + 4), step sizes, entry
-  // d, gate products P_t
+  // fused OSDN only: squares of the keys, gate prefix (C + 4), step sizes,
+  // entry d, gate products P_t
   static constexpr size_t oAs = oG + (size_t)DK * 4;
-  static constexpr size_t oLp = oAs + (size_t)C * LDK * E;
-  static constexpr size_t oGs = oLp + (size_t)(C + 4) * 4;
-  static constexpr size_t oDs = oGs + (size_t)C * 4;
-  static constexpr size_t oPv = oDs + (size_t)DK * 4;
-  static constexpr size_t oEnd = oPv + (size_t)C * 4;
-  // GDN-2: log alpha staged as fp32 rows, over the Gram/inverse buffers
-  // (not in use yet during the decay pass) when they are large enough
+  static constexpr size_t oLp = oAs + (kFused ? (size_t)C * LDK * E : 0);
+  static constexpr size_t oGs = oLp + (kFused ? (size_t)(C + 4) * 4 : 0);
+  static constexpr size_t oDs = oGs + (kFused ? (size_t)C * 4 : 0);
+  static constexpr size_t oPv = oDs + (kFused ? (size_t)DK * 4 : 0);
+  static constexpr size_t oEnd = oPv + (kFused ? (size_t)C * 4 : 0);
+  // GDN-2 only: log alpha staged as fp32 rows, in a region of its own when
+  // that fits, else over the Gram/inverse buffers (not in use yet during the
+  // decay pass), whose zero blocks above the diagonal are then restored
   static constexpr int LDA = DK + 4;
-  static constexpr size_t kLaBytes = (size_t)C * LDA * 4;
-  static constexpr bool kLaInGram = oAb + kLaBytes <= oG;
-  static constexpr size_t oLa = kLaInGram ? oAb : oEnd;
-  static constexpr size_t bytes = oEnd + (kLaInGram ? 0 : kLaBytes);
-  static constexpr bool fits = bytes <= 163840;
+  static constexpr size_t kLaBytes = kGdn2 ? (size_t)C * LDA * 4 : 0;
+  static constexpr bool kLaOwn = oEnd + kLaBytes <= 163840;
+  static constexpr bool kLaInGram = !kLaOwn && oAb + kLaBytes <= oG;
+  static constexpr size_t oLa = kLaOwn ? oEnd : oAb;
+  static constexpr size_t bytes = kLaOwn ? oEnd + kLaBytes : oEnd;
+  static constexpr bool fits = bytes <= 163840 && (kLaOwn || kLaInGram);
   // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
   static constexpr int TPC = NT / DK;
   static constexpr int TPT = C / TPC > 0 ? C / TPC : 1;
@@ -184,7 +188,7 @@ struct PrepCfg {
 // computes (padding rows are zero).
 template <class V, int DK, int DV, int C, typename Tin>
 struct PrepRegs {
-  using G = PrepCfg<DK, DV, C, Tin>;
+  using G = PrepCfg<V, DK, DV, C, Tin>;
   static constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
   static constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
   static constexpr int VEC = G::VEC;
@@ -331,7 +335,7 @@ struct PrepRegs {
 template <class V, int DK, int DV, int C, typename Tin>
 __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
                                                       WyBufs<Tin> wb) {
-  using G = PrepCfg<DK, DV, C, Tin>;
+  using G = PrepCfg<V, DK, DV, C, Tin>;
   constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
   constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDS16 = G::LDS16,
@@ -953,11 +957,11 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
 // Host-side dispatch
 // ---------------------------------------------------------------------------
 // Resident prep workgroups per compute unit (LDS-limited).
-template <int DK, int DV, int C, typename Tin>
+template <class V, int DK, int DV, int C, typename Tin>
 constexpr int kPrepWgPerCu() {
-  return (int)(163840 / PrepCfg<DK, DV, C, Tin>::bytes) < 2
+  return (int)(163840 / PrepCfg<V, DK, DV, C, Tin>::bytes) < 2
              ? 1
-             : (int)(163840 / PrepCfg<DK, DV, C, Tin>::bytes);
+             : (int)(163840 / PrepCfg<V, DK, DV, C, Tin>::bytes);
 }
 
 // Value-tile width of the scan: 32 columns when that already gives one
@@ -966,7 +970,7 @@ static int pick_vt(int BH, int Dv) { return (BH * (Dv / 32) >= 256) ? 32 : 16; }
 
 template <class V, int DK, int DV, int C, typename Tin>
 static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
-  if constexpr (!PrepCfg<DK, DV, C, Tin>::fits) {
+  if constexpr (!PrepCfg<V, DK, DV, C, Tin>::fits) {
     return -1;
   } else {
     constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
@@ -975,7 +979,7 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     const WyBufs<Tin> wb = wy_bufs<Tin>(a.ws, BH, nch, C, DK, DV, kGdn2);
     if (nch > 0) {
       // persistent grid: a few workgroups per compute unit at most
-      const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<DK, DV, C, Tin>());
+      const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<V, DK, DV, C, Tin>());
       ktimer_before(s, kGdn2 ? "gdn2_prep"
                              : std::is_same<V, OsdnFusedVariant>::value ? "wy_prep_fused"
                                                                        : "wy_prep");
@@ -1052,12 +1056,14 @@ int launch_osdn_fused(const ChunkArgs& a, hipStream_t s) {
   return launch_variant<OsdnFusedVariant>(a, s);
 }
 
+// Supported sizes: those where the largest layout (fused OSDN) fits, for
+// every variant alike.
 template <int DK, int DV, typename Tin>
 static bool fits_dv(int chunk) {
   switch (chunk) {
-    case 16: return PrepCfg<DK, DV, 16, Tin>::fits;
-    case 32: return PrepCfg<DK, DV, 32, Tin>::fits;
-    case 64: return PrepCfg<DK, DV, 64, Tin>::fits;
+    case 16: return PrepCfg<OsdnFusedVariant, DK, DV, 16, Tin>::fits;
+    case 32: return PrepCfg<OsdnFusedVariant, DK, DV, 32, Tin>::fits;
+    case 64: return PrepCfg<OsdnFusedVariant, DK, DV, 64, Tin>::fits;
   }
   return false;
 }
