@@ -373,23 +373,27 @@ struct ChainRegs {
   // prefetch is only waited on where its data is used: rows past the end of
   // the sequence read the last valid row instead (their g is zero, so they
   // add nothing), and V is stored in full (zero above the diagonal blocks).
-  __device__ __forceinline__ void load(const Tin* k, const float* rc, size_t t0,
+  // kb: the keys of this (batch, head); r0: the chunk's first row; rc: the
+  // chunk's record. Offsets are 32-bit (a (batch, head) holds under 2^32
+  // elements), which keeps the per-lane address arithmetic short.
+  __device__ __forceinline__ void load(const Tin* kb, const float* rc, int r0,
                                        int valid, int t, int q, int c3, int sg) {
-    const int tr = min(t, valid - 1);
+    const unsigned tr = (unsigned)(r0 + min(t, valid - 1));
 #pragma unroll
     for (int i = 0; i < NR1; ++i)
-      kr[i] = *reinterpret_cast<const uint4*>(k + (t0 + tr) * DK + q * SEG1 +
-                                              i * (16 / sizeof(Tin)));
+      kr[i] = *reinterpret_cast<const uint4*>(
+          kb + (tr * DK + (unsigned)(q * SEG1 + i * (16 / (int)sizeof(Tin)))));
 #pragma unroll
     for (int m = 0; m < RS3; ++m) {
-      const int row = min(sg * RS3 + m, valid - 1);
-      kc[m] = *reinterpret_cast<const Pair*>(k + (t0 + row) * DK + c3);
+      const unsigned row = (unsigned)(r0 + min(sg * RS3 + m, valid - 1));
+      kc[m] = *reinterpret_cast<const Pair*>(kb + (row * DK + (unsigned)c3));
     }
 #pragma unroll
     for (int i = 0; i < NV / 4; ++i)
-      vr[i] = *reinterpret_cast<const float4*>(rc + G::R_V + t * C + NV * q + 4 * i);
-    g0 = rc[G::R_G + t];
-    lpt1 = rc[G::R_LP + t + 1];
+      vr[i] = *reinterpret_cast<const float4*>(
+          rc + (unsigned)(G::R_V + t * C + NV * q + 4 * i));
+    g0 = rc[(unsigned)(G::R_G + t)];
+    lpt1 = rc[(unsigned)(G::R_LP + t + 1)];
     lpC = rc[G::R_LP + C];
   }
 };
@@ -412,8 +416,9 @@ __global__ __launch_bounds__(64 * chain_waves<DK>()) void precond_chain_kernel(
   __syncthreads();
 
   auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
+  const Tin* kb = k + (size_t)bh * T * DK;
   auto fetch_chunk = [&](R& r, int jj) {
-    r.load(k, recp(jj), (size_t)bh * T + (size_t)jj * C, min(C, T - jj * C), t, q, c3, sg);
+    r.load(kb, recp(jj), jj * C, min(C, T - jj * C), t, q, c3, sg);
   };
   // One chunk: `cur` holds chunk jj (fetched two chunks before); chunk jj + 2
   // is fetched into `fetch` at the start (the last chunk again near the end).
