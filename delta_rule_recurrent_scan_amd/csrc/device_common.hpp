@@ -295,6 +295,12 @@ __device__ __forceinline__ uint4 keep_or_zero(const uint4& v, bool keep) {
   return uint4{keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u};
 }
 
+// Index of this thread's wave in the workgroup as a wave-uniform value, so
+// that the compiler keeps indexing derived from it in scalar registers.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Row (within a 16x16 output tile) of element i held by this lane.
 __device__ __forceinline__ int acc_row(int i) { return 4 * ((threadIdx.x & 63) >> 4) + i; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
   float* ev = nv + C;     // eta beta / n
   float* rho = ev + C;    // eta beta^2 / n
   float* hv = rho + C;    // rho P
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
 
   // next chunk's keys (row e / NCB, 16-byte block e % NCB) and, on wave 0,
   // its gates (token = lane); padding tokens read as zero keys, r = 1, beta = 0
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * chain_waves<DK>()) void precond_chain_kernel(
   using KP = KeyPair<Tin>;
   constexpr int C = G::C, NT = R::NT, TPR = R::TPR;
   __shared__ float dv[DK], xs[C], cgs[C];
-  const int bh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int bh = blockIdx.x, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int t = tid / TPR, q = tid % TPR;
   const int sg = lane / R::NP;
   const int c3 = wave * (DK / R::NW) + 2 * (lane % R::NP);
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(256) void precond_ktilde_kernel(
   float* dv = gv + C;
 
   const int bh = blockIdx.x / nchunks, j = blockIdx.x - bh * nchunks;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = wave_id();
   const int valid = min(C, T - j * C);
   const size_t t0 = (size_t)bh * T + (size_t)j * C;
   const float* rc = rec + (size_t)blockIdx.x * G::RS;

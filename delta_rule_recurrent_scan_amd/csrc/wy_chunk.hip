@@ -351,7 +351,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   Tin* Ysc = reinterpret_cast<Tin*>(smem + G::oYs);
   float* gC = reinterpret_cast<float*>(smem + G::oG);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int total = p.B * p.H * nchunks;
   const Tin zero = from_f32<Tin>(0.f);
 
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
   const int bh = lin / nvt, vt = lin - bh * nvt;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = wave_id();
   const int v0 = vt * VT;
   Tin* o = (Tin*)p.o;
   const Tin* q = (const Tin*)p.q;
