@@ -39,6 +39,8 @@ _KERNEL_SOURCES = {
     "wy_scan": ["wy_chunk.hip"],
     "gdn2_prep": ["wy_chunk.hip"],
     "gdn2_scan": ["wy_chunk.hip"],
+    "osdn_decode": ["decode.hip"],
+    "gdn2_decode": ["decode.hip"],
 }
 PRECOND_CHUNK = 64  # phase-1 chunk length (fixed in the library)
 
@@ -239,6 +241,85 @@ def cpu_baseline_gdn2(w, inp, budget_s=12.0):
                       "streams" % (done, w.B * w.H, w.T)}
 
 
+def decode_bytes_per_head(w):
+    """Algorithmic bytes per (batch, head) of one decode call: the fp32 state
+    read and written once, plus the call's tokens (inputs and outputs) and,
+    for OSDN, the preconditioner read and written."""
+    s = 2 if w.dtype == "bf16" else 4
+    state = 2 * w.Dk * w.Dv * 4
+    if w.kind == "osdn":
+        tok = (2 * w.Dk + w.Dv) * s + w.Dv * s + 4 + (4 if w.apf else 0)
+        return state + 2 * w.Dk * 4 + w.T * tok
+    tok = (3 * w.Dk + 2 * w.Dv) * s + 4 * w.Dk + w.Dv * s
+    return state + w.T * tok
+
+
+def bench_decode(args, w, inp, x, dt, dev):
+    """One step = one recurrent decode call (w.T tokens for every (batch,
+    head) stream) with the state updated in place."""
+    import delta_rule_recurrent_scan_amd as osdn
+    S = x["S0"].clone()
+    o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
+    if w.kind == "osdn":
+        d = x["d0"].clone()
+
+        def step():
+            osdn.osdn_decode(x["q"], x["k"], x["v"], x["beta"], S, d, r=x["r"],
+                             eta=x["eta"], out=o)
+    else:
+        def step():
+            osdn.gdn2_decode(x["q"], x["k"], x["v"], x["log_alpha"], x["b"],
+                             x["w"], S, out=o)
+    ms_step, kt = timed_steps(step, args)
+    name = "%s_decode" % w.kind
+    alg = decode_bytes_per_head(w) * w.B * w.H
+    achieved = alg / (kt[name] * 1e-3) / 1e9
+    label = "OSDN" if w.kind == "osdn" else "GDN-2"
+    rec = {
+        "metric": "%s recurrent decode tokens/s + %% HBM roofline, B=%d H=%d "
+                  "d=%d, 1 GPU" % (label, w.B, w.H, w.Dk),
+        "value": w.B * w.T / (ms_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T,
+                   "Dk": w.Dk, "Dv": w.Dv},
+        "roofline": {"bound": "hbm", "kernel": name, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name, w.name),
+                     "alg_bytes": alg, "ms": kt[name]},
+        "kernels_ms": kt,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_decode(w, inp)
+    return rec
+
+
+def cpu_baseline_decode(w, inp, budget_s=12.0):
+    """The fp64 oracle on the same decode call, repeated until the budget is
+    spent (all streams at once, vectorised over (batch, head))."""
+    from oracle import recurrence as R
+    f = W.to_f64
+    if w.kind == "osdn":
+        args = [f(inp[k]) for k in ("q", "k", "v", "beta", "r")]
+        run = lambda: R.osdn_ref(*args, inp["eta"], f(inp["d0"]), f(inp["S0"]))
+    else:
+        args = [f(inp[k]) for k in ("q", "k", "v", "log_alpha", "b", "w", "S0")]
+        run = lambda: R.gdn2_ref(*args)
+    n, t_used = 0, 0.0
+    while t_used < budget_s and n < 50:
+        t0 = time.perf_counter()
+        run()
+        t_used += time.perf_counter() - t0
+        n += 1
+    return {"value": w.B * w.T * n / t_used, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d repetitions of the whole call (all %d streams, T=%d), "
+                      "fp64 NumPy token recurrence vectorised over streams, "
+                      "one thread" % (n, w.B * w.H, w.T)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +367,9 @@ def main():
     x = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
          for k, v in inp.items()}
     dt = W.torch_dtype(w.dtype)
+    if w.state:
+        print(json.dumps(bench_decode(args, w, inp, x, dt, dev)), flush=True)
+        return
     if w.kind == "gdn2":
         print(json.dumps(bench_gdn2(args, w, inp, x, dt, dev)), flush=True)
         return

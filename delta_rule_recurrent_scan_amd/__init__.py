@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
-           "gdn2_forward",
+           "gdn2_forward", "osdn_decode", "gdn2_decode",
            "workspace_bytes", "precond_workspace_bytes", "supported",
            "kernel_timing", "kernel_times",
            "OsdnError", "library_path", "load_library"]
@@ -73,6 +73,10 @@ def load_library():
     L.gdn2_forward.argtypes = ([I] * 7 + [P, P, P, P, P, P, P, F, P, P, P, Z,
                                           P])
     L.gdn2_forward.restype = I
+    L.osdn_decode.argtypes = [I] * 6 + [P, P, P, P, P, F, P, P, F, P, P]
+    L.osdn_decode.restype = I
+    L.gdn2_decode.argtypes = [I] * 6 + [P, P, P, P, P, P, P, F, P, P]
+    L.gdn2_decode.restype = I
     L.osdn_kernel_timing.argtypes = [I]
     L.osdn_kernel_timing.restype = None
     L.osdn_kernel_times.argtypes = [I, P, P, P]
@@ -290,3 +294,57 @@ def gdn2_forward(q, k, v, log_alpha, b, w, S0=None, chunk=64, scale=1.0,
     if rc != 0:
         raise OsdnError(rc, "gdn2_forward")
     return o, S_T
+
+
+def osdn_decode(q, k, v, beta, S, d, r=None, eta=0.1, scale=1.0, out=None):
+    """OSDN recurrent decode on the GPU: advances the T tokens of q, k, v
+    (usually T = 1) through the token recurrence, updating S ([B,H,Dv,Dk]
+    fp32) and d ([B,H,Dk] fp32) IN PLACE; returns o [B,H,T,Dv]."""
+    L = load_library()
+    dev = q.device
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    _check(r, "r", (B, H, T), torch.float32, dev)
+    _check(S, "S", (B, H, Dv, Dk), torch.float32, dev)
+    _check(d, "d", (B, H, Dk), torch.float32, dev)
+    o = torch.empty((B, H, T, Dv), dtype=dt, device=dev) if out is None else out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    rc = L.osdn_decode(B, H, T, Dk, Dv, _DTYPE_CODE[dt], _ptr(q), _ptr(k),
+                       _ptr(v), _ptr(beta), _ptr(r), float(eta), _ptr(S),
+                       _ptr(d), float(scale), _ptr(o), _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_decode")
+    return o
+
+
+def gdn2_decode(q, k, v, log_alpha, b, w, S, scale=1.0, out=None):
+    """Gated DeltaNet-2 recurrent decode on the GPU: T tokens with the state
+    S ([B,H,Dk,Dv] fp32) updated IN PLACE; returns o [B,H,T,Dv]."""
+    L = load_library()
+    dev = q.device
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    for t, n in ((q, "q"), (k, "k"), (b, "b")):
+        _check(t, n, (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(w, "w", (B, H, T, Dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, Dk), torch.float32, dev)
+    _check(S, "S", (B, H, Dk, Dv), torch.float32, dev)
+    o = torch.empty((B, H, T, Dv), dtype=dt, device=dev) if out is None else out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    rc = L.gdn2_decode(B, H, T, Dk, Dv, _DTYPE_CODE[dt], _ptr(q), _ptr(k),
+                       _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S),
+                       float(scale), _ptr(o), _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "gdn2_decode")
+    return o

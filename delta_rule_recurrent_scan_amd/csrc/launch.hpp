@@ -52,6 +52,28 @@ struct ChunkArgs {
   const float* pdent;
 };
 
+// Arguments of the recurrent decode kernels: T tokens through the token
+// recurrence with the state updated in place. OSDN: beta, r, eta, d; state
+// [B,H,Dv,Dk]. GDN-2: log_alpha, b, w; state [B,H,Dk,Dv].
+struct DecodeArgs {
+  int B, H, T, Dk, Dv;
+  int bf16;
+  int gdn2;
+  const void* q;            // [B,H,T,Dk]
+  const void* k;            // [B,H,T,Dk]
+  const void* v;            // [B,H,T,Dv]
+  const float* beta;        // OSDN: [B,H,T]
+  const float* r;           // OSDN: [B,H,T] or null
+  float eta;
+  const float* log_alpha;   // GDN-2: [B,H,T,Dk]
+  const void* b;            // GDN-2: [B,H,T,Dk]
+  const void* w;            // GDN-2: [B,H,T,Dv]
+  float* S;                 // in/out
+  float* d;                 // OSDN: [B,H,Dk] in/out
+  float scale;
+  void* o;                  // [B,H,T,Dv]
+};
+
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
 // (dims, dtype) combination has no kernel instance.
 int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
@@ -61,6 +83,7 @@ size_t precond_workspace_bytes(int B, int H, int T, int Dk, int bf16);
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_osdn_fused(const ChunkArgs& a, hipStream_t s);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
+int launch_decode(const DecodeArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 // Device scratch of the chunk engine: per chunk, the S0-independent operands

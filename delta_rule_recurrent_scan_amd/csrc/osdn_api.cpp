@@ -273,4 +273,53 @@ int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }
 
+int osdn_decode(int B, int H, int T, int Dk, int Dv, int dtype, const void* q,
+                const void* k, const void* v, const float* beta,
+                const float* r, float eta, float* S, float* d, float scale,
+                void* o, void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  const size_t BH = (size_t)B * H;
+  if (BH * T > 0 && (!q || !k || !v || !beta || !S || !d || !o))
+    return OSDN_ERR_NULL_ARG;
+  if (!dim_ok(Dk) || !dim_ok(Dv) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return OSDN_ERR_UNSUPPORTED;
+  if (BH * T == 0) return OSDN_OK;
+  const size_t es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(beta, BH * T * 4),
+                       rng(r, r ? BH * T * 4 : 0)};
+  const Range outs[] = {rng(o, BH * T * Dv * es), rng(S, BH * Dv * Dk * 4),
+                        rng(d, BH * Dk * 4)};
+  if (!aliasing_ok(outs, ins, nullptr, 0)) return OSDN_ERR_ALIASING;
+  osdn::DecodeArgs a{B, H, T, Dk, Dv, dtype == OSDN_BF16, 0, q, k, v, beta, r,
+                     eta, nullptr, nullptr, nullptr, S, d, scale, o};
+  const int rc = osdn::launch_decode(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype, const void* q,
+                const void* k, const void* v, const float* log_alpha,
+                const void* b, const void* w, float* S, float scale, void* o,
+                void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  const size_t BH = (size_t)B * H;
+  if (BH * T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !S || !o))
+    return OSDN_ERR_NULL_ARG;
+  if (!dim_ok(Dk) || !dim_ok(Dv) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return OSDN_ERR_UNSUPPORTED;
+  if (BH * T == 0) return OSDN_OK;
+  const size_t es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(log_alpha, BH * T * Dk * 4),
+                       rng(b, BH * T * Dk * es), rng(w, BH * T * Dv * es)};
+  const Range outs[] = {rng(o, BH * T * Dv * es), rng(S, BH * Dk * Dv * 4)};
+  if (!aliasing_ok(outs, ins, nullptr, 0)) return OSDN_ERR_ALIASING;
+  osdn::DecodeArgs a{B, H, T, Dk, Dv, dtype == OSDN_BF16, 1, q, k, v, nullptr,
+                     nullptr, 0.f, log_alpha, b, w, S, nullptr, scale, o};
+  const int rc = osdn::launch_decode(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
 }  // extern "C"

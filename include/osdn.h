@@ -198,6 +198,44 @@ size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
 
 /*
+ * Recurrent decode ([OSDN-it] section 1: constant-memory recurrent inference;
+ * same token rule as osdn_forward): advances T tokens (typically 1) through
+ * the token recurrence itself, reading the state once and updating it in
+ * place. No workspace; B*H workgroups, each holding one (batch, head) state
+ * in registers.
+ *
+ *   q, k     [B,H,T,Dk]  dtype            (required)
+ *   v        [B,H,T,Dv]  dtype            (required)
+ *   beta     [B,H,T]     fp32             (required)
+ *   r        [B,H,T]     fp32             (NULL: no forgetting gate)
+ *   eta      step size of the preconditioner learner
+ *   S        [B,H,Dv,Dk] fp32 IN/OUT: the state before the tokens on entry,
+ *                        after them on return (required)
+ *   d        [B,H,Dk]    fp32 IN/OUT: the preconditioner, likewise (required)
+ *   scale    readout scale
+ *   o        [B,H,T,Dv]  dtype            (required)
+ * Output o_t and the final S, d equal osdn_forward(..., d0 = d, S0 = S) up to
+ * rounding. T = 0 leaves S and d untouched. S, d and o must not overlap each
+ * other or any input (OSDN_ERR_ALIASING). Dk, Dv in {32, 64, 128}.
+ */
+int osdn_decode(int B, int H, int T, int Dk, int Dv, int dtype,
+                const void* q, const void* k, const void* v,
+                const float* beta, const float* r, float eta,
+                float* S, float* d, float scale, void* o, void* stream);
+
+/*
+ * Gated DeltaNet-2 recurrent decode ([GDN2-it] method part 1, token form):
+ * T tokens of the gdn2_forward rule with the state S ([B,H,Dk,Dv] fp32,
+ * required) updated in place; q, k, v, log_alpha, b, w and o as in
+ * gdn2_forward. T = 0 leaves S untouched. S and o must not overlap each other
+ * or any input. Dk, Dv in {32, 64, 128}; no workspace.
+ */
+int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype,
+                const void* q, const void* k, const void* v,
+                const float* log_alpha, const void* b, const void* w,
+                float* S, float scale, void* o, void* stream);
+
+/*
  * Per-kernel timing for measurement harnesses (not thread-safe). While
  * enabled, every entry point records a HIP event on its stream before and
  * after each kernel it launches (two event records per kernel; events are
@@ -213,7 +251,8 @@ void osdn_kernel_timing(int enable);
  * Returns the number of distinct kernels recorded, or -1 if the HIP runtime
  * fails. Kernel names: precond_prep, precond_chain, precond_ktilde (phase
  * 1), wy_prep, wy_prep_fused (phase 2 forming the preconditioned keys
- * itself), wy_scan (phase 2), gdn2_prep, gdn2_scan (GDN-2).
+ * itself), wy_scan (phase 2), gdn2_prep, gdn2_scan (GDN-2), osdn_decode,
+ * gdn2_decode (recurrent decode).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

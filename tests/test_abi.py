@@ -38,7 +38,8 @@ def test_header_declares_entry_points():
               "osdn_forward_supported", "osdn_precond_scan",
               "osdn_precond_workspace_bytes",
               "osdn_chunk_forward", "gdn2_forward", "gdn2_forward_supported",
-              "osdn_chunk_workspace_bytes", "gdn2_forward_workspace_bytes"):
+              "osdn_chunk_workspace_bytes", "gdn2_forward_workspace_bytes",
+              "osdn_decode", "gdn2_decode"):
         assert n in names
 
 
@@ -201,3 +202,40 @@ def test_gdn2_error_paths():
     assert call(ws=0x30000) == ALIASING          # workspace over v
     assert L.gdn2_forward_supported(128, 128, 64, 1) == 1
     assert L.gdn2_forward_supported(128, 128, 8, 1) == 0
+
+
+@needs_lib
+def test_decode_error_paths():
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    I, F = ctypes.c_int, ctypes.c_float
+    L.osdn_decode.argtypes = [I] * 6 + [P, P, P, P, P, F, P, P, F, P, P]
+    L.gdn2_decode.argtypes = [I] * 6 + [P] * 7 + [F, P, P]
+
+    def dec(B=2, T=1, Dk=32, q=0x10000, beta=0x40000, S=0x200000, d=0x300000,
+            o=0x50000, r=None):
+        return L.osdn_decode(B, 1, T, Dk, 32, 1, q, 0x20000, 0x30000, beta, r,
+                             0.1, S, d, 1.0, o, None)
+    assert dec(q=None) == NULL_ARG
+    assert dec(S=None) == NULL_ARG
+    assert dec(d=None) == NULL_ARG
+    assert dec(T=-1) == BAD_DIMS
+    assert dec(Dk=48) == UNSUPPORTED
+    assert dec(S=0x10000 + 4) == ALIASING        # state over q
+    assert dec(d=0x200000 + 64) == ALIASING      # d inside the state
+    assert dec(o=0x300000) == ALIASING           # o over d
+    assert dec(r=0x200000) == ALIASING           # gate over the state
+    # nothing to do: T = 0 or B = 0 needs no pointer
+    assert dec(T=0, q=None, S=None, d=None, o=None, beta=None) == OK
+    assert dec(B=0, q=None, S=None, d=None, o=None, beta=None) == OK
+
+    def gd(T=1, Dv=32, la=0x60000, S=0x200000, o=0x50000):
+        return L.gdn2_decode(1, 1, T, 32, Dv, 1, 0x10000, 0x20000, 0x30000,
+                             la, 0x70000, 0x80000, S, 1.0, o, None)
+    assert gd(la=None) == NULL_ARG
+    assert gd(S=None) == NULL_ARG
+    assert gd(T=-2) == BAD_DIMS
+    assert gd(Dv=16) == UNSUPPORTED
+    assert gd(S=0x70000) == ALIASING             # state over b
+    assert gd(o=0x200000 + 8) == ALIASING        # o inside the state
+    assert gd(T=0, la=None, S=None, o=None) == OK

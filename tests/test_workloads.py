@@ -24,6 +24,15 @@ def test_shapes_and_dtypes_small(w):
         assert torch.all(x["log_alpha"] < 0)
         assert x["b"].shape == (1, 2, ws.T, w.Dk) and x["b"].dtype == dt
         assert x["w"].shape == (1, 2, ws.T, w.Dv) and x["w"].dtype == dt
+    if w.state:
+        Ssh = (1, 2, w.Dv, w.Dk) if w.kind == "osdn" else (1, 2, w.Dk, w.Dv)
+        assert x["S0"].shape == Ssh and x["S0"].dtype == torch.float32
+        if w.kind == "osdn":
+            d0 = x["d0"].double()
+            assert d0.shape == (1, 2, w.Dk)
+            assert torch.all((d0 >= 0.5) & (d0 <= 1.5))
+    else:
+        assert x["S0"] is None
     n = x["k"].double().norm(dim=-1)
     assert torch.allclose(n, torch.ones_like(n), atol=2e-2)
 

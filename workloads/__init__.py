@@ -17,9 +17,14 @@ Workloads (dims B, H, T, Dk, Dv and chunk C):
    repeat earlier keys; beta = sigmoid(N(1,1)); gate on; eta 0.05.
 5. Gated DeltaNet-2: 4, 16, 4096, 128, 128, C=64; bf16; per-channel decay
    log alpha = -0.1 softplus(N(0,1)); erase/write gates sigmoid(N(0,1)).
+6. OSDN recurrent decode at the 1.3B-layer head shape with a serving batch:
+   128, 16, 1, 128, 128; bf16; gate on; a drawn initial state, S0 =
+   N(0,1)/sqrt(Dk) and d0 = U(0.5, 1.5).
+7. GDN-2 recurrent decode, same shape and gates as 5, S0 = N(0,1)/sqrt(Dk).
 
 Seeds: workload i draws from numpy SeedSequence(i - 1); each tensor comes
-from its own spawned child, in the fixed order q, k, v, beta, r, alpha, b, w.
+from its own spawned child, in the fixed order q, k, v, beta, r, alpha, b, w,
+S0, d0.
 """
 
 from dataclasses import dataclass, replace
@@ -44,6 +49,7 @@ class Workload:
     beta_mu: float = 0.0  # beta = sigmoid(N(beta_mu, 1))
     keys: str = "gauss"  # "gauss" or "pool" (multi-key recall)
     seed: int = 0
+    state: bool = False  # draw an initial state S0 (and d0 for OSDN)
 
     @property
     def tokens(self):
@@ -62,6 +68,10 @@ WORKLOADS = [
     Workload("osdn-recall-8k", "osdn", 2, 16, 8192, 128, 128, 64, "bf16",
              eta=0.05, apf=True, beta_mu=1.0, keys="pool", seed=3),
     Workload("gdn2-1.3b", "gdn2", 4, 16, 4096, 128, 128, 64, "bf16", seed=4),
+    Workload("osdn-decode", "osdn", 128, 16, 1, 128, 128, 64, "bf16",
+             apf=True, seed=5, state=True),
+    Workload("gdn2-decode", "gdn2", 128, 16, 1, 128, 128, 64, "bf16", seed=6,
+             state=True),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}
@@ -120,11 +130,12 @@ def _pool_queries(rng, k_stored):
 def make_inputs(w: Workload):
     """Generate one workload's inputs as CPU torch tensors.
 
-    OSDN: dict(q, k, v, beta, r, eta, d0=None, S0=None, chunk).
-    GDN-2: dict(q, k, v, log_alpha, b, w, S0=None, chunk).
+    OSDN: dict(q, k, v, beta, r, eta, d0, S0, chunk).
+    GDN-2: dict(q, k, v, log_alpha, b, w, S0, chunk).
+    S0 and d0 are None (zeros, ones) unless the workload draws a state.
     """
     ss = np.random.SeedSequence(w.seed)
-    ch = [np.random.default_rng(s) for s in ss.spawn(8)]
+    ch = [np.random.default_rng(s) for s in ss.spawn(10)]
     B, H, T, Dk, Dv = w.B, w.H, w.T, w.Dk, w.Dv
     if w.keys == "pool":
         k = _store(_pool_keys(ch[1], B, H, T, Dk), w.dtype)
@@ -140,6 +151,10 @@ def make_inputs(w: Workload):
         r = (_store(_sigmoid(ch[4].normal(2.0, 0.5, (B, H, T))), "f32")
              if w.apf else None)
         out.update(beta=beta, r=r, eta=w.eta, d0=None)
+        if w.state:
+            out["S0"] = _store(ch[8].standard_normal((B, H, Dv, Dk))
+                               / np.sqrt(Dk), "f32")
+            out["d0"] = _store(ch[9].uniform(0.5, 1.5, (B, H, Dk)), "f32")
     else:
         la = -0.1 * _softplus(ch[5].standard_normal((B, H, T, Dk)))
         out.update(log_alpha=_store(la, "f32"),
@@ -147,6 +162,9 @@ def make_inputs(w: Workload):
                             w.dtype),
                    w=_store(_sigmoid(ch[7].standard_normal((B, H, T, Dv))),
                             w.dtype))
+        if w.state:
+            out["S0"] = _store(ch[8].standard_normal((B, H, Dk, Dv))
+                               / np.sqrt(Dk), "f32")
     return out
 
 
