@@ -19,7 +19,8 @@ two papers):
 Modules:
 
 * ``recurrence``  fp64 NumPy token-by-token recurrences (OSDN, phase 1 alone,
-  GDN-2) and the surrogate h_t, by definition and in closed form.
+  GDN-2), the surrogate h_t, by definition and in closed form, and the
+  residual contraction ratios with their geometric mean q_geo.
 * ``exact``     the same recurrences in exact rational arithmetic
   (``fractions.Fraction``) plus an independent closed-form unrolling of the
   state as a sum of products of transition matrices, for tiny inputs.
@@ -34,6 +35,7 @@ perplexity, q_geo) cannot be reproduced without weights and datasets: those are
 from .recurrence import (  # noqa: F401
     osdn_ref,
     precond_scan_ref,
+    residual_ratio_ref,
     deltanet_ref,
     gdn2_ref,
     h_closed_form,

@@ -162,6 +162,29 @@ def precond_scan_ref(k, beta, r=None, eta=0.1, d0=None):
     return ktil, d, c_all, g_all
 
 
+def residual_ratio_ref(k, beta, r=None, eta=0.1, d0=None):
+    """Per-token residual contraction ratio and its geometric mean.
+
+    [OSDN-it] section 3 (Theorem 5.2) bounds the product over tokens of the
+    ratios f_t(S_t) / f_t(S_{t-1}); for the diagonal update this ratio is
+    rho_t = (1 - beta_t <d_t, k_t*k_t>)^2, whatever S_{t-1} and v_t are.
+    [OSDN-it] section 4.2 reports the geometric mean of these ratios, q_geo;
+    here it is taken per (batch, head) stream over its T tokens,
+    q_geo = (prod_t rho_t)^(1/T) = exp(mean_t log rho_t) (1 when T = 0).
+
+    Depends only on the phase-1 inputs. Returns (rho [B,H,T], q_geo [B,H]).
+    """
+    beta = _f64(beta)
+    _, _, c, _ = precond_scan_ref(k, beta, r, eta, d0)
+    rho = (1.0 - beta * c) ** 2
+    T = rho.shape[-1]
+    if T == 0:
+        return rho, np.ones(rho.shape[:-1])
+    with np.errstate(divide="ignore"):
+        q_geo = np.exp(np.mean(np.log(rho), axis=-1))
+    return rho, q_geo
+
+
 # ---------------------------------------------------------------------------
 # The full OSDN forward (phase 1 and the memory update, token by token)
 # ---------------------------------------------------------------------------

@@ -131,6 +131,30 @@ def pin_per_token_contraction():
                                    rtol=1e-10, atol=1e-14)
 
 
+def pin_residual_ratio_is_loss_ratio():
+    """residual_ratio_ref's rho_t equals the ratio of the regression losses
+    f_t(S_t) / f_t(S_{t-1}) computed from the states of the full recurrence
+    (random values and a random initial state), and q_geo is the T-th root
+    of their product ([OSDN-it] section 3, Theorem 5.2; section 4.2)."""
+    q, k, v, beta, r = _rand_osdn(15, T=40)
+    g = _rng(16)
+    S0 = g.standard_normal((2, 2, 5, 6))
+    d0 = g.uniform(0.5, 1.5, (2, 2, 6))
+    rho, qg = R.residual_ratio_ref(k, beta, r, 0.3, d0)
+    _, _, _, states = R.osdn_ref(q, k, v, beta, r, 0.3, d0, S0,
+                                 return_states=True)
+    ratios = np.stack([R.regression_loss(states[t + 1], k[:, :, t], v[:, :, t])
+                       / R.regression_loss(states[t], k[:, :, t], v[:, :, t])
+                       for t in range(k.shape[2])], axis=-1)
+    np.testing.assert_allclose(rho, ratios, rtol=1e-9)
+    np.testing.assert_allclose(qg, np.prod(ratios, axis=-1) ** (1.0 / 40),
+                               rtol=1e-9)
+    # no forgetting, d0 = 1, eta = 0: plain DeltaNet, rho_t = (1 - beta_t)^2
+    # for unit keys
+    rho0, _ = R.residual_ratio_ref(k, beta, None, 0.0)
+    np.testing.assert_allclose(rho0, (1.0 - beta) ** 2, rtol=1e-12)
+
+
 def pin_exact_unrolled():
     """fp64 oracle vs exact rationals vs the transition-product unrolling."""
     g = _rng(6)
@@ -290,6 +314,7 @@ PINS = [
     pin_repeated_key_dynamics,
     pin_constant_gate_fixed_point,
     pin_per_token_contraction,
+    pin_residual_ratio_is_loss_ratio,
     pin_exact_unrolled,
     pin_deltanet_reduction,
     pin_newton_condition,
