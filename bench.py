@@ -34,6 +34,7 @@ _KERNEL_SOURCES = {
     "precond_prep": ["precond_scan.hip"],
     "precond_chain": ["precond_scan.hip"],
     "precond_ktilde": ["precond_scan.hip"],
+    "precond_rho": ["precond_scan.hip"],
     "wy_prep": ["wy_chunk.hip"],
     "wy_prep_fused": ["wy_chunk.hip"],
     "wy_scan": ["wy_chunk.hip"],
@@ -388,7 +389,7 @@ def main():
         rc = L.osdn_forward(w.B, w.H, w.T, w.Dk, w.Dv, w.chunk, code, P(x["q"]),
                             P(x["k"]), P(x["v"]), P(x["beta"]), P(x["r"]),
                             float(x["eta"]), None, None, 1.0, P(o), P(S_T),
-                            P(d_T), P(ws), ws.numel(), sp)
+                            P(d_T), None, None, P(ws), ws.numel(), sp)
         if rc:
             raise RuntimeError("launch failed: %s" % L.osdn_strerror(rc))
 

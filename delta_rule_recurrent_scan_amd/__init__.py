@@ -55,11 +55,12 @@ def load_library():
     L.osdn_forward_workspace_bytes.argtypes = [I] * 7
     L.osdn_forward_workspace_bytes.restype = Z
     L.osdn_forward.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, F, P, P, P, P,
-                                          Z, P])
+                                          P, P, Z, P])
     L.osdn_forward.restype = I
     L.osdn_precond_workspace_bytes.argtypes = [I] * 5
     L.osdn_precond_workspace_bytes.restype = Z
-    L.osdn_precond_scan.argtypes = [I, I, I, I, I, P, P, P, F, P, P, P, P, Z, P]
+    L.osdn_precond_scan.argtypes = [I, I, I, I, I, P, P, P, F, P, P, P, P, P,
+                                    P, Z, P]
     L.osdn_precond_scan.restype = I
     L.osdn_chunk_workspace_bytes.argtypes = [I] * 7
     L.osdn_chunk_workspace_bytes.restype = Z
@@ -140,8 +141,11 @@ def workspace_bytes(B, H, T, Dk, Dv, chunk, dtype):
 
 
 def osdn_forward(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None, chunk=64,
-                 scale=1.0, out=None, workspace=None):
-    """OSDN forward on the GPU: returns (o, S_T, d_T).
+                 scale=1.0, out=None, workspace=None, diagnostics=False):
+    """OSDN forward on the GPU: returns (o, S_T, d_T), and with
+    ``diagnostics=True`` also (rho [B,H,T], q_geo [B,H]): the per-token
+    residual contraction ratios (1 - beta_t <d_t, k_t^2>)^2 and their
+    geometric mean per stream.
 
     q, k: [B,H,T,Dk]; v: [B,H,T,Dv] (fp32 or bf16, one dtype); beta, r:
     [B,H,T] fp32 (r=None: no forgetting gate); d0: [B,H,Dk] fp32 (None: ones);
@@ -178,13 +182,19 @@ def osdn_forward(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None, chunk=64,
                                           _DTYPE_CODE[dt])
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rho = qg = None
+    if diagnostics:
+        rho = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        qg = torch.empty((B, H), dtype=torch.float32, device=dev)
     rc = L.osdn_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt], _ptr(q),
                         _ptr(k), _ptr(v), _ptr(beta), _ptr(r), float(eta),
                         _ptr(d0), _ptr(S0), float(scale), _ptr(o), _ptr(S_T),
-                        _ptr(d_T), _ptr(workspace), workspace.numel(),
-                        _stream(dev))
+                        _ptr(d_T), _ptr(rho), _ptr(qg), _ptr(workspace),
+                        workspace.numel(), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_forward")
+    if diagnostics:
+        return o, S_T, d_T, rho, qg
     return o, S_T, d_T
 
 
@@ -194,8 +204,9 @@ def precond_workspace_bytes(B, H, T, Dk, dtype):
 
 
 def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True,
-                      out=None, workspace=None):
-    """Phase 1 alone on the GPU: returns (ktilde or None, d_T).
+                      out=None, workspace=None, diagnostics=False):
+    """Phase 1 alone on the GPU: returns (ktilde or None, d_T), and with
+    ``diagnostics=True`` also (rho, q_geo) as in osdn_forward.
 
     ``out`` may pass preallocated (ktilde, d_T) (ktilde may be None to skip
     it) and ``workspace`` a preallocated uint8 device buffer.
@@ -218,11 +229,18 @@ def osdn_precond_scan(k, beta, r=None, eta=0.1, d0=None, want_ktilde=True,
     need = L.osdn_precond_workspace_bytes(B, H, T, Dk, _DTYPE_CODE[dt])
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rho = qg = None
+    if diagnostics:
+        rho = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        qg = torch.empty((B, H), dtype=torch.float32, device=dev)
     rc = L.osdn_precond_scan(B, H, T, Dk, _DTYPE_CODE[dt], _ptr(k), _ptr(beta),
                              _ptr(r), float(eta), _ptr(d0), _ptr(kt), _ptr(d_T),
-                             _ptr(workspace), workspace.numel(), _stream(dev))
+                             _ptr(rho), _ptr(qg), _ptr(workspace),
+                             workspace.numel(), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_precond_scan")
+    if diagnostics:
+        return kt, d_T, rho, qg
     return kt, d_T
 
 

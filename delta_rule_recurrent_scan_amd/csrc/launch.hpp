@@ -25,6 +25,8 @@ struct PrecondArgs {
   void* ktilde;             // [B,H,T,Dk] in the k dtype, or null
   float* dT;                // [B,H,Dk] or null
   void* ws;                 // precond_workspace_bytes(...) bytes, 16-byte aligned
+  float* rho;               // [B,H,T] residual contraction ratios, or null
+  float* qgeo;              // [B,H] their geometric mean, or null
 };
 
 // Arguments of the chunked WY engine. OSDN uses ktilde and beta, with the

@@ -113,8 +113,9 @@ size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
 
 int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
                       const float* beta, const float* r, float eta,
-                      const float* d0, void* ktilde, float* d_T,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      const float* d0, void* ktilde, float* d_T, float* rho,
+                      float* q_geo, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
   // Pointers of zero-size tensors may be NULL.
   if ((size_t)B * H * T > 0 && (!k || !beta)) return OSDN_ERR_NULL_ARG;
@@ -129,11 +130,13 @@ int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
   const Range ins[] = {rng(k, BH * T * Dk * es), rng(beta, BH * T * 4),
                        rng(r, r ? BH * T * 4 : 0), rng(d0, d0 ? BH * Dk * 4 : 0)};
   const Range outs[] = {rng(ktilde, ktilde ? BH * T * Dk * es : 0),
-                        rng(d_T, d_T ? BH * Dk * 4 : 0), rng(workspace, need)};
+                        rng(d_T, d_T ? BH * Dk * 4 : 0), rng(workspace, need),
+                        rng(rho, rho ? BH * T * 4 : 0),
+                        rng(q_geo, q_geo ? BH * 4 : 0)};
   const int allowed[][2] = {{1, 3}};  // d_T == d0
   if (!aliasing_ok(outs, ins, allowed, 1)) return OSDN_ERR_ALIASING;
   osdn::PrecondArgs a{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                      ktilde, d_T, workspace};
+                      ktilde, d_T, workspace, rho, q_geo};
   const int rc = osdn::launch_precond_scan(a, (hipStream_t)stream);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
@@ -143,8 +146,8 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  const void* q, const void* k, const void* v,
                  const float* beta, const float* r, float eta,
                  const float* d0, const float* S0, float scale, void* o,
-                 float* S_T, float* d_T, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 float* S_T, float* d_T, float* rho, float* q_geo,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
   if ((size_t)B * H * T > 0 && (!q || !k || !v || !beta || !o))
     return OSDN_ERR_NULL_ARG;
@@ -163,7 +166,8 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
   const Range outs[] = {rng(o, BH * T * Dv * es),
                         rng(S_T, S_T ? BH * Dv * Dk * 4 : 0),
                         rng(d_T, d_T ? BH * Dk * 4 : 0),
-                        rng(workspace, need)};
+                        rng(workspace, need), rng(rho, rho ? BH * T * 4 : 0),
+                        rng(q_geo, q_geo ? BH * 4 : 0)};
   const int allowed[][2] = {{1, 6}, {2, 5}};  // S_T == S0, d_T == d0
   if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
 
@@ -175,7 +179,7 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
     // operands; K~ is formed inside phase 2
     const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
     osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                         nullptr, d_T, wsb};
+                         nullptr, d_T, wsb, rho, q_geo};
     rc = osdn::launch_precond_scan(pa, s);
     if (rc == -1) return OSDN_ERR_UNSUPPORTED;
     if (rc != 0) return OSDN_ERR_HIP;
@@ -191,7 +195,7 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
     const size_t kt_bytes = round256(BH * T * Dk * es);
     void* pws = wsb + kt_bytes;
     osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                         workspace, d_T, pws};
+                         workspace, d_T, pws, rho, q_geo};
     rc = osdn::launch_precond_scan(pa, s);
     if (rc == -1) return OSDN_ERR_UNSUPPORTED;
     if (rc != 0) return OSDN_ERR_HIP;

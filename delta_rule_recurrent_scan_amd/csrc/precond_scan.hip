@@ -576,6 +576,71 @@ __global__ __launch_bounds__(256) void precond_ktilde_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// rho: the per-token residual contraction ratio and its geometric mean
+// ---------------------------------------------------------------------------
+// [OSDN-it] section 3 (Theorem 5.2): f_t(S_t) / f_t(S_{t-1}) =
+// (1 - beta_t c_t)^2 with c_t = <d_t, a_t>; section 4.2 reports its geometric
+// mean q_geo. From the chain's step sizes, 1 - beta_t c_t = g_t / e_t where
+// e_t = eta beta_t / n_t is nonzero; otherwise (eta = 0, beta_t = 0 or a zero
+// key) no step has been taken inside the chunk before t that the ratio could
+// see, so c_t = P_t <d_entry, a_t> exactly. One workgroup per (batch, head),
+// one token per thread, the entry values of d of the four chunks a block of
+// 256 tokens spans staged in LDS. Runs after the chain; reads its records.
+template <int DK, typename Tin>
+__global__ __launch_bounds__(256) void precond_rho_kernel(
+    int T, int nchunks, const Tin* __restrict__ k, const float* __restrict__ beta,
+    float eta, const float* __restrict__ rec, const float* __restrict__ dent,
+    float* __restrict__ rho, float* __restrict__ qgeo) {
+  using G = P1Cfg<DK, Tin>;
+  constexpr int C = G::C, VEC = G::VEC, NB = 256 / C;
+  __shared__ float dsh[NB * DK];
+  __shared__ float red[4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  float lsum = 0.f;
+  for (int t0 = 0; t0 < T; t0 += 256) {
+    const int j0 = t0 / C;
+    for (int e = tid; e < NB * DK; e += 256) {
+      const int jc = j0 + e / DK;
+      dsh[e] = jc < nchunks ? dent[((size_t)bh * nchunks + jc) * DK + e % DK] : 0.f;
+    }
+    __syncthreads();
+    const int t = t0 + tid;
+    if (t < T) {
+      const int j = t / C, i = t % C;
+      const float* dd = dsh + (j - j0) * DK;
+      const Tin* kr = k + ((size_t)bh * T + t) * DK;
+      float n = 0.f, x = 0.f;
+#pragma unroll
+      for (int c = 0; c < DK; c += VEC) {
+        const uint4 u = *reinterpret_cast<const uint4*>(kr + c);
+        const Tin* kv = reinterpret_cast<const Tin*>(&u);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float kx = to_f32(kv[e]);
+          const float a = kx * kx;
+          n += a;
+          x += a * dd[c + e];
+        }
+      }
+      const float bt = beta[(size_t)bh * T + t];
+      const float et = n > 0.f ? eta * bt / n : 0.f;
+      const float* rc = rec + ((size_t)bh * nchunks + j) * G::RS;
+      const float y = et != 0.f ? rc[G::R_G + i] / et
+                                : 1.f - bt * expf(rc[G::R_LP + i]) * x;
+      const float rt = y * y;
+      if (rho) rho[(size_t)bh * T + t] = rt;
+      lsum += logf(rt);
+    }
+    __syncthreads();
+  }
+  lsum = wave_sum(lsum);
+  if ((tid & 63) == 0) red[tid >> 6] = lsum;
+  __syncthreads();
+  if (tid == 0 && qgeo)
+    qgeo[bh] = T > 0 ? expf((red[0] + red[1] + red[2] + red[3]) / (float)T) : 1.f;
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static int nchunks_of(int T) { return (T + kPrecondChunk - 1) / kPrecondChunk; }
@@ -611,6 +676,14 @@ static int launch_dk(const PrecondArgs& a, hipStream_t s) {
   ktimer_after(s);
   int rc = (int)hipGetLastError();
   if (rc) return rc;
+  if (a.rho || a.qgeo) {
+    ktimer_before(s, "precond_rho");
+    hipLaunchKernelGGL((precond_rho_kernel<DK, Tin>), dim3(BH), block, 0, s, a.T, nch,
+                       (const Tin*)a.k, a.beta, a.eta, rec, dent, a.rho, a.qgeo);
+    ktimer_after(s);
+    rc = (int)hipGetLastError();
+    if (rc) return rc;
+  }
   if (nch > 0 && a.ktilde) {
     ktimer_before(s, "precond_ktilde");
     hipLaunchKernelGGL((precond_ktilde_kernel<DK, Tin>), dim3(BH * nch), block, 0, s,

@@ -97,6 +97,15 @@ size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
  *   S_T      [B,H,Dv,Dk] fp32 final state (NULL: not written)
  *   d_T      [B,H,Dk]    fp32 preconditioner after the last token (NULL: not
  *                        written)
+ *   rho      [B,H,T]     fp32 residual contraction ratio per token (NULL: not
+ *                        computed): rho_t = f_t(S_t) / f_t(S_{t-1}) =
+ *                        (1 - beta_t <d_t, k_t*k_t>)^2, f_t(S) = ||S k_t - v_t||^2/2
+ *                        ([OSDN-it] section 3, Theorem 5.2)
+ *   q_geo    [B,H]       fp32 geometric mean of rho over the T tokens of each
+ *                        stream, exp(mean log rho) (1 when T = 0; NULL: not
+ *                        computed) ([OSDN-it] section 4.2)
+ *            rho and q_geo depend on the phase-1 inputs only; asking for
+ *            either adds one pass over the keys after phase 1.
  *   workspace / workspace_bytes: device scratch of at least
  *            osdn_forward_workspace_bytes(...) bytes, 256-byte aligned.
  * S_T may be exactly S0 and d_T exactly d0 (in-place state update); any other
@@ -106,7 +115,7 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  const void* q, const void* k, const void* v,
                  const float* beta, const float* r, float eta,
                  const float* d0, const float* S0, float scale,
-                 void* o, float* S_T, float* d_T,
+                 void* o, float* S_T, float* d_T, float* rho, float* q_geo,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -120,16 +129,18 @@ size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype);
 /*
  * Phase 1 alone ([OSDN-it] 2.2, first phase of the two-phase implementation):
  * writes the preconditioned keys k~_t = d_t*k_t ([B,H,T,Dk], dtype; NULL: not
- * written) and d_T ([B,H,Dk] fp32; NULL: not written). Reads only k, beta, r,
- * eta and d0, with the same meaning and layout as in osdn_forward.
+ * written), d_T ([B,H,Dk] fp32; NULL: not written) and the residual ratios
+ * rho and q_geo (as in osdn_forward; NULL: not computed). Reads only k, beta,
+ * r, eta and d0, with the same meaning and layout as in osdn_forward.
  * workspace / workspace_bytes: device scratch of at least
  * osdn_precond_workspace_bytes(...) bytes, 256-byte aligned, not overlapping
  * any argument.
  */
 int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
                       const float* beta, const float* r, float eta,
-                      const float* d0, void* ktilde, float* d_T,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      const float* d0, void* ktilde, float* d_T, float* rho,
+                      float* q_geo, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * Phase 2 alone ([OSDN-it] 2.1-2.2, second phase): the chunkwise WY delta rule
@@ -249,10 +260,10 @@ void osdn_kernel_timing(int enable);
  * in first-launch order (at most `max`), its name (static storage), launch
  * count and mean duration in milliseconds; any output pointer may be NULL.
  * Returns the number of distinct kernels recorded, or -1 if the HIP runtime
- * fails. Kernel names: precond_prep, precond_chain, precond_ktilde (phase
- * 1), wy_prep, wy_prep_fused (phase 2 forming the preconditioned keys
- * itself), wy_scan (phase 2), gdn2_prep, gdn2_scan (GDN-2), osdn_decode,
- * gdn2_decode (recurrent decode).
+ * fails. Kernel names: precond_prep, precond_chain, precond_ktilde,
+ * precond_rho (phase 1), wy_prep, wy_prep_fused (phase 2 forming the
+ * preconditioned keys itself), wy_scan (phase 2), gdn2_prep, gdn2_scan
+ * (GDN-2), osdn_decode, gdn2_decode (recurrent decode).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

@@ -106,13 +106,14 @@ def test_supported_and_workspace_sizes():
 
 def _fwd(L, B=1, H=1, T=64, Dk=32, Dv=32, C=16, dt=1, q=0x10000, k=0x20000,
          v=0x30000, beta=0x40000, r=None, d0=None, S0=None, o=0x50000,
-         ST=None, dT=None, ws=0x100000, wsb=1 << 20):
+         ST=None, dT=None, rho=None, qg=None, ws=0x100000, wsb=1 << 20):
     P = ctypes.c_void_p
     L.osdn_forward.argtypes = ([ctypes.c_int] * 7 +
                                [P, P, P, P, P, ctypes.c_float, P, P,
-                                ctypes.c_float, P, P, P, P, ctypes.c_size_t, P])
+                                ctypes.c_float, P, P, P, P, P, P,
+                                ctypes.c_size_t, P])
     return L.osdn_forward(B, H, T, Dk, Dv, C, dt, q, k, v, beta, r, 0.1, d0,
-                          S0, 1.0, o, ST, dT, ws, wsb, None)
+                          S0, 1.0, o, ST, dT, rho, qg, ws, wsb, None)
 
 
 @needs_lib
@@ -136,6 +137,10 @@ def test_error_paths_are_host_side():
     # partial overlap of S_T with S0 is rejected (exact aliasing would pass)
     assert _fwd(L, S0=0x200000, ST=0x200000 + 4) == ALIASING
     assert _fwd(L, d0=0x300000, dT=0x300000 + 4) == ALIASING
+    # the residual-ratio outputs are outputs like the others
+    assert _fwd(L, rho=0x40000 + 8) == ALIASING      # over beta
+    assert _fwd(L, qg=0x50000) == ALIASING           # over o
+    assert _fwd(L, rho=0x400000, qg=0x400000 + 16) == ALIASING
 
 
 @needs_lib
@@ -143,13 +148,13 @@ def test_precond_scan_error_paths():
     L = osdn.load_library()
     P = ctypes.c_void_p
     L.osdn_precond_scan.argtypes = [ctypes.c_int] * 5 + [P, P, P, ctypes.c_float,
-                                                         P, P, P, P,
+                                                         P, P, P, P, P, P,
                                                          ctypes.c_size_t, P]
 
     def pre(B=1, T=8, Dk=32, k=0x1000, beta=0x2000, kt=None, dT=None,
-            ws=0x100000, wsb=1 << 20):
+            rho=None, qg=None, ws=0x100000, wsb=1 << 20):
         return L.osdn_precond_scan(B, 1, T, Dk, 1, k, beta, None, 0.1, None,
-                                   kt, dT, ws, wsb, None)
+                                   kt, dT, rho, qg, ws, wsb, None)
     assert pre(k=None) == NULL_ARG
     assert pre(T=-8) == BAD_DIMS
     assert pre(Dk=40) == UNSUPPORTED
@@ -158,6 +163,8 @@ def test_precond_scan_error_paths():
     assert pre(ws=0x100040) == WORKSPACE          # not 256-byte aligned
     assert pre(kt=0x1000 + 16) == ALIASING
     assert pre(ws=0x1000) == ALIASING             # workspace over k
+    assert pre(rho=0x2000) == ALIASING            # rho over beta
+    assert pre(qg=0x100000 + 256) == ALIASING     # q_geo inside the workspace
     # B = 0: nothing to do, no pointer or workspace needed
     assert pre(B=0, k=None, beta=None, ws=None, wsb=0) == OK
 

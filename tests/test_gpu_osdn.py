@@ -271,3 +271,90 @@ def test_parity_full_size_sampled(name):
         ref = oracle(inp, sl)
         check((o[sl], S[sl], d[sl]), ref, w.dtype, "%s b=%d h=%d" % (name, b, h))
     assert np.all(np.isfinite(o))
+
+
+# Residual contraction ratios rho_t = (1 - beta_t c_t)^2 and their geometric
+# mean per stream. They come from the same fp32 phase-1 arithmetic as d_T, so
+# they are held to d_T's bound: relative L2 <= 1e-5 over the compared tensor.
+RHO_TOL = 1e-5
+
+
+def check_rho(rho, qg, inp, where, sl=(slice(None), slice(None))):
+    f = lambda key: None if inp.get(key) is None else W.to_f64(inp[key])[sl]
+    rr, rq = R.residual_ratio_ref(f("k"), f("beta"), f("r"), inp["eta"], f("d0"))
+    er, eq = rel_l2(W.to_f64(rho)[sl], rr), rel_l2(W.to_f64(qg)[sl], rq)
+    print("%s: rel_l2 rho=%.3e q_geo=%.3e" % (where, er, eq), flush=True)
+    assert er <= RHO_TOL and eq <= RHO_TOL
+
+
+@pytest.mark.parametrize("w", SMALL, ids=["%s-T%d" % (w.name, w.T) for w in SMALL])
+def test_residual_ratio_small(w):
+    x = to_dev(W.make_inputs(w))
+    inp = W.make_inputs(w)
+    o, S, d, rho, qg = osdn.osdn_forward(x["q"], x["k"], x["v"], x["beta"],
+                                         x["r"], x["eta"], chunk=w.chunk,
+                                         diagnostics=True)
+    torch.cuda.synchronize()
+    check_rho(rho, qg, inp, w.name)
+    # asking for the diagnostics changes nothing else
+    check((W.to_f64(o), W.to_f64(S), W.to_f64(d)), oracle(inp), w.dtype,
+          w.name + " with diagnostics")
+
+
+def test_residual_ratio_degenerate_steps():
+    """Tokens where the step size e_t = eta beta_t / n_t is zero (zero keys,
+    beta = 0) take the ratio from the entry preconditioner; eta = 0 makes
+    every token do so."""
+    w = small("osdn-1.3b-apf", B=1, H=2, T=64 * 2 + 30)
+    inp = W.make_inputs(w)
+    k = inp["k"].clone()
+    k[:, :, 3] = 0
+    k[:, 1, 70:80] = 0
+    inp["k"] = k
+    b = inp["beta"].clone()
+    b[:, :, 10] = 0
+    b[:, 0, 100:130] = 0
+    inp["beta"] = b
+    g = np.random.default_rng(8)
+    inp["d0"] = torch.from_numpy(g.uniform(0.5, 1.5, (1, 2, w.Dk)).astype(np.float32))
+    for eta in (0.1, 0.0):
+        inp["eta"] = eta
+        x = to_dev(inp)
+        _, _, rho, qg = osdn.osdn_precond_scan(x["k"], x["beta"], x["r"], eta,
+                                               x["d0"], want_ktilde=False,
+                                               diagnostics=True)
+        torch.cuda.synchronize()
+        check_rho(rho, qg, inp, "degenerate eta=%g" % eta)
+        assert np.all(W.to_f64(rho)[0, :, 3] == 1.0)
+
+
+def test_residual_ratio_chunk16_path_and_empty():
+    w = small("osdn-340m", B=2, H=1, T=200, chunk=16)
+    inp = W.make_inputs(w)
+    x = to_dev(inp)
+    _, _, _, rho, qg = osdn.osdn_forward(x["q"], x["k"], x["v"], x["beta"],
+                                         None, x["eta"], chunk=16,
+                                         diagnostics=True)
+    torch.cuda.synchronize()
+    check_rho(rho, qg, inp, "chunk 16")
+    w0 = small("osdn-340m", B=2, H=1, T=0)
+    x0 = to_dev(W.make_inputs(w0))
+    _, _, _, rho0, qg0 = osdn.osdn_forward(x0["q"], x0["k"], x0["v"],
+                                           x0["beta"], None, 0.1,
+                                           diagnostics=True)
+    torch.cuda.synchronize()
+    assert rho0.shape == (2, 1, 0) and torch.all(qg0.cpu() == 1.0)
+
+
+@pytest.mark.parametrize("name", ["osdn-340m", "osdn-1.3b-apf"])
+def test_residual_ratio_full_size_sampled(name):
+    w = W.BY_NAME[name]
+    inp = W.make_inputs(w)
+    x = to_dev(inp)
+    _, _, _, rho, qg = osdn.osdn_forward(x["q"], x["k"], x["v"], x["beta"],
+                                         x["r"], x["eta"], chunk=w.chunk,
+                                         diagnostics=True)
+    torch.cuda.synchronize()
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]:
+        check_rho(rho, qg, inp, "%s b=%d h=%d" % (name, b, h),
+                  (slice(b, b + 1), slice(h, h + 1)))
