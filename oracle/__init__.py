@@ -19,7 +19,7 @@ two papers):
 Modules:
 
 * ``recurrence``  fp64 NumPy token-by-token recurrences (OSDN, phase 1 alone,
-  GDN-2), the surrogate h_t, by definition and in closed form, and the
+  GDN-2, OSDN on a per-channel-decay backbone), the surrogate h_t, by definition and in closed form, and the
   residual contraction ratios with their geometric mean q_geo.
 * ``exact``     the same recurrences in exact rational arithmetic
   (``fractions.Fraction``) plus an independent closed-form unrolling of the
@@ -36,6 +36,7 @@ from .recurrence import (  # noqa: F401
     osdn_ref,
     precond_scan_ref,
     residual_ratio_ref,
+    osdn_gated_ref,
     deltanet_ref,
     gdn2_ref,
     h_closed_form,

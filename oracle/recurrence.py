@@ -242,6 +242,50 @@ def osdn_ref(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None, scale=1.0,
     return out
 
 
+def osdn_gated_ref(q, k, v, beta, log_alpha, r=None, eta=0.1, d0=None,
+                   S0=None, scale=1.0, return_states=False):
+    """OSDN on a gated backbone (per-key-channel decay), token by token, fp64.
+
+    [OSDN-it] section 4 runs OSDN on DeltaNet, Gated DeltaNet and Kimi Delta
+    Attention backbones without printing the combined rule. Reading taken:
+    the backbone's decay acts on the memory state before the token's delta
+    step, and OSDN's step is unchanged, reading with the plain key and
+    writing with the preconditioned key; the preconditioner learner (phase 1)
+    is untouched:
+      S_dec = S_{t-1} Diag(alpha_t)                          (alpha = exp(log_alpha))
+      S_t   = S_dec + beta_t (v_t - S_dec k_t) k~_t^T, k~_t = d_t * k_t
+      o_t   = scale * S_t q_t
+      d_{t+1} as in osdn_ref.
+    State [B,H,Dv,Dk] as in osdn_ref (the decay scales the key columns).
+    log_alpha: [B,H,T,Dk]; a per-head scalar decay (Gated DeltaNet) is the
+    case of equal channels. Returns (o, S_T, d_T) (and every S_t on request).
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    la = _f64(log_alpha)
+    r, d = _defaults(k, beta, _f64(r), _f64(d0))
+    lead = k.shape[:-2]
+    T, Dk = k.shape[-2], k.shape[-1]
+    Dv = v.shape[-1]
+    S = (np.zeros(lead + (Dv, Dk)) if S0 is None
+         else np.array(S0, dtype=np.float64, copy=True))
+    o = np.empty(lead + (T, Dv))
+    states = [S.copy()] if return_states else None
+    for t in range(T):
+        kt = k[..., t, :]
+        bt = beta[..., t]
+        ktil, d_next, _, _ = _phase1_step(d, kt, bt, r[..., t], eta)
+        S = S * np.exp(la[..., t, :])[..., None, :]
+        u = v[..., t, :] - np.einsum("...vk,...k->...v", S, kt)
+        S = S + bt[..., None, None] * u[..., :, None] * ktil[..., None, :]
+        o[..., t, :] = scale * np.einsum("...vk,...k->...v", S, q[..., t, :])
+        if return_states:
+            states.append(S.copy())
+        d = d_next
+    if return_states:
+        return o, S, d, states
+    return o, S, d
+
+
 def deltanet_ref(q, k, v, beta, S0=None, scale=1.0):
     """Plain DeltaNet, S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T.
 

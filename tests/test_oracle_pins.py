@@ -155,6 +155,40 @@ def pin_residual_ratio_is_loss_ratio():
     np.testing.assert_allclose(rho0, (1.0 - beta) ** 2, rtol=1e-12)
 
 
+def pin_gated_osdn_reductions():
+    """OSDN on a decaying backbone: no decay gives OSDN exactly; d = 1, eta = 0
+    and no forgetting give Kimi-style delta attention, i.e. GDN-2 with erase
+    and write gates equal to beta (transposed state); and on every token the
+    write contracts the loss of the DECAYED state by (1 - beta c)^2."""
+    q, k, v, beta, r = _rand_osdn(21, T=25)
+    g = _rng(22)
+    la = -0.3 * g.random(k.shape)
+    S0 = g.standard_normal((2, 2, 5, 6))
+    d0 = g.uniform(0.5, 1.5, (2, 2, 6))
+    o1, S1, d1 = R.osdn_gated_ref(q, k, v, beta, np.zeros(k.shape), r, 0.2,
+                                  d0, S0)
+    o2, S2, d2 = R.osdn_ref(q, k, v, beta, r, 0.2, d0, S0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(S1, S2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(d1, d2)
+    o3, S3, _ = R.osdn_gated_ref(q, k, v, beta, la, None, 0.0)
+    bb = np.broadcast_to(beta[..., None], k.shape)
+    ww = np.broadcast_to(beta[..., None], v.shape)
+    o4, S4 = R.gdn2_ref(q, k, v, la, bb, ww)
+    np.testing.assert_allclose(o3, o4, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S3, np.swapaxes(S4, -1, -2), rtol=1e-11,
+                               atol=1e-12)
+    _, _, _, states = R.osdn_gated_ref(q, k, v, beta, la, r, 0.2, d0, S0,
+                                       return_states=True)
+    _, _, c, _ = R.precond_scan_ref(k, beta, r, 0.2, d0)
+    for t in range(k.shape[2]):
+        dec = states[t] * np.exp(la[:, :, t])[:, :, None, :]
+        f_new = R.regression_loss(states[t + 1], k[:, :, t], v[:, :, t])
+        f_old = R.regression_loss(dec, k[:, :, t], v[:, :, t])
+        np.testing.assert_allclose(f_new, (1 - beta[:, :, t] * c[:, :, t]) ** 2
+                                   * f_old, rtol=1e-10, atol=1e-14)
+
+
 def pin_exact_unrolled():
     """fp64 oracle vs exact rationals vs the transition-product unrolling."""
     g = _rng(6)
@@ -315,6 +349,7 @@ PINS = [
     pin_constant_gate_fixed_point,
     pin_per_token_contraction,
     pin_residual_ratio_is_loss_ratio,
+    pin_gated_osdn_reductions,
     pin_exact_unrolled,
     pin_deltanet_reduction,
     pin_newton_condition,
