@@ -40,6 +40,8 @@ _KERNEL_SOURCES = {
     "wy_scan": ["wy_chunk.hip"],
     "gdn2_prep": ["wy_chunk.hip"],
     "gdn2_scan": ["wy_chunk.hip"],
+    "gated_prep": ["wy_chunk.hip"],
+    "gated_scan": ["wy_chunk.hip"],
     "osdn_decode": ["decode.hip"],
     "gdn2_decode": ["decode.hip"],
 }
@@ -107,6 +109,9 @@ def kernel_bytes_per_token_head(w, apf=False):
         "gdn2_prep": (3 * dk + 2 * dv) * s + 4 * dk + frags_g,
         # Wk, X', U, P, Q^, exit decay -> o
         "gdn2_scan": frags_g + dv * s,
+        # q, k, k~, v, beta, log alpha -> Wk, X', U, P, Q^, exit decay
+        "gated_prep": (3 * dk + dv) * s + 4 + 4 * dk + frags_g,
+        "gated_scan": frags_g + dv * s,
     }
 
 
@@ -174,6 +179,65 @@ def cpu_baseline(w, inp, budget_s=12.0):
         done += 1
     per_stream = t_used / done
     total = per_stream * w.B * w.H
+    return {"value": w.B * w.T / total, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) streams at full length T=%d, "
+                      "fp64 NumPy token recurrence, one thread; scaled to all "
+                      "streams" % (done, w.B * w.H, w.T)}
+
+
+def bench_gated(args, w, inp, x, dt, dev):
+    """One step = one osdn_gated_forward call (OSDN on a per-channel-decay
+    backbone) over the workload."""
+    import delta_rule_recurrent_scan_amd as osdn
+    L = osdn.load_library()
+    o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
+    S_T = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)
+    d_T = torch.empty((w.B, w.H, w.Dk), dtype=torch.float32, device=dev)
+    ws_n = L.osdn_gated_forward_workspace_bytes(w.B, w.H, w.T, w.Dk, w.Dv,
+                                                w.chunk, 1 if w.dtype == "bf16"
+                                                else 0)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        osdn.osdn_gated_forward(x["q"], x["k"], x["v"], x["beta"],
+                                x["log_alpha"], x["r"], x["eta"],
+                                chunk=w.chunk, out=(o, S_T, d_T), workspace=ws)
+
+    ms_step, kt = timed_steps(step, args)
+    kb = kernel_bytes_per_token_head(w, inp["r"] is not None)
+    rec = {
+        "metric": "OSDN on a per-channel-decay backbone forward tokens/s + % "
+                  "HBM roofline, H=16 d=128 T=4096, 1 GPU",
+        "value": w.B * w.T / (ms_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T,
+                   "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk},
+        "roofline": roofline(w, kt, kb),
+        "kernels_ms": kt,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_gated(w, inp)
+    return rec
+
+
+def cpu_baseline_gated(w, inp, budget_s=12.0):
+    from oracle import recurrence as R
+    f = W.to_f64
+    arrs = {k: f(inp[k]) for k in ("q", "k", "v", "beta", "log_alpha", "r")}
+    done, t_used = 0, 0.0
+    order = [(b, h) for b in range(w.B) for h in range(w.H)]
+    while done < len(order) and t_used < budget_s:
+        b, h = order[done]
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        R.osdn_gated_ref(*(arrs[k][sl] for k in ("q", "k", "v", "beta",
+                                                  "log_alpha", "r")), inp["eta"])
+        t_used += time.perf_counter() - t0
+        done += 1
+    total = t_used / done * w.B * w.H
     return {"value": w.B * w.T / total, "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
             "sample": "%d of %d (batch, head) streams at full length T=%d, "
@@ -373,6 +437,9 @@ def main():
         return
     if w.kind == "gdn2":
         print(json.dumps(bench_gdn2(args, w, inp, x, dt, dev)), flush=True)
+        return
+    if w.decay:
+        print(json.dumps(bench_gated(args, w, inp, x, dt, dev)), flush=True)
         return
     o = torch.empty((w.B, w.H, w.T, w.Dv), dtype=dt, device=dev)
     S_T = torch.empty((w.B, w.H, w.Dv, w.Dk), dtype=torch.float32, device=dev)

@@ -13,7 +13,8 @@ import os
 import torch
 
 __all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
-           "gdn2_forward", "osdn_decode", "gdn2_decode",
+           "gdn2_forward", "osdn_gated_forward", "osdn_decode",
+           "gdn2_decode",
            "workspace_bytes", "precond_workspace_bytes", "supported",
            "kernel_timing", "kernel_times",
            "OsdnError", "library_path", "load_library"]
@@ -74,7 +75,14 @@ def load_library():
     L.gdn2_forward.argtypes = ([I] * 7 + [P, P, P, P, P, P, P, F, P, P, P, Z,
                                           P])
     L.gdn2_forward.restype = I
-    L.osdn_decode.argtypes = [I] * 6 + [P, P, P, P, P, F, P, P, F, P, P]
+    L.osdn_decode.argtypes = [I] * 6 + [P, P, P, P, P, F, P, P, P, F, P, P]
+    L.osdn_gated_forward_supported.argtypes = [I, I, I, I]
+    L.osdn_gated_forward_supported.restype = I
+    L.osdn_gated_forward_workspace_bytes.argtypes = [I] * 7
+    L.osdn_gated_forward_workspace_bytes.restype = Z
+    L.osdn_gated_forward.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, P, F, P,
+                                                P, P, P, Z, P])
+    L.osdn_gated_forward.restype = I
     L.osdn_decode.restype = I
     L.gdn2_decode.argtypes = [I] * 6 + [P, P, P, P, P, P, P, F, P, P]
     L.gdn2_decode.restype = I
@@ -314,10 +322,13 @@ def gdn2_forward(q, k, v, log_alpha, b, w, S0=None, chunk=64, scale=1.0,
     return o, S_T
 
 
-def osdn_decode(q, k, v, beta, S, d, r=None, eta=0.1, scale=1.0, out=None):
+def osdn_decode(q, k, v, beta, S, d, r=None, eta=0.1, scale=1.0, out=None,
+                log_alpha=None):
     """OSDN recurrent decode on the GPU: advances the T tokens of q, k, v
     (usually T = 1) through the token recurrence, updating S ([B,H,Dv,Dk]
-    fp32) and d ([B,H,Dk] fp32) IN PLACE; returns o [B,H,T,Dv]."""
+    fp32) and d ([B,H,Dk] fp32) IN PLACE; returns o [B,H,T,Dv].
+    log_alpha ([B,H,T,Dk] fp32): per-channel decay of a gated backbone, as
+    in osdn_gated_forward (None: plain OSDN)."""
     L = load_library()
     dev = q.device
     B, H, T, Dk = q.shape
@@ -332,11 +343,13 @@ def osdn_decode(q, k, v, beta, S, d, r=None, eta=0.1, scale=1.0, out=None):
     _check(r, "r", (B, H, T), torch.float32, dev)
     _check(S, "S", (B, H, Dv, Dk), torch.float32, dev)
     _check(d, "d", (B, H, Dk), torch.float32, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, Dk), torch.float32, dev)
     o = torch.empty((B, H, T, Dv), dtype=dt, device=dev) if out is None else out
     _check(o, "o", (B, H, T, Dv), dt, dev)
     rc = L.osdn_decode(B, H, T, Dk, Dv, _DTYPE_CODE[dt], _ptr(q), _ptr(k),
-                       _ptr(v), _ptr(beta), _ptr(r), float(eta), _ptr(S),
-                       _ptr(d), float(scale), _ptr(o), _stream(dev))
+                       _ptr(v), _ptr(beta), _ptr(r), float(eta),
+                       _ptr(log_alpha), _ptr(S), _ptr(d), float(scale),
+                       _ptr(o), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_decode")
     return o
@@ -366,3 +379,47 @@ def gdn2_decode(q, k, v, log_alpha, b, w, S, scale=1.0, out=None):
     if rc != 0:
         raise OsdnError(rc, "gdn2_decode")
     return o
+
+
+def osdn_gated_forward(q, k, v, beta, log_alpha, r=None, eta=0.1, d0=None,
+                       S0=None, chunk=64, scale=1.0, out=None, workspace=None):
+    """OSDN on a per-key-channel-decay backbone on the GPU: returns
+    (o, S_T, d_T). Arguments as for osdn_forward plus log_alpha
+    [B,H,T,Dk] fp32 (the decay applied to the state before each token's
+    step)."""
+    L = load_library()
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    _check(r, "r", (B, H, T), torch.float32, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, Dk), torch.float32, dev)
+    _check(d0, "d0", (B, H, Dk), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+        d_T = torch.empty((B, H, Dk), dtype=torch.float32, device=dev)
+    else:
+        o, S_T, d_T = out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    _check(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    _check(d_T, "d_T", (B, H, Dk), torch.float32, dev)
+    need = L.osdn_gated_forward_workspace_bytes(B, H, T, Dk, Dv, chunk,
+                                                _DTYPE_CODE[dt])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = L.osdn_gated_forward(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt],
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                              float(eta), _ptr(log_alpha), _ptr(d0), _ptr(S0),
+                              float(scale), _ptr(o), _ptr(S_T), _ptr(d_T),
+                              _ptr(workspace), workspace.numel(), _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_gated_forward")
+    return o, S_T, d_T

@@ -12,6 +12,7 @@
 //
 // OSDN (state [Dv, Dk], row = value channel):
 //   a = k*k, n = ||k||^2, c = <d, a>, k~ = d*k         (lane-local, 16-lane sums)
+//   S <- S Diag(alpha)                                 (decaying backbone only)
 //   S <- S + beta (v - S k) k~^T, o = scale S q        (per row, 16-lane sums)
 //   d <- r d + eta beta (1 - beta c)/n a              (0 step if n = 0)
 // Every row group tracks d for its own columns, so d needs no exchange.
@@ -82,8 +83,8 @@ template <int DK, int DV, typename Tin>
 __global__ __launch_bounds__(kDecThreads) void osdn_decode_kernel(
     int T, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const float* __restrict__ beta,
-    const float* __restrict__ r, float eta, float* __restrict__ S,
-    float* __restrict__ d, float scale, Tin* __restrict__ o) {
+    const float* __restrict__ r, float eta, const float* __restrict__ log_alpha,
+    float* __restrict__ S, float* __restrict__ d, float scale, Tin* __restrict__ o) {
   constexpr int NC = DK / 16, NR = DV / 16;
   const int bh = blockIdx.x;
   const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
@@ -105,6 +106,17 @@ __global__ __launch_bounds__(kDecThreads) void osdn_decode_kernel(
     for (int i = 0; i < NR; ++i) vv[i] = to_f32(v[tt * DV + rg + 16 * i]);
     const float bt = beta[tt];
     const float rt = r ? r[tt] : 1.f;
+    if (log_alpha) {
+      // per-key-channel decay of the state before the token's step
+      float la[NC];
+      load_cols<DK, float>(log_alpha + tt * DK, cl, la);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const float al = expf(la[j]);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) s[i][j] *= al;
+      }
+    }
 
     // key statistics and the read S k, all with the plain key
     float n = 0.f, c = 0.f, kt[NC], p[NR];
@@ -259,7 +271,7 @@ int launch_decode_t(const DecodeArgs& a, hipStream_t s) {
     ktimer_before(s, "osdn_decode");
     hipLaunchKernelGGL((osdn_decode_kernel<DK, DV, Tin>), dim3(BH), dim3(kDecThreads), 0, s,
                        a.T, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, a.beta, a.r,
-                       a.eta, a.S, a.d, a.scale, (Tin*)a.o);
+                       a.eta, a.log_alpha, a.S, a.d, a.scale, (Tin*)a.o);
   }
   ktimer_after(s);
   return (int)hipGetLastError();

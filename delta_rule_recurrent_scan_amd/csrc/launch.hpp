@@ -67,7 +67,7 @@ struct DecodeArgs {
   const float* beta;        // OSDN: [B,H,T]
   const float* r;           // OSDN: [B,H,T] or null
   float eta;
-  const float* log_alpha;   // GDN-2: [B,H,T,Dk]
+  const float* log_alpha;   // [B,H,T,Dk] (OSDN: null = no decay)
   const void* b;            // GDN-2: [B,H,T,Dk]
   const void* w;            // GDN-2: [B,H,T,Dv]
   float* S;                 // in/out
@@ -84,6 +84,9 @@ int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
 size_t precond_workspace_bytes(int B, int H, int T, int Dk, int bf16);
 int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_osdn_fused(const ChunkArgs& a, hipStream_t s);
+// OSDN on a per-channel-decay backbone: ktilde, beta and log_alpha used,
+// state [B,H,Dv,Dk]; workspace as for GDN-2 (wy_workspace_bytes(..., 1)).
+int launch_osdn_gated_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_decode(const DecodeArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);

@@ -279,8 +279,8 @@ int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
 
 int osdn_decode(int B, int H, int T, int Dk, int Dv, int dtype, const void* q,
                 const void* k, const void* v, const float* beta,
-                const float* r, float eta, float* S, float* d, float scale,
-                void* o, void* stream) {
+                const float* r, float eta, const float* log_alpha, float* S,
+                float* d, float scale, void* o, void* stream) {
   if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
   const size_t BH = (size_t)B * H;
   if (BH * T > 0 && (!q || !k || !v || !beta || !S || !d || !o))
@@ -291,12 +291,13 @@ int osdn_decode(int B, int H, int T, int Dk, int Dv, int dtype, const void* q,
   const size_t es = elem(dtype);
   const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
                        rng(v, BH * T * Dv * es), rng(beta, BH * T * 4),
-                       rng(r, r ? BH * T * 4 : 0)};
+                       rng(r, r ? BH * T * 4 : 0),
+                       rng(log_alpha, log_alpha ? BH * T * Dk * 4 : 0)};
   const Range outs[] = {rng(o, BH * T * Dv * es), rng(S, BH * Dv * Dk * 4),
                         rng(d, BH * Dk * 4)};
   if (!aliasing_ok(outs, ins, nullptr, 0)) return OSDN_ERR_ALIASING;
   osdn::DecodeArgs a{B, H, T, Dk, Dv, dtype == OSDN_BF16, 0, q, k, v, beta, r,
-                     eta, nullptr, nullptr, nullptr, S, d, scale, o};
+                     eta, log_alpha, nullptr, nullptr, S, d, scale, o};
   const int rc = osdn::launch_decode(a, (hipStream_t)stream);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
@@ -322,6 +323,69 @@ int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype, const void* q,
   osdn::DecodeArgs a{B, H, T, Dk, Dv, dtype == OSDN_BF16, 1, q, k, v, nullptr,
                      nullptr, 0.f, log_alpha, b, w, S, nullptr, scale, o};
   const int rc = osdn::launch_decode(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype) {
+  return gdn2_forward_supported(Dk, Dv, chunk, dtype);
+}
+
+size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                          int chunk, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
+      !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return 0;
+  const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
+  const size_t p2 = chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 1);
+  if (p1 == 0 && p2 == 0) return 0;
+  // the preconditioned keys, then scratch shared by the two phases
+  return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
+}
+
+int osdn_gated_forward(int B, int H, int T, int Dk, int Dv, int chunk,
+                       int dtype, const void* q, const void* k, const void* v,
+                       const float* beta, const float* r, float eta,
+                       const float* log_alpha, const float* d0,
+                       const float* S0, float scale, void* o, float* S_T,
+                       float* d_T, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  if ((size_t)B * H * T > 0 && (!q || !k || !v || !beta || !log_alpha || !o))
+    return OSDN_ERR_NULL_ARG;
+  if (!osdn_gated_forward_supported(Dk, Dv, chunk, dtype))
+    return OSDN_ERR_UNSUPPORTED;
+  const size_t need =
+      osdn_gated_forward_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
+  if ((size_t)B * H == 0) return OSDN_OK;
+  const size_t BH = (size_t)B * H, es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(beta, BH * T * 4),
+                       rng(r, r ? BH * T * 4 : 0), rng(log_alpha, BH * T * Dk * 4),
+                       rng(d0, d0 ? BH * Dk * 4 : 0),
+                       rng(S0, S0 ? BH * Dv * Dk * 4 : 0)};
+  const Range outs[] = {rng(o, BH * T * Dv * es),
+                        rng(S_T, S_T ? BH * Dv * Dk * 4 : 0),
+                        rng(d_T, d_T ? BH * Dk * 4 : 0),
+                        rng(workspace, need)};
+  const int allowed[][2] = {{1, 7}, {2, 6}};  // S_T == S0, d_T == d0
+  if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char* wsb = static_cast<unsigned char*>(workspace);
+  const size_t kt_bytes = round256(BH * T * Dk * es);
+  void* pws = wsb + kt_bytes;
+  osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                       workspace, d_T, pws, nullptr, nullptr};
+  int rc = osdn::launch_precond_scan(pa, s);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  if (rc != 0) return OSDN_ERR_HIP;
+  osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                     workspace, v, beta, S0, scale, o, S_T,
+                     log_alpha, nullptr, nullptr, pws};
+  rc = osdn::launch_osdn_gated_chunk(ca, s);
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }

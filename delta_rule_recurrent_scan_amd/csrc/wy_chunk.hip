@@ -52,6 +52,18 @@ struct Gdn2Variant {};
 // of d: K~ = (P d^T + L A) * K, L[t][i] = (P_t / P_{i+1}) g_i for i < t,
 // A = K * K ([OSDN-it] 2.2). Requires chunk == the phase-1 chunk.
 struct OsdnFusedVariant {};
+// OSDN on a backbone with per-key-channel decay (Kimi-style; a Gated
+// DeltaNet scalar decay is the case of equal channels): S_t = S_{t-1}
+// Diag(alpha_t) + beta_t (v_t - S_{t-1} Diag(alpha_t) k_t) k~_t^T. The decay
+// is absorbed as for GDN-2, with read key y_t = gamma_t*beta_t*k_t, write key
+// x_t = k~_t/gamma_t, value beta_t v_t, query gamma_t*q_t, exit keys
+// k~_t*gamma_C/gamma_t and exit decay gamma_C; the state is stored [Dv, Dk].
+struct OsdnGatedVariant {};
+
+// Variants whose chunk operands carry a per-channel decay.
+template <class V>
+constexpr bool kDecayVariant =
+    std::is_same<V, Gdn2Variant>::value || std::is_same<V, OsdnGatedVariant>::value;
 
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
 // storage dtype: Wk as 16-row A fragments (row block tb at tb*16*Dk); the
@@ -173,7 +185,7 @@ struct PrepCfg {
   // that fits, else over the Gram/inverse buffers (not in use yet during the
   // decay pass), whose zero blocks above the diagonal are then restored
   static constexpr int LDA = DK + 4;
-  static constexpr size_t kLaBytes = kGdn2 ? (size_t)C * LDA * 4 : 0;
+  static constexpr size_t kLaBytes = kDecayVariant<V> ? (size_t)C * LDA * 4 : 0;
   static constexpr bool kLaOwn = oEnd + kLaBytes <= 163840;
   static constexpr bool kLaInGram = !kLaOwn && oAb + kLaBytes <= oG;
   static constexpr size_t oLa = kLaOwn ? oEnd : oAb;
@@ -198,7 +210,8 @@ struct PrepRegs {
   uint4 k[NLK], q[NLK], x[kFused ? 1 : NLK], v[NLV], w[kGdn2 ? NLV : 1];
   float bk[NLK], bv[NLV];          // OSDN: beta of the row
   static constexpr int NLA = (C * DK / 4 + G::NT - 1) / G::NT;
-  uint4 la4[kGdn2 ? NLA : 1];      // GDN-2: log alpha, 4 channels per load
+  static constexpr bool kDecay = kDecayVariant<V>;
+  uint4 la4[kDecay ? NLA : 1];     // decay variants: log alpha, 4 channels per load
   float plp, pg, pd;               // fused OSDN: record entries, entry d
   int vrows;                       // valid rows of the fetched chunk
 
@@ -240,7 +253,7 @@ struct PrepRegs {
       else
         bv[i] = p.beta[t0 + rr];
     }
-    if constexpr (kGdn2) {
+    if constexpr (kDecay) {
 #pragma unroll
       for (int i = 0; i < NLA; ++i) {
         const int e = min(tid + i * G::NT, C * DK / 4 - 1);
@@ -289,7 +302,7 @@ struct PrepRegs {
         }
       }
     }
-    if constexpr (kGdn2) {
+    if constexpr (kDecay) {
       float* La = reinterpret_cast<float*>(smem + G::oLa);
 #pragma unroll
       for (int i = 0; i < NLA; ++i) {
@@ -338,6 +351,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   using G = PrepCfg<V, DK, DV, C, Tin>;
   constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
   constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
+  constexpr bool kDecay = kDecayVariant<V>;
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDS16 = G::LDS16,
                 TB = G::TB, DB = G::DB, VBT = G::VBT, NW = G::NW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
@@ -378,12 +392,14 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     regs.store(Ys, Xs, Qs, Zs, smem);
     // the next chunk's raw operands (the last chunk again at the end)
     regs.load(p, chunk_of(min(pos + (int)gridDim.x, total - 1)), nchunks);
-    if constexpr (kGdn2) {
+    if constexpr (kDecay) {
       // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
       // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
       // staged log alpha into the inclusive prefix lambda in place and give
-      // the exit decay g = gamma_C. (2) Row pass: X = k/gamma, Y = gamma*b*k,
-      // Q = gamma*q with gamma = exp(lambda), VEC channels per access.
+      // the exit decay g = gamma_C. (2) Row pass: X = x/gamma, Y = gamma*y,
+      // Q = gamma*q with gamma = exp(lambda), VEC channels per access (GDN-2:
+      // x = k and y = b*k from the staged k and b; gated OSDN: x = k~ and
+      // y = beta*k as staged).
       constexpr int TPC = G::TPC, TPT = G::TPT, CPW = 64 / TPC, LDA = G::LDA;
       float* La = reinterpret_cast<float*>(smem + G::oLa);
       __syncthreads();
@@ -425,7 +441,10 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
           const float igam = __builtin_amdgcn_rcpf(gam);
           const float kk = to_f32(kv[u]);
           xo[u] = from_f32<Tin>(kk * igam);
-          yo[u] = from_f32<Tin>(gam * to_f32(bv[u]) * kk);
+          if constexpr (kGdn2)
+            yo[u] = from_f32<Tin>(gam * to_f32(bv[u]) * kk);
+          else
+            yo[u] = from_f32<Tin>(gam * to_f32(bv[u]));
           qo[u] = from_f32<Tin>(gam * to_f32(qv[u]));
         }
         *reinterpret_cast<uint4*>(Xs + t * LDK + c0) = *reinterpret_cast<const uint4*>(xo);
@@ -570,7 +589,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         if (db >= DB) break;
         Frag<C, Tin> fx;
         fx.load_kmajor_perm(Xs + db * 16, LDK);  // the scan's k order
-        if constexpr (kGdn2) {
+        if constexpr (kDecay) {
           const float gd = gC[db * 16 + (lane & 15)];
           if constexpr (sizeof(Tin) == 2) {
 #pragma unroll
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         }
         fx.store_global(wb.xp + xoff + (size_t)db * 16 * C);
       }
-      if constexpr (kGdn2) {
+      if constexpr (kDecay) {
         if (tid < DK) wb.g[(size_t)n * DK + tid] = gC[tid];
       }
     }
@@ -678,7 +697,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     // ---- Wk (and GDN-2's Q^) as row-block fragments -------------------------
     {
       const size_t koff = (size_t)n * C * DK;
-      constexpr int NJ = (kGdn2 ? 2 : 1) * TB;
+      constexpr int NJ = (kDecay ? 2 : 1) * TB;
 #pragma unroll
       for (int it = 0; it < (NJ + NW - 1) / NW; ++it) {
         const int job = wave + it * NW;
@@ -714,7 +733,9 @@ struct ScanCfg {
   static_assert(TB <= NW, "one row block per wave");
 };
 
-template <bool GDN2, int DK, int C, int VT, typename Tin>
+// DECAY: the chunk operands carry a decay (decayed queries Q^ and exit
+// decays g read from the workspace); KD: the state is stored [Dk, Dv].
+template <bool DECAY, int DK, int C, int VT, typename Tin>
 struct ScanRegs {
   using G = ScanCfg<DK, C, VT, Tin>;
   Frag<DK, Tin> wk, qh;      // the wave's 16 rows of Wk and of the queries
@@ -736,7 +757,7 @@ struct ScanRegs {
     const size_t n = (size_t)bh * nchunks + j;
     const size_t koff = n * C * DK + (size_t)tb * 16 * DK;
     wk.load_global(wb.wk + koff);
-    if constexpr (GDN2) {
+    if constexpr (DECAY) {
       qh.load_global(wb.qh + koff);
     } else {
       const int row = min(tb * 16 + (int)(threadIdx.x & 15), min(C, T - j * C) - 1);
@@ -757,16 +778,16 @@ struct ScanRegs {
     for (int d = 0; d < G::DPW; ++d) {
       const int db = min(wave * G::DPW + d, G::DB - 1);
       x[d].load_global(wb.xp + n * C * DK + (size_t)db * 16 * C);
-      if constexpr (GDN2) gd[d] = wb.g[n * DK + db * 16 + (threadIdx.x & 15)];
+      if constexpr (DECAY) gd[d] = wb.g[n * DK + db * 16 + (threadIdx.x & 15)];
     }
   }
 };
 
-template <bool GDN2, int DK, int C, int VT, typename Tin>
+template <bool DECAY, bool KD, int DK, int C, int VT, typename Tin>
 __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
                                                       WyBufs<Tin> wb) {
   using G = ScanCfg<DK, C, VT, Tin>;
-  using R = ScanRegs<GDN2, DK, C, VT, Tin>;
+  using R = ScanRegs<DECAY, DK, C, VT, Tin>;
   constexpr int LDK = G::LDK, LDW = G::LDW, LDO = G::LDO, TB = G::TB, VB = G::VB,
                 DB = G::DB, DPW = G::DPW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
@@ -790,7 +811,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   // Persistent state slice S[v][dk] (v in this tile), fp32, MFMA layout.
   // OSDN stores the state [Dv][Dk]; GDN-2 stores it [Dk][Dv].
   auto sidx = [&](int vv, int kk) -> size_t {
-    return GDN2 ? ((size_t)bh * DK + kk) * Dv + v0 + vv
+    return KD ? ((size_t)bh * DK + kk) * Dv + v0 + vv
                 : ((size_t)bh * Dv + v0 + vv) * DK + kk;
   };
   f32x4 Sacc[G::NS];
@@ -899,7 +920,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
 #pragma unroll
           for (int vb = 0; vb < VB; ++vb) {
             f32x4& acc = Sacc[vb * DPW + d];
-            if constexpr (GDN2) {
+            if constexpr (DECAY) {
 #pragma unroll
               for (int i = 0; i < 4; ++i) acc[i] *= cur.gd[d];
             }
@@ -974,27 +995,30 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     return -1;
   } else {
     constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
+    constexpr bool kGated = std::is_same<V, OsdnGatedVariant>::value;
+    constexpr bool kDecay = kDecayVariant<V>;
     const int BH = a.B * a.H, nch = (a.T + C - 1) / C;
     if (BH == 0) return 0;
-    const WyBufs<Tin> wb = wy_bufs<Tin>(a.ws, BH, nch, C, DK, DV, kGdn2);
+    const WyBufs<Tin> wb = wy_bufs<Tin>(a.ws, BH, nch, C, DK, DV, kDecay);
     if (nch > 0) {
       // persistent grid: a few workgroups per compute unit at most
       const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<V, DK, DV, C, Tin>());
-      ktimer_before(s, kGdn2 ? "gdn2_prep"
-                             : std::is_same<V, OsdnFusedVariant>::value ? "wy_prep_fused"
-                                                                       : "wy_prep");
+      ktimer_before(s, kGdn2    ? "gdn2_prep"
+                       : kGated ? "gated_prep"
+                       : std::is_same<V, OsdnFusedVariant>::value ? "wy_prep_fused"
+                                                                  : "wy_prep");
       hipLaunchKernelGGL((wy_prep_kernel<V, DK, DV, C, Tin>), dim3(grid),
                          dim3(512), 0, s, a, nch, wb);
       ktimer_after(s);
       const int rc = (int)hipGetLastError();
       if (rc) return rc;
     }
-    ktimer_before(s, kGdn2 ? "gdn2_scan" : "wy_scan");
+    ktimer_before(s, kGdn2 ? "gdn2_scan" : kGated ? "gated_scan" : "wy_scan");
     if (pick_vt(BH, DV) == 32)
-      hipLaunchKernelGGL((wy_scan_kernel<kGdn2, DK, C, 32, Tin>),
+      hipLaunchKernelGGL((wy_scan_kernel<kDecay, kGdn2, DK, C, 32, Tin>),
                          dim3(BH * (DV / 32)), dim3(256), 0, s, a, nch, wb);
     else
-      hipLaunchKernelGGL((wy_scan_kernel<kGdn2, DK, C, 16, Tin>),
+      hipLaunchKernelGGL((wy_scan_kernel<kDecay, kGdn2, DK, C, 16, Tin>),
                          dim3(BH * (DV / 16)), dim3(256), 0, s, a, nch, wb);
     ktimer_after(s);
     return (int)hipGetLastError();
@@ -1049,6 +1073,10 @@ int launch_osdn_chunk(const ChunkArgs& a, hipStream_t s) {
 
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s) {
   return launch_variant<Gdn2Variant>(a, s);
+}
+
+int launch_osdn_gated_chunk(const ChunkArgs& a, hipStream_t s) {
+  return launch_variant<OsdnGatedVariant>(a, s);
 }
 
 int launch_osdn_fused(const ChunkArgs& a, hipStream_t s) {

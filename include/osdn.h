@@ -208,6 +208,42 @@ int gdn2_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
 size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
 
+/* 1 if (Dk, Dv, chunk, dtype) has a gated-OSDN kernel instance, else 0 (the
+ * sizes of gdn2_forward_supported). */
+int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype);
+
+/* Device workspace, in bytes, that osdn_gated_forward needs (0 if the sizes
+ * are invalid or the call needs none): the preconditioned keys ([B,H,T,Dk]
+ * in the storage dtype, rounded up to 256 bytes), then scratch shared by the
+ * two phases (the larger of osdn_precond_workspace_bytes and
+ * gdn2_forward_workspace_bytes). */
+size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
+                                          int chunk, int dtype);
+
+/*
+ * OSDN on a backbone with per-key-channel decay ([OSDN-it] section 4 runs
+ * OSDN on Gated DeltaNet and Kimi Delta Attention backbones; the pages do not
+ * print the combined rule). Reading taken: the decay acts on the memory
+ * before the token's OSDN step, and the preconditioner learner is unchanged:
+ *   S_t = S_{t-1} Diag(alpha_t) + beta_t (v_t - S_{t-1} Diag(alpha_t) k_t) k~_t^T
+ *   o_t = scale * S_t q_t,  k~_t = d_t*k_t,  d as in osdn_forward,
+ * alpha_t = exp(log_alpha_t) per key channel (a per-head scalar decay is the
+ * case of equal channels). Arguments as in osdn_forward, plus
+ *   log_alpha [B,H,T,Dk] fp32 (required; <= 0 for a decay; its sum over one
+ *             chunk must stay above about -80 per channel, as for
+ *             gdn2_forward).
+ * State [B,H,Dv,Dk] as in osdn_forward; S_T may be exactly S0 and d_T exactly
+ * d0. Runs phase 1 (writing the preconditioned keys into the workspace), then
+ * the chunked engine with the decay absorbed into the keys.
+ */
+int osdn_gated_forward(int B, int H, int T, int Dk, int Dv, int chunk,
+                       int dtype, const void* q, const void* k, const void* v,
+                       const float* beta, const float* r, float eta,
+                       const float* log_alpha, const float* d0,
+                       const float* S0, float scale, void* o, float* S_T,
+                       float* d_T, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /*
  * Recurrent decode ([OSDN-it] section 1: constant-memory recurrent inference;
  * same token rule as osdn_forward): advances T tokens (typically 1) through
@@ -220,19 +256,23 @@ size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
  *   beta     [B,H,T]     fp32             (required)
  *   r        [B,H,T]     fp32             (NULL: no forgetting gate)
  *   eta      step size of the preconditioner learner
+ *   log_alpha [B,H,T,Dk] fp32 per-key-channel decay of a gated backbone,
+ *            applied to the state before each token's step as in
+ *            osdn_gated_forward (NULL: no decay, plain OSDN)
  *   S        [B,H,Dv,Dk] fp32 IN/OUT: the state before the tokens on entry,
  *                        after them on return (required)
  *   d        [B,H,Dk]    fp32 IN/OUT: the preconditioner, likewise (required)
  *   scale    readout scale
  *   o        [B,H,T,Dv]  dtype            (required)
- * Output o_t and the final S, d equal osdn_forward(..., d0 = d, S0 = S) up to
- * rounding. T = 0 leaves S and d untouched. S, d and o must not overlap each
+ * Output o_t and the final S, d equal osdn_forward(..., d0 = d, S0 = S) (or
+ * osdn_gated_forward with log_alpha) up to rounding. T = 0 leaves S and d untouched. S, d and o must not overlap each
  * other or any input (OSDN_ERR_ALIASING). Dk, Dv in {32, 64, 128}.
  */
 int osdn_decode(int B, int H, int T, int Dk, int Dv, int dtype,
                 const void* q, const void* k, const void* v,
                 const float* beta, const float* r, float eta,
-                float* S, float* d, float scale, void* o, void* stream);
+                const float* log_alpha, float* S, float* d, float scale,
+                void* o, void* stream);
 
 /*
  * Gated DeltaNet-2 recurrent decode ([GDN2-it] method part 1, token form):
@@ -263,7 +303,8 @@ void osdn_kernel_timing(int enable);
  * fails. Kernel names: precond_prep, precond_chain, precond_ktilde,
  * precond_rho (phase 1), wy_prep, wy_prep_fused (phase 2 forming the
  * preconditioned keys itself), wy_scan (phase 2), gdn2_prep, gdn2_scan
- * (GDN-2), osdn_decode, gdn2_decode (recurrent decode).
+ * (GDN-2), gated_prep, gated_scan (OSDN on a decaying backbone),
+ * osdn_decode, gdn2_decode (recurrent decode).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

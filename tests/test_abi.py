@@ -39,7 +39,9 @@ def test_header_declares_entry_points():
               "osdn_precond_workspace_bytes",
               "osdn_chunk_forward", "gdn2_forward", "gdn2_forward_supported",
               "osdn_chunk_workspace_bytes", "gdn2_forward_workspace_bytes",
-              "osdn_decode", "gdn2_decode"):
+              "osdn_decode", "gdn2_decode", "osdn_gated_forward",
+              "osdn_gated_forward_workspace_bytes",
+              "osdn_gated_forward_supported"):
         assert n in names
 
 
@@ -216,13 +218,13 @@ def test_decode_error_paths():
     L = osdn.load_library()
     P = ctypes.c_void_p
     I, F = ctypes.c_int, ctypes.c_float
-    L.osdn_decode.argtypes = [I] * 6 + [P, P, P, P, P, F, P, P, F, P, P]
+    L.osdn_decode.argtypes = [I] * 6 + [P, P, P, P, P, F, P, P, P, F, P, P]
     L.gdn2_decode.argtypes = [I] * 6 + [P] * 7 + [F, P, P]
 
     def dec(B=2, T=1, Dk=32, q=0x10000, beta=0x40000, S=0x200000, d=0x300000,
-            o=0x50000, r=None):
+            o=0x50000, r=None, la=None):
         return L.osdn_decode(B, 1, T, Dk, 32, 1, q, 0x20000, 0x30000, beta, r,
-                             0.1, S, d, 1.0, o, None)
+                             0.1, la, S, d, 1.0, o, None)
     assert dec(q=None) == NULL_ARG
     assert dec(S=None) == NULL_ARG
     assert dec(d=None) == NULL_ARG
@@ -232,6 +234,7 @@ def test_decode_error_paths():
     assert dec(d=0x200000 + 64) == ALIASING      # d inside the state
     assert dec(o=0x300000) == ALIASING           # o over d
     assert dec(r=0x200000) == ALIASING           # gate over the state
+    assert dec(la=0x300000 + 16) == ALIASING     # decay over d
     # nothing to do: T = 0 or B = 0 needs no pointer
     assert dec(T=0, q=None, S=None, d=None, o=None, beta=None) == OK
     assert dec(B=0, q=None, S=None, d=None, o=None, beta=None) == OK
@@ -246,3 +249,36 @@ def test_decode_error_paths():
     assert gd(S=0x70000) == ALIASING             # state over b
     assert gd(o=0x200000 + 8) == ALIASING        # o inside the state
     assert gd(T=0, la=None, S=None, o=None) == OK
+
+
+@needs_lib
+def test_gated_forward_error_paths_and_workspace():
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    I, F = ctypes.c_int, ctypes.c_float
+    L.osdn_gated_forward.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, P, F, P,
+                                                P, P, P, ctypes.c_size_t, P])
+
+    def call(T=64, Dk=32, C=16, la=0x60000, o=0x50000, ST=None, S0=None,
+             ws=0x100000, wsb=1 << 20):
+        return L.osdn_gated_forward(1, 1, T, Dk, 32, C, 1, 0x10000, 0x20000,
+                                    0x30000, 0x40000, None, 0.1, la, None, S0,
+                                    1.0, o, ST, None, ws, wsb, None)
+    assert call(la=None) == NULL_ARG
+    assert call(T=-1) == BAD_DIMS
+    assert call(Dk=48) == UNSUPPORTED
+    assert call(Dk=32, C=8) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(o=0x60000 + 64) == ALIASING      # o over log alpha
+    assert call(S0=0x200000, ST=0x200000 + 4) == ALIASING
+    assert call(ws=0x30000) == ALIASING          # workspace over v
+    # preconditioned keys, then the larger of the two scratch regions
+    def r256(n):
+        return (n + 255) // 256 * 256
+    kt = r256(64 * 4096 * 128 * 2)
+    p1 = L.osdn_precond_workspace_bytes(4, 16, 4096, 128, 1)
+    p2 = L.gdn2_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1)
+    assert L.osdn_gated_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) \
+        == kt + max(p1, p2)
+    assert L.osdn_gated_forward_supported(128, 128, 64, 1) == 1
+    assert L.osdn_gated_forward_supported(128, 128, 8, 1) == 0

@@ -19,6 +19,11 @@ def test_shapes_and_dtypes_small(w):
         assert (x["r"] is not None) == w.apf
         b = x["beta"].double()
         assert torch.all((b > 0) & (b < 1))
+        if w.decay:
+            assert x["log_alpha"].shape == (1, 2, ws.T, w.Dk)
+            assert torch.all(x["log_alpha"] < 0)
+        else:
+            assert "log_alpha" not in x
     else:
         assert x["log_alpha"].shape == (1, 2, ws.T, w.Dk)
         assert torch.all(x["log_alpha"] < 0)

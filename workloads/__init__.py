@@ -21,6 +21,8 @@ Workloads (dims B, H, T, Dk, Dv and chunk C):
    128, 16, 1, 128, 128; bf16; gate on; a drawn initial state, S0 =
    N(0,1)/sqrt(Dk) and d0 = U(0.5, 1.5).
 7. GDN-2 recurrent decode, same shape and gates as 5, S0 = N(0,1)/sqrt(Dk).
+8. OSDN on a per-channel-decay backbone at the 1.3B-layer shape: as 3, plus
+   log alpha = -0.1 softplus(N(0,1)) per key channel (the decay of 5).
 
 Seeds: workload i draws from numpy SeedSequence(i - 1); each tensor comes
 from its own spawned child, in the fixed order q, k, v, beta, r, alpha, b, w,
@@ -50,6 +52,7 @@ class Workload:
     keys: str = "gauss"  # "gauss" or "pool" (multi-key recall)
     seed: int = 0
     state: bool = False  # draw an initial state S0 (and d0 for OSDN)
+    decay: bool = False  # OSDN on a decaying backbone: log alpha per channel
 
     @property
     def tokens(self):
@@ -72,6 +75,8 @@ WORKLOADS = [
              apf=True, seed=5, state=True),
     Workload("gdn2-decode", "gdn2", 128, 16, 1, 128, 128, 64, "bf16", seed=6,
              state=True),
+    Workload("osdn-gated-1.3b", "osdn", 4, 16, 4096, 128, 128, 64, "bf16",
+             apf=True, seed=7, decay=True),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}
@@ -151,6 +156,9 @@ def make_inputs(w: Workload):
         r = (_store(_sigmoid(ch[4].normal(2.0, 0.5, (B, H, T))), "f32")
              if w.apf else None)
         out.update(beta=beta, r=r, eta=w.eta, d0=None)
+        if w.decay:
+            la = -0.1 * _softplus(ch[5].standard_normal((B, H, T, Dk)))
+            out["log_alpha"] = _store(la, "f32")
         if w.state:
             out["S0"] = _store(ch[8].standard_normal((B, H, Dv, Dk))
                                / np.sqrt(Dk), "f32")
