@@ -123,9 +123,12 @@ def flops_per_token_head(w):
     return 6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3.0
 
 
+LAUNCHES_PER_STEP = {}
+
+
 def timed_steps(step, args):
     """Warm up, then time exactly args.steps steps (synchronised on both
-    sides); returns the wall time per step (ms) and {kernel: mean ms}. The
+    sides); returns the wall time per step (ms) and {kernel: ms per step}. The
     per-kernel durations come from a second pass of the same steps with the
     library's event timing on, so that the events do not weigh on the wall
     time."""
@@ -143,21 +146,28 @@ def timed_steps(step, args):
         step()
     torch.cuda.synchronize()
     osdn.kernel_timing(False)
-    kt = {n: ms for n, (cnt, ms) in osdn.kernel_times().items()}
+    # per step: the summed duration of each kernel's launches (a kernel run
+    # over time pieces launches several times per step)
+    rec = osdn.kernel_times()
+    kt = {n: ms * cnt / args.steps for n, (cnt, ms) in rec.items()}
+    global LAUNCHES_PER_STEP
+    LAUNCHES_PER_STEP = {n: cnt / args.steps for n, (cnt, ms) in rec.items()}
     return wall * 1e3 / args.steps, kt
 
 
 def roofline(w, kt, kb):
-    """Roofline entry of the dominant (longest) kernel: algorithmic bytes per
-    launch over its mean launch duration, against the HBM peak."""
+    """Roofline entry of the dominant (longest) kernel: its algorithmic bytes
+    per step over its summed launch durations per step (= bytes per launch
+    over the mean launch duration), against the HBM peak."""
     th = w.B * w.H * w.T
     dom = max(kt, key=lambda n: kt[n])
-    alg = kb[dom] * th
-    achieved = alg / (kt[dom] * 1e-3) / 1e9
+    n_l = LAUNCHES_PER_STEP.get(dom, 1.0)
+    alg = kb[dom] * th / n_l
+    achieved = alg / (kt[dom] / n_l * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": dom, "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(dom, w.name), "alg_bytes": alg,
-            "ms": kt[dom]}
+            "ms": kt[dom] / n_l, "launches_per_step": n_l}
 
 
 def cpu_baseline(w, inp, budget_s=12.0):
