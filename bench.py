@@ -41,6 +41,7 @@ _KERNEL_SOURCES = {
     "gdn2_prep": ["wy_chunk.hip"],
     "gdn2_scan": ["wy_chunk.hip"],
     "gated_prep": ["wy_chunk.hip"],
+    "gated_prep_fused": ["wy_chunk.hip"],
     "gated_scan": ["wy_chunk.hip"],
     "osdn_decode": ["decode.hip"],
     "gdn2_decode": ["decode.hip"],
@@ -112,6 +113,10 @@ def kernel_bytes_per_token_head(w, apf=False):
         # q, k, k~, v, beta, log alpha -> Wk, X', U, P, Q^, exit decay
         "gated_prep": (3 * dk + dv) * s + 4 + 4 * dk + frags_g,
         "gated_scan": frags_g + dv * s,
+        # q, k, v, beta, log alpha, log gate prefix, g, d entries -> Wk, X',
+        # U, P, Q^, exit decay
+        "gated_prep_fused": (2 * dk + dv) * s + 4 + 4 * dk
+        + 4 * (C1 + 4.0) / C1 + 4 + dent + frags_g,
     }
 
 

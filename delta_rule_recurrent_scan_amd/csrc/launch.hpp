@@ -87,6 +87,12 @@ int launch_osdn_fused(const ChunkArgs& a, hipStream_t s);
 // OSDN on a per-channel-decay backbone: ktilde, beta and log_alpha used,
 // state [B,H,Dv,Dk]; workspace as for GDN-2 (wy_workspace_bytes(..., 1)).
 int launch_osdn_gated_chunk(const ChunkArgs& a, hipStream_t s);
+// The same forming K~ inside the engine from prec / pdent (chunk ==
+// kPrecondChunk); workspace: the phase-1 scratch stays live beside it.
+int launch_osdn_gated_fused(const ChunkArgs& a, hipStream_t s);
+// Whether the fused gated variant has an instance for (Dk, Dv, dtype) at
+// chunk kPrecondChunk (its LDS layout fits).
+bool gated_fused_supported(int Dk, int Dv, int bf16);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_decode(const DecodeArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);

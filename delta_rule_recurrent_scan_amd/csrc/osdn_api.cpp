@@ -46,6 +46,13 @@ bool aliasing_ok(const Range (&outs)[NO], const Range (&ins)[NI],
   return true;
 }
 
+// The gated forward forms K~ inside the engine at chunk 64 where that layout
+// fits; otherwise it goes through the preconditioned keys in the workspace.
+bool gated_fused(int Dk, int Dv, int chunk, int dtype) {
+  return chunk == osdn::kPrecondChunk &&
+         osdn::gated_fused_supported(Dk, Dv, dtype == OSDN_BF16);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,7 +114,7 @@ size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
   // chunk = 64: phase 2 forms K~ itself from the phase-1 records, so both
   // scratch regions are live at once; otherwise the preconditioned keys,
   // then scratch shared by the two phases
-  if (chunk == osdn::kPrecondChunk) return p1 + p2;
+  if (gated_fused(Dk, Dv, chunk, dtype)) return p1 + p2;
   return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
 }
 
@@ -339,7 +346,10 @@ size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
   const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
   const size_t p2 = chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 1);
   if (p1 == 0 && p2 == 0) return 0;
-  // the preconditioned keys, then scratch shared by the two phases
+  // chunk = 64: the engine forms K~ from the phase-1 records, so both scratch
+  // regions are live at once; otherwise the preconditioned keys, then
+  // scratch shared by the two phases
+  if (gated_fused(Dk, Dv, chunk, dtype)) return p1 + p2;
   return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
 }
 
@@ -375,17 +385,35 @@ int osdn_gated_forward(int B, int H, int T, int Dk, int Dv, int chunk,
   if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
   hipStream_t s = (hipStream_t)stream;
   unsigned char* wsb = static_cast<unsigned char*>(workspace);
-  const size_t kt_bytes = round256(BH * T * Dk * es);
-  void* pws = wsb + kt_bytes;
-  osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                       workspace, d_T, pws, nullptr, nullptr};
-  int rc = osdn::launch_precond_scan(pa, s);
-  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
-  if (rc != 0) return OSDN_ERR_HIP;
-  osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                     workspace, v, beta, S0, scale, o, S_T,
-                     log_alpha, nullptr, nullptr, pws};
-  rc = osdn::launch_osdn_gated_chunk(ca, s);
+  int rc;
+  if (gated_fused(Dk, Dv, chunk, dtype)) {
+    // phase-1 records and entry values of d, then the engine's operands
+    const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
+    osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                         nullptr, d_T, wsb, nullptr, nullptr};
+    rc = osdn::launch_precond_scan(pa, s);
+    if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+    if (rc != 0) return OSDN_ERR_HIP;
+    const int nch = (T + chunk - 1) / chunk;
+    const float* prec = reinterpret_cast<const float*>(wsb);
+    const float* pdent = prec + BH * (size_t)nch * osdn::kRecStride;
+    osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                       nullptr, v, beta, S0, scale, o, S_T,
+                       log_alpha, nullptr, nullptr, wsb + p1, prec, pdent};
+    rc = osdn::launch_osdn_gated_fused(ca, s);
+  } else {
+    const size_t kt_bytes = round256(BH * T * Dk * es);
+    void* pws = wsb + kt_bytes;
+    osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
+                         workspace, d_T, pws, nullptr, nullptr};
+    rc = osdn::launch_precond_scan(pa, s);
+    if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+    if (rc != 0) return OSDN_ERR_HIP;
+    osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
+                       workspace, v, beta, S0, scale, o, S_T,
+                       log_alpha, nullptr, nullptr, pws};
+    rc = osdn::launch_osdn_gated_chunk(ca, s);
+  }
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }

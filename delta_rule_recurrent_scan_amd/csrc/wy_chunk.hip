@@ -59,11 +59,20 @@ struct OsdnFusedVariant {};
 // x_t = k~_t/gamma_t, value beta_t v_t, query gamma_t*q_t, exit keys
 // k~_t*gamma_C/gamma_t and exit decay gamma_C; the state is stored [Dv, Dk].
 struct OsdnGatedVariant {};
+// The same with the preconditioned keys formed in the engine, as for
+// OsdnFusedVariant (chunk == the phase-1 chunk); K~ is formed first, then
+// the decay pass turns it into K~/gamma.
+struct OsdnGatedFusedVariant {};
 
 // Variants whose chunk operands carry a per-channel decay.
 template <class V>
-constexpr bool kDecayVariant =
-    std::is_same<V, Gdn2Variant>::value || std::is_same<V, OsdnGatedVariant>::value;
+constexpr bool kDecayVariant = std::is_same<V, Gdn2Variant>::value ||
+                               std::is_same<V, OsdnGatedVariant>::value ||
+                               std::is_same<V, OsdnGatedFusedVariant>::value;
+// Variants that form K~ from the raw keys and the phase-1 records.
+template <class V>
+constexpr bool kFusedVariant = std::is_same<V, OsdnFusedVariant>::value ||
+                               std::is_same<V, OsdnGatedFusedVariant>::value;
 
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
 // storage dtype: Wk as 16-row A fragments (row block tb at tb*16*Dk); the
@@ -155,7 +164,7 @@ struct RawTile<float> {
 template <class V, int DK, int DV, int C, typename Tin>
 struct PrepCfg {
   static constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
-  static constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
+  static constexpr bool kFused = kFusedVariant<V>;
   static constexpr int NW = 8, NT = 512;
   static constexpr int PAD = sizeof(Tin) == 2 ? 8 : 4;
   static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD;
@@ -190,7 +199,10 @@ struct PrepCfg {
   static constexpr bool kLaInGram = !kLaOwn && oAb + kLaBytes <= oG;
   static constexpr size_t oLa = kLaOwn ? oEnd : oAb;
   static constexpr size_t bytes = kLaOwn ? oEnd + kLaBytes : oEnd;
-  static constexpr bool fits = bytes <= 163840 && (kLaOwn || kLaInGram);
+  // (the fused decay variant forms L in the Gram buffer before its decay
+  // pass, so its log alpha needs a region of its own)
+  static constexpr bool fits =
+      bytes <= 163840 && (kLaOwn || (kLaInGram && !(kFused && kDecayVariant<V>)));
   // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
   static constexpr int TPC = NT / DK;
   static constexpr int TPT = C / TPC > 0 ? C / TPC : 1;
@@ -202,7 +214,7 @@ template <class V, int DK, int DV, int C, typename Tin>
 struct PrepRegs {
   using G = PrepCfg<V, DK, DV, C, Tin>;
   static constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
-  static constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
+  static constexpr bool kFused = kFusedVariant<V>;
   static constexpr int VEC = G::VEC;
   static constexpr int NKB = C * (DK / VEC), NVB = C * (DV / VEC);
   static constexpr int NLK = (NKB + G::NT - 1) / G::NT;
@@ -350,8 +362,10 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
                                                       WyBufs<Tin> wb) {
   using G = PrepCfg<V, DK, DV, C, Tin>;
   constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
-  constexpr bool kFused = std::is_same<V, OsdnFusedVariant>::value;
+  constexpr bool kFused = kFusedVariant<V>;
   constexpr bool kDecay = kDecayVariant<V>;
+  static_assert(!(kFused && kDecay) || G::kLaOwn,
+                "the fused decay variant stages log alpha in a region of its own");
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDS16 = G::LDS16,
                 TB = G::TB, DB = G::DB, VBT = G::VBT, NW = G::NW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
@@ -392,7 +406,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     regs.store(Ys, Xs, Qs, Zs, smem);
     // the next chunk's raw operands (the last chunk again at the end)
     regs.load(p, chunk_of(min(pos + (int)gridDim.x, total - 1)), nchunks);
-    if constexpr (kDecay) {
+    auto decay_pass = [&]() {
       // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
       // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
       // staged log alpha into the inclusive prefix lambda in place and give
@@ -460,7 +474,8 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
           if ((cc >> 4) > (rr >> 4)) Tb[rr * LDC + cc] = zero;
         }
       }
-    }
+    };
+    if constexpr (kDecay && !kFused) decay_pass();
     __syncthreads();
     if constexpr (kFused) {
       // ---- K~ = (P d^T + L A) * K in place over the raw keys --------------
@@ -493,6 +508,12 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         }
       }
       __syncthreads();
+      if constexpr (kDecay) {
+        // the decay pass turns the preconditioned keys just formed into
+        // K~/gamma (and decays the read keys and queries)
+        decay_pass();
+        __syncthreads();
+      }
     }
 
     // ---- Gram A, scores P, diagonal blocks of T; X' fragments ---------------
@@ -995,7 +1016,8 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     return -1;
   } else {
     constexpr bool kGdn2 = std::is_same<V, Gdn2Variant>::value;
-    constexpr bool kGated = std::is_same<V, OsdnGatedVariant>::value;
+    constexpr bool kGated = std::is_same<V, OsdnGatedVariant>::value ||
+                            std::is_same<V, OsdnGatedFusedVariant>::value;
     constexpr bool kDecay = kDecayVariant<V>;
     const int BH = a.B * a.H, nch = (a.T + C - 1) / C;
     if (BH == 0) return 0;
@@ -1004,6 +1026,7 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
       // persistent grid: a few workgroups per compute unit at most
       const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<V, DK, DV, C, Tin>());
       ktimer_before(s, kGdn2    ? "gdn2_prep"
+                       : std::is_same<V, OsdnGatedFusedVariant>::value ? "gated_prep_fused"
                        : kGated ? "gated_prep"
                        : std::is_same<V, OsdnFusedVariant>::value ? "wy_prep_fused"
                                                                   : "wy_prep");
@@ -1027,7 +1050,7 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
 
 template <class V, int DK, int DV, typename Tin>
 static int launch_dv(const ChunkArgs& a, hipStream_t s) {
-  if constexpr (std::is_same<V, OsdnFusedVariant>::value) {
+  if constexpr (kFusedVariant<V>) {
     return a.chunk == kPrecondChunk ? launch_cfg<V, DK, DV, kPrecondChunk, Tin>(a, s)
                                     : -1;
   }
@@ -1079,6 +1102,11 @@ int launch_osdn_gated_chunk(const ChunkArgs& a, hipStream_t s) {
   return launch_variant<OsdnGatedVariant>(a, s);
 }
 
+int launch_osdn_gated_fused(const ChunkArgs& a, hipStream_t s) {
+  if (a.chunk != kPrecondChunk) return -1;
+  return launch_variant<OsdnGatedFusedVariant>(a, s);
+}
+
 int launch_osdn_fused(const ChunkArgs& a, hipStream_t s) {
   if (a.chunk != kPrecondChunk) return -1;
   return launch_variant<OsdnFusedVariant>(a, s);
@@ -1102,6 +1130,33 @@ static bool fits_dk(int Dv, int chunk) {
     case 32: return fits_dv<DK, 32, Tin>(chunk);
     case 64: return fits_dv<DK, 64, Tin>(chunk);
     case 128: return fits_dv<DK, 128, Tin>(chunk);
+  }
+  return false;
+}
+
+template <int DK, typename Tin>
+static bool gated_fused_fits(int Dv) {
+  switch (Dv) {
+    case 32: return PrepCfg<OsdnGatedFusedVariant, DK, 32, kPrecondChunk, Tin>::fits;
+    case 64: return PrepCfg<OsdnGatedFusedVariant, DK, 64, kPrecondChunk, Tin>::fits;
+    case 128: return PrepCfg<OsdnGatedFusedVariant, DK, 128, kPrecondChunk, Tin>::fits;
+  }
+  return false;
+}
+
+bool gated_fused_supported(int Dk, int Dv, int bf16) {
+  if (bf16) {
+    switch (Dk) {
+      case 32: return gated_fused_fits<32, __bf16>(Dv);
+      case 64: return gated_fused_fits<64, __bf16>(Dv);
+      case 128: return gated_fused_fits<128, __bf16>(Dv);
+    }
+  } else {
+    switch (Dk) {
+      case 32: return gated_fused_fits<32, float>(Dv);
+      case 64: return gated_fused_fits<64, float>(Dv);
+      case 128: return gated_fused_fits<128, float>(Dv);
+    }
   }
   return false;
 }

@@ -213,10 +213,12 @@ size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
 int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype);
 
 /* Device workspace, in bytes, that osdn_gated_forward needs (0 if the sizes
- * are invalid or the call needs none): the preconditioned keys ([B,H,T,Dk]
- * in the storage dtype, rounded up to 256 bytes), then scratch shared by the
- * two phases (the larger of osdn_precond_workspace_bytes and
- * gdn2_forward_workspace_bytes). */
+ * are invalid or the call needs none). chunk = 64, where the engine's layout
+ * with the preconditioned keys formed inside it fits (bf16 at every
+ * supported Dk, Dv): osdn_precond_workspace_bytes followed by
+ * gdn2_forward_workspace_bytes. Otherwise the preconditioned keys
+ * ([B,H,T,Dk] in the storage dtype, rounded up to 256 bytes), then scratch
+ * shared by the two phases (the larger of the two). */
 size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                           int chunk, int dtype);
 
@@ -233,8 +235,9 @@ size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
  *             chunk must stay above about -80 per channel, as for
  *             gdn2_forward).
  * State [B,H,Dv,Dk] as in osdn_forward; S_T may be exactly S0 and d_T exactly
- * d0. Runs phase 1 (writing the preconditioned keys into the workspace), then
- * the chunked engine with the decay absorbed into the keys.
+ * d0. Runs phase 1, then the chunked engine with the decay absorbed into the
+ * keys (at chunk 64 the engine forms the preconditioned keys itself from the
+ * phase-1 records; otherwise phase 1 writes them into the workspace).
  */
 int osdn_gated_forward(int B, int H, int T, int Dk, int Dv, int chunk,
                        int dtype, const void* q, const void* k, const void* v,
@@ -303,7 +306,8 @@ void osdn_kernel_timing(int enable);
  * fails. Kernel names: precond_prep, precond_chain, precond_ktilde,
  * precond_rho (phase 1), wy_prep, wy_prep_fused (phase 2 forming the
  * preconditioned keys itself), wy_scan (phase 2), gdn2_prep, gdn2_scan
- * (GDN-2), gated_prep, gated_scan (OSDN on a decaying backbone),
+ * (GDN-2), gated_prep, gated_prep_fused, gated_scan (OSDN on a decaying
+ * backbone),
  * osdn_decode, gdn2_decode (recurrent decode).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);

@@ -272,13 +272,17 @@ def test_gated_forward_error_paths_and_workspace():
     assert call(o=0x60000 + 64) == ALIASING      # o over log alpha
     assert call(S0=0x200000, ST=0x200000 + 4) == ALIASING
     assert call(ws=0x30000) == ALIASING          # workspace over v
-    # preconditioned keys, then the larger of the two scratch regions
+    # chunk 64 (bf16): both scratch regions, the engine forms K~ itself;
+    # other chunks: the preconditioned keys, then the larger of the two
     def r256(n):
         return (n + 255) // 256 * 256
     kt = r256(64 * 4096 * 128 * 2)
     p1 = L.osdn_precond_workspace_bytes(4, 16, 4096, 128, 1)
     p2 = L.gdn2_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1)
     assert L.osdn_gated_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) \
-        == kt + max(p1, p2)
+        == p1 + p2
+    p2b = L.gdn2_forward_workspace_bytes(4, 16, 4096, 128, 128, 32, 1)
+    assert L.osdn_gated_forward_workspace_bytes(4, 16, 4096, 128, 128, 32, 1) \
+        == kt + max(p1, p2b)
     assert L.osdn_gated_forward_supported(128, 128, 64, 1) == 1
     assert L.osdn_gated_forward_supported(128, 128, 8, 1) == 0
