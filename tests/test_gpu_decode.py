@@ -78,7 +78,7 @@ def check(got, ref, dtype, where):
 OSDN_CASES = [(dk, dv, T, dt, apf)
               for dk, dv in [(128, 128), (32, 64), (64, 32)]
               for T, dt, apf in [(1, "bf16", True), (5, "bf16", False),
-                                 (3, "f32", True)]]
+                                 (3, "f32", True)]] + [(128, 64, 40, "f32", True)]
 
 
 @pytest.mark.parametrize("dk,dv,T,dt,apf", OSDN_CASES,
@@ -148,7 +148,7 @@ def test_osdn_decode_rejects_state_aliasing_input():
 
 
 GDN2_CASES = [(128, 128, 1, "bf16"), (128, 128, 4, "bf16"), (32, 64, 2, "f32"),
-              (64, 32, 3, "bf16"), (64, 128, 1, "f32")]
+              (64, 32, 3, "bf16"), (64, 128, 1, "f32"), (128, 64, 40, "f32")]
 
 
 @pytest.mark.parametrize("dk,dv,T,dt", GDN2_CASES,

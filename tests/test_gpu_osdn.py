@@ -358,3 +358,21 @@ def test_residual_ratio_full_size_sampled(name):
     for b, h in [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]:
         check_rho(rho, qg, inp, "%s b=%d h=%d" % (name, b, h),
                   (slice(b, b + 1), slice(h, h + 1)))
+
+
+def test_forgetting_gate_zero_and_one():
+    """Gate values of exactly 0 (full forgetting of the preconditioner) and
+    exactly 1 inside chunks, at a chunk's first and last token and for a
+    whole chunk: the chunked phase 1 takes log r with r clamped to 1e-30, a
+    relative difference the tolerances cannot see."""
+    w = small("osdn-1.3b-apf", B=1, H=2, T=64 * 3 + 10)
+    inp = W.make_inputs(w)
+    r = inp["r"].clone()
+    for t in (0, 7, 63, 64, 100):
+        r[:, 0, t] = 0.0
+    r[:, 1, 128:192] = 0.0
+    r[:, 0, 30:50] = 1.0
+    inp["r"] = r
+    for chunk in (64, 16):
+        check(gpu_forward(inp, chunk=chunk), oracle(inp), "bf16",
+              "r in {0, 1} C=%d" % chunk)
