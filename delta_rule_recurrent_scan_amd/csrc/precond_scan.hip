@@ -660,8 +660,12 @@ static int launch_dk(const PrecondArgs& a, hipStream_t s) {
   const dim3 block(256);
   if (nch > 0) {
     ktimer_before(s, "precond_prep");
-    // persistent grid: as many workgroups as fit on the 256 compute units
-    constexpr int per_cu = (int)(163840 / G::prep_bytes);
+    // persistent grid of two workgroups per compute unit: three fit by LDS,
+    // but two measured faster (at 4096 and at 2048 chunks the prep took
+    // 65 and 36 us with two per unit against 76 and 40 us with three, and
+    // 69 and 39 us with one workgroup per chunk)
+    constexpr int per_cu = 2;
+    static_assert(per_cu * G::prep_bytes <= 163840, "LDS");
     const int total = BH * nch;
     const int grid = total < 256 * per_cu ? total : 256 * per_cu;
     hipLaunchKernelGGL((precond_prep_kernel<DK, Tin>), dim3(grid), block, 0, s,
