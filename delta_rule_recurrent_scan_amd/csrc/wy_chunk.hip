@@ -74,6 +74,12 @@ template <class V>
 constexpr bool kFusedVariant = std::is_same<V, OsdnFusedVariant>::value ||
                                std::is_same<V, OsdnGatedFusedVariant>::value;
 
+// Four consecutive elements of the storage dtype as one LDS access.
+template <typename Tin>
+struct alignas(4 * sizeof(Tin)) RawQuad {
+  Tin v[4];
+};
+
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
 // storage dtype: Wk as 16-row A fragments (row block tb at tb*16*Dk); the
 // scores P as 16-row A fragments (row block tb at tb*16*C) and X' as k-major
@@ -492,20 +498,25 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       if (tid < C) Pv[tid] = expf(lps[tid]);
       __syncthreads();
       // one job = (16-token block tb, 16-channel block db), db-major so a
-      // wave keeps its squares fragment
+      // wave keeps its squares fragment. The tile is formed transposed,
+      // (L A)^T = A^T L^T, so that a lane holds four consecutive channels of
+      // one token: its keys are read and K~ written 8 bytes at a time.
       for (int job = wave; job < TB * DB; job += NW) {
         const int db = job % DB, tb = job / DB;
         Frag<C, Tin> fl, fa;
         fl.load(Lb + tb * 16 * LDC, LDC);
         fa.load_kmajor(As + db * 16, LDK);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        mma(acc, fl, fa);
+        mma(acc, fa, fl);
+        const int t = tb * 16 + acc_col(), c0 = db * 16 + acc_row(0);
+        Tin* xe = Xs + t * LDK + c0;
+        Tin kk[4];
+        *reinterpret_cast<RawQuad<Tin>*>(kk) = *reinterpret_cast<const RawQuad<Tin>*>(xe);
+        const float pt = Pv[t];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tb * 16 + acc_row(i), c = db * 16 + acc_col();
-          Tin* xe = Xs + t * LDK + c;
-          *xe = from_f32<Tin>((Pv[t] * ds[c] + acc[i]) * to_f32(*xe));
-        }
+        for (int i = 0; i < 4; ++i)
+          kk[i] = from_f32<Tin>((pt * ds[c0 + i] + acc[i]) * to_f32(kk[i]));
+        *reinterpret_cast<RawQuad<Tin>*>(xe) = *reinterpret_cast<const RawQuad<Tin>*>(kk);
       }
       __syncthreads();
       if constexpr (kDecay) {
