@@ -558,19 +558,22 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         // straight to the workspace; the mirrored tile above the diagonal
         // is stored as zeros)
         f32x4 aa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
-        mma(aa, fy, fx);
         mma(pa, fx, fq);
         Tin* prow = wb.pp + (size_t)n * C * C;
         if (a > b) {
+          // formed transposed (X Y^T), so that a lane holds four
+          // consecutive columns of one row of A: one 8-byte LDS write
+          mma(aa, fx, fy);
+          Tin av[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = a * 16 + acc_row(i), cc = b * 16 + acc_col();
-            Ab[rr * LDC + cc] = from_f32<Tin>(aa[i]);
-          }
+          for (int i = 0; i < 4; ++i) av[i] = from_f32<Tin>(aa[i]);
+          *reinterpret_cast<RawQuad<Tin>*>(Ab + (a * 16 + acc_col()) * LDC + b * 16 + acc_row(0)) =
+              *reinterpret_cast<const RawQuad<Tin>*>(av);
           Frag<C, Tin>::store_acc_tile(prow + (size_t)a * 16 * C, b, pa);
           Frag<C, Tin>::store_acc_tile(prow + (size_t)b * 16 * C, a,
                                        f32x4{0.f, 0.f, 0.f, 0.f});
         } else {
+          mma(aa, fy, fx);
           // diagonal tile: A in fp32, transposed, strictly lower part only
           float4 col;
           col.x = acc_row(0) > acc_col() ? aa[0] : 0.f;
@@ -691,9 +694,12 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       }
     }
 
-    // ---- Wk = T diag(rs) Y and U = T diag(rs) Z, in place ----------------------
-    // One job = one 16-wide column block of Y (or Z), all row blocks; only the
-    // job's own wave reads that column block, so it is overwritten in place.
+    // ---- Wk = T diag(rs) Y and U = T diag(rs) Z --------------------------------
+    // One job = one 16-wide column block of Y (or Z), all row blocks. Wk
+    // overwrites Y in place (only the job's own wave reads that column
+    // block), formed transposed so that a lane writes four consecutive
+    // columns of one row at once; U goes from the accumulators straight to
+    // the workspace.
     const size_t uoff = (size_t)n * C * DV;
     {
       Frag<C, Tin> ft[TB];
@@ -710,17 +716,30 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         Frag<C, Tin> fm;
         fm.load_kmajor(M + ct * 16, ld);
         f32x4 acc[TB];
+        if (isU) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          mma(acc[tb], ft[tb], fm);
-        }
+          for (int tb = 0; tb < TB; ++tb) {
+            acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma(acc[tb], ft[tb], fm);
+          }
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
+          for (int tb = 0; tb < TB; ++tb)
+            RawTile<Tin>::store(acc[tb], wb.u + uoff + u_tile(tb, ct, VBT));
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            M[(tb * 16 + acc_row(i)) * ld + ct * 16 + acc_col()] = from_f32<Tin>(acc[tb][i]);
-          if (isU) RawTile<Tin>::store(acc[tb], wb.u + uoff + u_tile(tb, ct, VBT));
+          for (int tb = 0; tb < TB; ++tb) {
+            acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma(acc[tb], fm, ft[tb]);
+          }
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            Tin wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = from_f32<Tin>(acc[tb][i]);
+            *reinterpret_cast<RawQuad<Tin>*>(M + (tb * 16 + acc_col()) * ld + ct * 16 +
+                                             acc_row(0)) =
+                *reinterpret_cast<const RawQuad<Tin>*>(wv);
+          }
         }
       }
     }
