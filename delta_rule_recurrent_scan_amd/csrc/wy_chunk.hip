@@ -652,7 +652,9 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     // ---- recursive doubling, T21 = -T22 (A21 T11) ----------------------------
     // One job = one 16-wide column of T21 in one pair: that column of
     // Y = A21 T11 goes to the wave's own scratch (row-major), then the same
-    // column of T21 = -T22 Y; the right operands are read k-major.
+    // column of T21 = -T22 Y; the right operands are read k-major. Both
+    // products are formed transposed, so that a lane writes four
+    // consecutive columns of one row with one 8-byte access.
     {
       Tin* ys = Ysc + wave * (C / 2) * LDS16;
 #pragma unroll
@@ -668,11 +670,13 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
               Frag<16, Tin> fa, fb;
               fa.load(Ab + (rb + r * 16) * LDC + cb + kk, LDC);
               fb.load_kmajor(Tb + (cb + kk) * LDC + cb + c * 16, LDC);
-              mma(acc, fa, fb);
+              mma(acc, fb, fa);
             }
+            Tin yv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              ys[(r * 16 + acc_row(i)) * LDS16 + acc_col()] = from_f32<Tin>(acc[i]);
+            for (int i = 0; i < 4; ++i) yv[i] = from_f32<Tin>(acc[i]);
+            *reinterpret_cast<RawQuad<Tin>*>(ys + (r * 16 + acc_col()) * LDS16 + acc_row(0)) =
+                *reinterpret_cast<const RawQuad<Tin>*>(yv);
           }
           wave_lds_sync();
           for (int r = 0; r < nt; ++r) {
@@ -681,12 +685,14 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
               Frag<16, Tin> fa, fb;
               fa.load(Tb + (rb + r * 16) * LDC + rb + kk, LDC);
               fb.load_kmajor(ys + kk * LDS16, LDS16);
-              mma(acc, fa, fb);
+              mma(acc, fb, fa);
             }
+            Tin tv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              Tb[(rb + r * 16 + acc_row(i)) * LDC + cb + c * 16 + acc_col()] =
-                  from_f32<Tin>(-acc[i]);
+            for (int i = 0; i < 4; ++i) tv[i] = from_f32<Tin>(-acc[i]);
+            *reinterpret_cast<RawQuad<Tin>*>(Tb + (rb + r * 16 + acc_col()) * LDC + cb + c * 16 +
+                                             acc_row(0)) =
+                *reinterpret_cast<const RawQuad<Tin>*>(tv);
           }
           wave_lds_sync();  // the scratch is rewritten by this wave's next job
         }
