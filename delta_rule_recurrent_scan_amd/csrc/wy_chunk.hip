@@ -491,9 +491,17 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       float* Pv = reinterpret_cast<float*>(smem + G::oPv);
       const Tin* As = reinterpret_cast<const Tin*>(smem + G::oAs);
       Tin* Lb = Ab;  // L lives in the Gram buffer until the Gram step
-      for (int e = tid; e < C * C; e += G::NT) {
-        const int t = e / C, i = e % C;
-        Lb[t * LDC + i] = from_f32<Tin>(i < t ? __expf(lps[t] - lps[i + 1]) * gs[i] : 0.f);
+      // four consecutive entries of a row per thread and access
+      for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
+        const int t = e4 / (C / 4), i0 = (e4 % (C / 4)) * 4;
+        Tin lv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u;
+          lv[u] = from_f32<Tin>(i < t ? __expf(lps[t] - lps[i + 1]) * gs[i] : 0.f);
+        }
+        *reinterpret_cast<RawQuad<Tin>*>(Lb + t * LDC + i0) =
+            *reinterpret_cast<const RawQuad<Tin>*>(lv);
       }
       if (tid < C) Pv[tid] = expf(lps[tid]);
       __syncthreads();
