@@ -204,9 +204,11 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
         al.load(Al + a * 16 * LDH, LDH);
         bh_.load(Ah + b * 16 * LDH, LDH);
         bl.load(Al + b * 16 * LDH, LDH);
-        mma(gacc[s2], ah, bh_);
-        mma(gacc[s2], ah, bl);
-        mma(gacc[s2], al, bh_);
+        // tile (b, a) of the symmetric Gram, so that a lane holds four
+        // consecutive columns of one row of tile (a, b)
+        mma(gacc[s2], bh_, ah);
+        mma(gacc[s2], bl, ah);
+        mma(gacc[s2], bh_, al);
       }
     }
     __syncthreads();  // the split squares are dead from here on (T reuses them)
@@ -215,12 +217,14 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
     for (int s2 = 0; s2 < NJ; ++s2) {
       const int a = gja[s2], b = gjb[s2];
       if (a >= 0) {
+        const int t = a * 16 + acc_col(), c0 = b * 16 + acc_row(0);
+        float mv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = a * 16 + acc_row(i), c = b * 16 + acc_col();
-          Mf[t * LDF + c] =
-              c < t ? rho[t] * __expf(lpv[t] - lpv[c + 1]) * gacc[s2][i] : 0.f;
+          const int c = c0 + i;
+          mv[i] = c < t ? rho[t] * __expf(lpv[t] - lpv[c + 1]) * gacc[s2][i] : 0.f;
         }
+        *reinterpret_cast<float4*>(Mf + t * LDF + c0) = float4{mv[0], mv[1], mv[2], mv[3]};
       }
     }
     // Blocks of T above the diagonal are zero.
@@ -269,11 +273,10 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
               Frag<16, float> fa, fb;
               fa.load(Mf + (rb + rt * 16) * LDF + cb + kk, LDF);
               fb.load_kmajor(Tf + (cb + kk) * LDF + cb + c * 16, LDF);
-              mma(acc, fa, fb);
+              mma(acc, fb, fa);  // transposed: four consecutive columns per lane
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              ys[(rt * 16 + acc_row(i)) * LDYS + acc_col()] = acc[i];
+            *reinterpret_cast<float4*>(ys + (rt * 16 + acc_col()) * LDYS + acc_row(0)) =
+                float4{acc[0], acc[1], acc[2], acc[3]};
           }
           wave_lds_sync();
           for (int rt = 0; rt < nt; ++rt) {
@@ -282,11 +285,11 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
               Frag<16, float> fa, fb;
               fa.load(Tf + (rb + rt * 16) * LDF + rb + kk, LDF);
               fb.load_kmajor(ys + kk * LDYS, LDYS);
-              mma(acc, fa, fb);
+              mma(acc, fb, fa);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              Tf[(rb + rt * 16 + acc_row(i)) * LDF + cb + c * 16 + acc_col()] = -acc[i];
+            *reinterpret_cast<float4*>(Tf + (rb + rt * 16 + acc_col()) * LDF + cb + c * 16 +
+                                       acc_row(0)) =
+                float4{-acc[0], -acc[1], -acc[2], -acc[3]};
           }
           wave_lds_sync();  // the scratch is rewritten by this wave's next job
         }
