@@ -807,7 +807,7 @@ struct ScanRegs {
   Frag<C, Tin> pr;           // the same rows of the scores P
   RawTile<Tin> u[G::VB];
   Frag<C, Tin> x[G::DPW];
-  float gd[G::DPW];
+  float4 gd[G::DPW];         // exit decays of the lane's four state channels
 
   // Chunk j of (batch, head) bh. Loads are unconditional (indices of idle
   // waves and rows past the sequence end clamped into range), so that the
@@ -843,7 +843,9 @@ struct ScanRegs {
     for (int d = 0; d < G::DPW; ++d) {
       const int db = min(wave * G::DPW + d, G::DB - 1);
       x[d].load_global(wb.xp + n * C * DK + (size_t)db * 16 * C);
-      if constexpr (DECAY) gd[d] = wb.g[n * DK + db * 16 + (threadIdx.x & 15)];
+      if constexpr (DECAY)
+        gd[d] = *reinterpret_cast<const float4*>(wb.g + n * DK + db * 16 +
+                                                 4 * ((threadIdx.x & 63) >> 4));
     }
   }
 };
@@ -879,7 +881,18 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
     return KD ? ((size_t)bh * DK + kk) * Dv + v0 + vv
                 : ((size_t)bh * Dv + v0 + vv) * DK + kk;
   };
+  // The state tiles are held transposed: lane element i of tile (vb, db) is
+  // S[v = vb*16 + acc_col()][dk = db*16 + acc_row(i)], so that each lane's
+  // four values are consecutive channels of one row of the bf16 copy in LDS
+  // (one 8-byte write).
   f32x4 Sacc[G::NS];
+  auto store_state = [&](const f32x4& acc, int vb, int db) {
+    Tin sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = from_f32<Tin>(acc[i]);
+    *reinterpret_cast<RawQuad<Tin>*>(Ss + (vb * 16 + acc_col()) * LDK + db * 16 + acc_row(0)) =
+        *reinterpret_cast<const RawQuad<Tin>*>(sv);
+  };
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb) {
 #pragma unroll
@@ -889,14 +902,10 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = 0.f;
-        if (db < DB && p.S0) x = p.S0[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())];
+        if (db < DB && p.S0) x = p.S0[sidx(vb * 16 + acc_col(), db * 16 + acc_row(i))];
         acc[i] = x;
       }
-      if (db < DB) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] = from_f32<Tin>(acc[i]);
-      }
+      if (db < DB) store_state(acc, vb, db);
     }
   }
   __syncthreads();
@@ -924,7 +933,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
         f32x4 wa = {0.f, 0.f, 0.f, 0.f};
         oacc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
         mma(wa, cur.wk, fs);
-        mma(oacc[vb], cur.qh, fs);
+        mma(oacc[vb], fs, cur.qh);  // transposed: [v][t]
         Tin w4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) w4[i] = from_f32<Tin>(cur.u[vb][i] - wa[i]);
@@ -959,11 +968,13 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
         // and out as one 16-byte store per lane
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-          mma(oacc[vb], cur.pr, fw[vb]);
+          mma(oacc[vb], fw[vb], cur.pr);  // transposed: four columns per lane
+          Tin ov[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            Os[(wave * 16 + acc_row(i)) * LDO + vb * 16 + acc_col()] =
-                from_f32<Tin>(p.scale * oacc[vb][i]);
+          for (int i = 0; i < 4; ++i) ov[i] = from_f32<Tin>(p.scale * oacc[vb][i]);
+          *reinterpret_cast<RawQuad<Tin>*>(Os + (wave * 16 + acc_col()) * LDO + vb * 16 +
+                                           acc_row(0)) =
+              *reinterpret_cast<const RawQuad<Tin>*>(ov);
         }
         wave_lds_sync();
         constexpr int VPL = 16 / (int)sizeof(Tin);           // elements per lane access
@@ -986,13 +997,13 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
           for (int vb = 0; vb < VB; ++vb) {
             f32x4& acc = Sacc[vb * DPW + d];
             if constexpr (DECAY) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[i] *= cur.gd[d];
+              acc[0] *= cur.gd[d].x;
+              acc[1] *= cur.gd[d].y;
+              acc[2] *= cur.gd[d].z;
+              acc[3] *= cur.gd[d].w;
             }
-            mma(acc, fw[vb], cur.x[d]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              Ss[(vb * 16 + acc_row(i)) * LDK + db * 16 + acc_col()] = from_f32<Tin>(acc[i]);
+            mma(acc, cur.x[d], fw[vb]);  // transposed state tile
+            store_state(acc, vb, db);
           }
         }
       }
@@ -1032,7 +1043,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
         if (db < DB) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            p.ST[sidx(vb * 16 + acc_row(i), db * 16 + acc_col())] = Sacc[vb * DPW + d][i];
+            p.ST[sidx(vb * 16 + acc_col(), db * 16 + acc_row(i))] = Sacc[vb * DPW + d][i];
         }
       }
     }
