@@ -227,10 +227,11 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
         *reinterpret_cast<float4*>(Mf + t * LDF + c0) = float4{mv[0], mv[1], mv[2], mv[3]};
       }
     }
-    // Blocks of T above the diagonal are zero.
-    for (int e = tid; e < C * C; e += G::NT) {
-      const int rr = e / C, cc = e % C;
-      if ((cc >> 4) > (rr >> 4)) Tf[rr * LDF + cc] = 0.f;
+    // Blocks of T above the diagonal are zero (four entries per access).
+    for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
+      const int rr = e4 / (C / 4), cc = (e4 % (C / 4)) * 4;
+      if ((cc >> 4) > (rr >> 4))
+        *reinterpret_cast<float4*>(Tf + rr * LDF + cc) = float4{0.f, 0.f, 0.f, 0.f};
     }
 
     // ---- diagonal 16x16 blocks of T = (I + M)^-1 ----------------------------
