@@ -543,9 +543,19 @@ __global__ __launch_bounds__(256) void precond_ktilde_kernel(
   if (tid < DK) dv[tid] = dent[(size_t)blockIdx.x * DK + tid];
   __syncthreads();
   if (tid < C) Pv[tid] = expf(lpv[tid]);
-  for (int e = tid; e < C * C; e += G::NT) {
-    const int tt = e / C, i = e % C;
-    Lb[tt * LDC + i] = from_f32<Tin>(i < tt ? __expf(lpv[tt] - lpv[i + 1]) * gv[i] : 0.f);
+  // four consecutive entries of a row per thread and access
+  for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
+    const int tt = e4 / (C / 4), i0 = (e4 % (C / 4)) * 4;
+    Tin lv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u;
+      lv[u] = from_f32<Tin>(i < tt ? __expf(lpv[tt] - lpv[i + 1]) * gv[i] : 0.f);
+    }
+    if constexpr (sizeof(Tin) == 2)
+      *reinterpret_cast<uint2*>(Lb + tt * LDC + i0) = *reinterpret_cast<const uint2*>(lv);
+    else
+      *reinterpret_cast<uint4*>(Lb + tt * LDC + i0) = *reinterpret_cast<const uint4*>(lv);
   }
   __syncthreads();
   // wave w: token block w, all channel blocks; K~ overwrites K in place (each
