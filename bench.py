@@ -129,6 +129,7 @@ def flops_per_token_head(w):
 
 
 LAUNCHES_PER_STEP = {}
+COLD = None
 
 
 def timed_steps(step, args):
@@ -155,9 +156,32 @@ def timed_steps(step, args):
     # over time pieces launches several times per step)
     rec = osdn.kernel_times()
     kt = {n: ms * cnt / args.steps for n, (cnt, ms) in rec.items()}
-    global LAUNCHES_PER_STEP
+    global LAUNCHES_PER_STEP, COLD
     LAUNCHES_PER_STEP = {n: cnt / args.steps for n, (cnt, ms) in rec.items()}
+    COLD = cold_steps(step, args.steps)
     return wall * 1e3 / args.steps, kt
+
+
+def cold_steps(step, n):
+    """Each step timed alone (HIP events on the current stream) after 1 GiB
+    of other data has been written, so that the memory-side cache and the L2
+    no longer hold the step's inputs; returns median and min in ms."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    times = []
+    for i in range(n):
+        flush.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    times.sort()
+    return {"median_ms": times[len(times) // 2], "min_ms": times[0],
+            "note": "each step timed alone after writing 1 GiB elsewhere "
+                    "(inputs not in the memory-side cache or L2)"}
 
 
 def roofline(w, kt, kb):
@@ -232,6 +256,7 @@ def bench_gated(args, w, inp, x, dt, dev):
                    "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk},
         "roofline": roofline(w, kt, kb),
         "kernels_ms": kt,
+        "cold_step": COLD,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_gated(w, inp)
@@ -294,6 +319,7 @@ def bench_gdn2(args, w, inp, x, dt, dev):
                    "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk},
         "roofline": roofline(w, kt, kb),
         "kernels_ms": kt,
+        "cold_step": COLD,
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_gdn2(w, inp)
@@ -370,6 +396,14 @@ def bench_decode(args, w, inp, x, dt, dev):
                      "traffic": measured_traffic(name, w.name),
                      "alg_bytes": alg, "ms": kt[name]},
         "kernels_ms": kt,
+        "cold_step": COLD,
+        # back-to-back decode steps find much of the state in the memory-side
+        # cache (the whole state of this workload fits in it); the cold step
+        # (state and inputs evicted first, launch included) bounds the HBM rate
+        "roofline_cold": {"achieved": alg / (COLD["median_ms"] * 1e-3) / 1e9,
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": alg / (COLD["median_ms"] * 1e-3) / 1e9
+                          / HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_decode(w, inp)
@@ -500,6 +534,7 @@ def main():
                    "forgetting_gate": apf, "eta": w.eta},
         "roofline": roofline(w, kt, kb),
         "kernels_ms": kt,
+        "cold_step": COLD,
         "path": {"alg_bytes": path_b * th,
                  "hbm_GBs": path_b * th / (ms_step * 1e-3) / 1e9,
                  "hbm_frac": path_b * th / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
