@@ -342,6 +342,34 @@ def pin_gdn2_reductions():
                                atol=1e-13)
 
 
+def pin_grad_h_scale():
+    """grad_h_closed_form equals the central-difference gradient of h, taken
+    both from the printed closed form and from h's definition with a random
+    state and value ([OSDN-it] section 2.2), in direction and in scale
+    (keys of random norm, so a dropped 1/||k||^2 or beta shows)."""
+    g = _rng(23)
+    eps = 1e-6
+    for _ in range(25):
+        Dk, Dv = 6, 4
+        k = g.standard_normal(Dk) * g.uniform(0.3, 3.0)
+        d = g.uniform(0.2, 2.0, Dk)
+        beta = g.uniform(0.05, 0.95)
+        S = g.standard_normal((Dv, Dk))
+        v = g.standard_normal(Dv)
+        fd_c = np.empty(Dk)
+        fd_d = np.empty(Dk)
+        for i in range(Dk):
+            e = np.zeros(Dk)
+            e[i] = eps
+            fd_c[i] = (R.h_closed_form(d + e, k, beta)
+                       - R.h_closed_form(d - e, k, beta)) / (2 * eps)
+            fd_d[i] = (R.h_by_definition(S, v, d + e, k, beta)
+                       - R.h_by_definition(S, v, d - e, k, beta)) / (2 * eps)
+        gr = R.grad_h_closed_form(d, k, beta)
+        np.testing.assert_allclose(gr, fd_c, rtol=1e-6, atol=1e-10)
+        np.testing.assert_allclose(gr, fd_d, rtol=1e-6, atol=1e-10)
+
+
 PINS = [
     pin_closed_form_equals_definition,
     pin_step_is_descent_on_definition,
@@ -357,6 +385,7 @@ PINS = [
     pin_readout_inclusive,
     pin_gdn2_exact_and_orientation,
     pin_gdn2_reductions,
+    pin_grad_h_scale,
 ]
 
 
@@ -483,13 +512,37 @@ def _mut_plain_key_dot(d, kt, beta_t, r_t, eta):
 
 
 _ORIG_STEP = R._phase1_step
+_ORIG_GRAD = R.grad_h_closed_form
 
 
-@pytest.mark.parametrize("mutant", [_mut_ascent, _mut_grad_at_gated,
-                                    _mut_ktilde_after_update,
-                                    _mut_norm_not_squared, _mut_plain_key_dot])
-def test_mutants_are_caught(monkeypatch, mutant):
-    monkeypatch.setattr(R, "_phase1_step", mutant)
+def _mut_grad_no_norm(d, k, beta):
+    # the 1 / ||k||^2 factor dropped
+    n = np.sum(np.asarray(k, float) ** 2, axis=-1)
+    return _ORIG_GRAD(d, k, beta) * np.asarray(n)[..., None]
+
+
+def _mut_grad_one_beta(d, k, beta):
+    # one factor beta dropped: -(1 - beta c) a / n
+    return _ORIG_GRAD(d, k, beta) / np.asarray(beta, float)[..., None]
+
+
+def _mut_grad_sign(d, k, beta):
+    return -_ORIG_GRAD(d, k, beta)
+
+
+MUTANTS = [("_phase1_step", m) for m in (_mut_ascent, _mut_grad_at_gated,
+                                         _mut_ktilde_after_update,
+                                         _mut_norm_not_squared,
+                                         _mut_plain_key_dot)]
+MUTANTS += [("grad_h_closed_form", m) for m in (_mut_grad_no_norm,
+                                                _mut_grad_one_beta,
+                                                _mut_grad_sign)]
+
+
+@pytest.mark.parametrize("attr,mutant", MUTANTS,
+                         ids=[m.__name__ for _, m in MUTANTS])
+def test_mutants_are_caught(monkeypatch, attr, mutant):
+    monkeypatch.setattr(R, attr, mutant)
     failed = []
     for pin in PINS:
         try:
