@@ -262,18 +262,17 @@ __global__ __launch_bounds__(kDecThreads) void gdn2_decode_kernel(
 template <int DK, int DV, typename Tin>
 int launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
+  const int tk = ktimer_before(s, a.gdn2 ? "gdn2_decode" : "osdn_decode");
   if (a.gdn2) {
-    ktimer_before(s, "gdn2_decode");
     hipLaunchKernelGGL((gdn2_decode_kernel<DK, DV, Tin>), dim3(BH), dim3(kDecThreads), 0, s,
                        a.T, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, a.log_alpha,
                        (const Tin*)a.b, (const Tin*)a.w, a.S, a.scale, (Tin*)a.o);
   } else {
-    ktimer_before(s, "osdn_decode");
     hipLaunchKernelGGL((osdn_decode_kernel<DK, DV, Tin>), dim3(BH), dim3(kDecThreads), 0, s,
                        a.T, (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.v, a.beta, a.r,
                        a.eta, a.log_alpha, a.S, a.d, a.scale, (Tin*)a.o);
   }
-  ktimer_after(s);
+  ktimer_after(s, tk);
   return (int)hipGetLastError();
 }
 

@@ -104,7 +104,9 @@ size_t wy_workspace_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
 
 // Kernel timing hooks (no-ops unless enabled through osdn_kernel_timing):
 // an event on stream s before the kernel `name` is launched and one after.
-void ktimer_before(hipStream_t s, const char* name);
-void ktimer_after(hipStream_t s);
+// ktimer_before returns the handle of the record it started (-1 when timing
+// is off or no event was available); ktimer_after completes that record only.
+int ktimer_before(hipStream_t s, const char* name);
+void ktimer_after(hipStream_t s, int handle);
 
 }  // namespace osdn

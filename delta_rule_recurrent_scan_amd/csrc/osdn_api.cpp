@@ -53,6 +53,35 @@ bool gated_fused(int Dk, int Dv, int chunk, int dtype) {
          osdn::gated_fused_supported(Dk, Dv, dtype == OSDN_BF16);
 }
 
+// Workspace layout of a two-phase forward (osdn_forward, osdn_gated_forward).
+// Fused (phase 2 forms K~ itself from the phase-1 records): the phase-1
+// scratch at 0, the phase-2 scratch right after it, both live at once.
+// Otherwise: K~ at 0, then one region shared by the two phases. The size
+// queries return `total` and the launch paths take their offsets from the
+// same struct, so the two cannot disagree.
+struct Layout {
+  bool fused;
+  size_t kt_off, p1_off, p2_off, total;
+};
+
+Layout two_phase_layout(int B, int H, int T, int Dk, int dtype, bool fused,
+                        size_t p1, size_t p2) {
+  Layout l{};
+  l.fused = fused;
+  if (fused) {
+    l.kt_off = 0;
+    l.p1_off = 0;
+    l.p2_off = p1;
+    l.total = p1 + p2;
+  } else {
+    const size_t kt = round256((size_t)B * H * T * Dk * elem(dtype));
+    l.kt_off = 0;
+    l.p1_off = l.p2_off = kt;
+    l.total = kt + (p1 > p2 ? p1 : p2);
+  }
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,26 +125,30 @@ static size_t chunk_ws_bytes(int B, int H, int T, int Dk, int Dv, int chunk,
 
 size_t osdn_chunk_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                   int chunk, int dtype) {
+  if (!osdn_forward_supported(Dk, Dv, chunk, dtype)) return 0;
   return chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 0);
 }
 
 size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype) {
+  if (!gdn2_forward_supported(Dk, Dv, chunk, dtype)) return 0;
   return chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 1);
+}
+
+static Layout osdn_layout(int B, int H, int T, int Dk, int Dv, int chunk,
+                          int dtype) {
+  // chunk = 64: phase 2 forms K~ itself from the phase-1 records
+  return two_phase_layout(
+      B, H, T, Dk, dtype, chunk == osdn::kPrecondChunk,
+      osdn_precond_workspace_bytes(B, H, T, Dk, dtype),
+      osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype));
 }
 
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype) {
-  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
-      !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+  if (B < 0 || H < 0 || T < 0 || !osdn_forward_supported(Dk, Dv, chunk, dtype))
     return 0;
-  const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
-  const size_t p2 = osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, chunk, dtype);
-  // chunk = 64: phase 2 forms K~ itself from the phase-1 records, so both
-  // scratch regions are live at once; otherwise the preconditioned keys,
-  // then scratch shared by the two phases
-  if (gated_fused(Dk, Dv, chunk, dtype)) return p1 + p2;
-  return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
+  return osdn_layout(B, H, T, Dk, Dv, chunk, dtype).total;
 }
 
 int osdn_precond_scan(int B, int H, int T, int Dk, int dtype, const void* k,
@@ -180,35 +213,34 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
 
   hipStream_t s = (hipStream_t)stream;
   unsigned char* wsb = static_cast<unsigned char*>(workspace);
+  const Layout lay = osdn_layout(B, H, T, Dk, Dv, chunk, dtype);
   int rc;
-  if (chunk == osdn::kPrecondChunk) {
+  if (lay.fused) {
     // phase-1 scratch (records, then entry values of d), then the phase-2
     // operands; K~ is formed inside phase 2
-    const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
     osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                         nullptr, d_T, wsb, rho, q_geo};
+                         nullptr, d_T, wsb + lay.p1_off, rho, q_geo};
     rc = osdn::launch_precond_scan(pa, s);
     if (rc == -1) return OSDN_ERR_UNSUPPORTED;
     if (rc != 0) return OSDN_ERR_HIP;
     const int nch = (T + chunk - 1) / chunk;
-    const float* prec = reinterpret_cast<const float*>(wsb);
+    const float* prec = reinterpret_cast<const float*>(wsb + lay.p1_off);
     const float* pdent = prec + BH * (size_t)nch * osdn::kRecStride;
     osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
                        nullptr, v, beta, S0, scale, o, S_T,
-                       nullptr, nullptr, nullptr, wsb + p1, prec, pdent};
+                       nullptr, nullptr, nullptr, wsb + lay.p2_off, prec, pdent};
     rc = osdn::launch_osdn_fused(ca, s);
   } else {
     // workspace: the preconditioned keys, then scratch shared by the phases
-    const size_t kt_bytes = round256(BH * T * Dk * es);
-    void* pws = wsb + kt_bytes;
+    void* kt = wsb + lay.kt_off;
     osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                         workspace, d_T, pws, rho, q_geo};
+                         kt, d_T, wsb + lay.p1_off, rho, q_geo};
     rc = osdn::launch_precond_scan(pa, s);
     if (rc == -1) return OSDN_ERR_UNSUPPORTED;
     if (rc != 0) return OSDN_ERR_HIP;
     osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                       workspace, v, beta, S0, scale, o, S_T,
-                       nullptr, nullptr, nullptr, pws};
+                       kt, v, beta, S0, scale, o, S_T,
+                       nullptr, nullptr, nullptr, wsb + lay.p2_off};
     rc = osdn::launch_osdn_chunk(ca, s);
   }
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;
@@ -338,19 +370,22 @@ int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype) {
   return gdn2_forward_supported(Dk, Dv, chunk, dtype);
 }
 
+static Layout gated_layout(int B, int H, int T, int Dk, int Dv, int chunk,
+                           int dtype) {
+  // chunk = 64 where that engine layout fits: the engine forms K~ from the
+  // phase-1 records
+  return two_phase_layout(B, H, T, Dk, dtype,
+                          gated_fused(Dk, Dv, chunk, dtype),
+                          osdn_precond_workspace_bytes(B, H, T, Dk, dtype),
+                          chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 1));
+}
+
 size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                           int chunk, int dtype) {
-  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv) ||
-      !chunk_ok(chunk) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+  if (B < 0 || H < 0 || T < 0 ||
+      !osdn_gated_forward_supported(Dk, Dv, chunk, dtype))
     return 0;
-  const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
-  const size_t p2 = chunk_ws_bytes(B, H, T, Dk, Dv, chunk, dtype, 1);
-  if (p1 == 0 && p2 == 0) return 0;
-  // chunk = 64: the engine forms K~ from the phase-1 records, so both scratch
-  // regions are live at once; otherwise the preconditioned keys, then
-  // scratch shared by the two phases
-  if (gated_fused(Dk, Dv, chunk, dtype)) return p1 + p2;
-  return round256((size_t)B * H * T * Dk * elem(dtype)) + (p1 > p2 ? p1 : p2);
+  return gated_layout(B, H, T, Dk, Dv, chunk, dtype).total;
 }
 
 int osdn_gated_forward(int B, int H, int T, int Dk, int Dv, int chunk,
@@ -385,33 +420,32 @@ int osdn_gated_forward(int B, int H, int T, int Dk, int Dv, int chunk,
   if (!aliasing_ok(outs, ins, allowed, 2)) return OSDN_ERR_ALIASING;
   hipStream_t s = (hipStream_t)stream;
   unsigned char* wsb = static_cast<unsigned char*>(workspace);
+  const Layout lay = gated_layout(B, H, T, Dk, Dv, chunk, dtype);
   int rc;
-  if (gated_fused(Dk, Dv, chunk, dtype)) {
+  if (lay.fused) {
     // phase-1 records and entry values of d, then the engine's operands
-    const size_t p1 = osdn_precond_workspace_bytes(B, H, T, Dk, dtype);
     osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                         nullptr, d_T, wsb, nullptr, nullptr};
+                         nullptr, d_T, wsb + lay.p1_off, nullptr, nullptr};
     rc = osdn::launch_precond_scan(pa, s);
     if (rc == -1) return OSDN_ERR_UNSUPPORTED;
     if (rc != 0) return OSDN_ERR_HIP;
     const int nch = (T + chunk - 1) / chunk;
-    const float* prec = reinterpret_cast<const float*>(wsb);
+    const float* prec = reinterpret_cast<const float*>(wsb + lay.p1_off);
     const float* pdent = prec + BH * (size_t)nch * osdn::kRecStride;
     osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
                        nullptr, v, beta, S0, scale, o, S_T,
-                       log_alpha, nullptr, nullptr, wsb + p1, prec, pdent};
+                       log_alpha, nullptr, nullptr, wsb + lay.p2_off, prec, pdent};
     rc = osdn::launch_osdn_gated_fused(ca, s);
   } else {
-    const size_t kt_bytes = round256(BH * T * Dk * es);
-    void* pws = wsb + kt_bytes;
+    void* kt = wsb + lay.kt_off;
     osdn::PrecondArgs pa{B, H, T, Dk, dtype == OSDN_BF16, k, beta, r, eta, d0,
-                         workspace, d_T, pws, nullptr, nullptr};
+                         kt, d_T, wsb + lay.p1_off, nullptr, nullptr};
     rc = osdn::launch_precond_scan(pa, s);
     if (rc == -1) return OSDN_ERR_UNSUPPORTED;
     if (rc != 0) return OSDN_ERR_HIP;
     osdn::ChunkArgs ca{B, H, T, Dk, Dv, chunk, dtype == OSDN_BF16, q, k,
-                       workspace, v, beta, S0, scale, o, S_T,
-                       log_alpha, nullptr, nullptr, pws};
+                       kt, v, beta, S0, scale, o, S_T,
+                       log_alpha, nullptr, nullptr, wsb + lay.p2_off};
     rc = osdn::launch_osdn_gated_chunk(ca, s);
   }
   if (rc == -1) return OSDN_ERR_UNSUPPORTED;

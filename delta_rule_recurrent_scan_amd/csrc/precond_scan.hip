@@ -673,7 +673,7 @@ static int launch_dk(const PrecondArgs& a, hipStream_t s) {
   float* dent = rec + (size_t)BH * nch * G::RS;
   const dim3 block(256);
   if (nch > 0) {
-    ktimer_before(s, "precond_prep");
+    const int tk_prep = ktimer_before(s, "precond_prep");
     // persistent grid of two workgroups per compute unit: three fit by LDS,
     // but two measured faster (at 4096 and at 2048 chunks the prep took
     // 65 and 36 us with two per unit against 76 and 40 us with three, and
@@ -684,29 +684,29 @@ static int launch_dk(const PrecondArgs& a, hipStream_t s) {
     const int grid = total < 256 * per_cu ? total : 256 * per_cu;
     hipLaunchKernelGGL((precond_prep_kernel<DK, Tin>), dim3(grid), block, 0, s,
                        a.T, nch, total, (const Tin*)a.k, a.beta, a.r, a.eta, rec);
-    ktimer_after(s);
+    ktimer_after(s, tk_prep);
     const int rc = (int)hipGetLastError();
     if (rc) return rc;
   }
-  ktimer_before(s, "precond_chain");
+  const int tk_chain = ktimer_before(s, "precond_chain");
   hipLaunchKernelGGL((precond_chain_kernel<DK, Tin>), dim3(BH), dim3(64 * chain_waves<DK>()), 0, s, a.T,
                      nch, (const Tin*)a.k, a.d0, rec, dent, a.dT);
-  ktimer_after(s);
+  ktimer_after(s, tk_chain);
   int rc = (int)hipGetLastError();
   if (rc) return rc;
   if (a.rho || a.qgeo) {
-    ktimer_before(s, "precond_rho");
+    const int tk_rho = ktimer_before(s, "precond_rho");
     hipLaunchKernelGGL((precond_rho_kernel<DK, Tin>), dim3(BH), block, 0, s, a.T, nch,
                        (const Tin*)a.k, a.beta, a.eta, rec, dent, a.rho, a.qgeo);
-    ktimer_after(s);
+    ktimer_after(s, tk_rho);
     rc = (int)hipGetLastError();
     if (rc) return rc;
   }
   if (nch > 0 && a.ktilde) {
-    ktimer_before(s, "precond_ktilde");
+    const int tk_ktilde = ktimer_before(s, "precond_ktilde");
     hipLaunchKernelGGL((precond_ktilde_kernel<DK, Tin>), dim3(BH * nch), block, 0, s,
                        a.T, nch, (const Tin*)a.k, rec, dent, (Tin*)a.ktilde);
-    ktimer_after(s);
+    ktimer_after(s, tk_ktilde);
     rc = (int)hipGetLastError();
   }
   return rc;

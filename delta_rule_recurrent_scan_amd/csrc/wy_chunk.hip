@@ -1080,25 +1080,25 @@ static int launch_cfg(const ChunkArgs& a, hipStream_t s) {
     if (nch > 0) {
       // persistent grid: a few workgroups per compute unit at most
       const int grid = std::min(BH * nch, 256 * kPrepWgPerCu<V, DK, DV, C, Tin>());
-      ktimer_before(s, kGdn2    ? "gdn2_prep"
+      const int tk_prep = ktimer_before(s, kGdn2    ? "gdn2_prep"
                        : std::is_same<V, OsdnGatedFusedVariant>::value ? "gated_prep_fused"
                        : kGated ? "gated_prep"
                        : std::is_same<V, OsdnFusedVariant>::value ? "wy_prep_fused"
                                                                   : "wy_prep");
       hipLaunchKernelGGL((wy_prep_kernel<V, DK, DV, C, Tin>), dim3(grid),
                          dim3(512), 0, s, a, nch, wb);
-      ktimer_after(s);
+      ktimer_after(s, tk_prep);
       const int rc = (int)hipGetLastError();
       if (rc) return rc;
     }
-    ktimer_before(s, kGdn2 ? "gdn2_scan" : kGated ? "gated_scan" : "wy_scan");
+    const int tk_scan = ktimer_before(s, kGdn2 ? "gdn2_scan" : kGated ? "gated_scan" : "wy_scan");
     if (pick_vt(BH, DV) == 32)
       hipLaunchKernelGGL((wy_scan_kernel<kDecay, kGdn2, DK, C, 32, Tin>),
                          dim3(BH * (DV / 32)), dim3(256), 0, s, a, nch, wb);
     else
       hipLaunchKernelGGL((wy_scan_kernel<kDecay, kGdn2, DK, C, 16, Tin>),
                          dim3(BH * (DV / 16)), dim3(256), 0, s, a, nch, wb);
-    ktimer_after(s);
+    ktimer_after(s, tk_scan);
     return (int)hipGetLastError();
   }
 }

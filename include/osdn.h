@@ -14,7 +14,10 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
  *    caller, contiguous, row-major, in the layouts stated below. The library
- *    allocates nothing and keeps no global mutable state; calls are reentrant.
+ *    allocates nothing, and calls are reentrant and thread-safe. Its one piece
+ *    of process-global mutable state is the optional per-kernel timing record
+ *    of osdn_kernel_timing / osdn_kernel_times (off by default; guarded by a
+ *    lock); no compute call depends on it.
  *  - Inputs are read-only. Outputs are fully overwritten. Pointers marked
  *    "required" may be NULL only when the tensor has no elements (B*H*T = 0).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
@@ -62,13 +65,14 @@ int osdn_forward_supported(int Dk, int Dv, int chunk, int dtype);
 
 /*
  * Device workspace, in bytes, that osdn_forward needs for these sizes
- * (0 if the sizes are invalid or the call needs none); its contents are only
- * meaningful during one call. chunk = 64: the phase-1 scratch
- * (osdn_precond_workspace_bytes) followed by the phase-2 scratch
+ * (0 if the sizes are invalid or unsupported, or the call needs none); its
+ * contents are only meaningful during one call. chunk = 64: the phase-1
+ * scratch (osdn_precond_workspace_bytes) followed by the phase-2 scratch
  * (osdn_chunk_workspace_bytes), since phase 2 then forms the preconditioned
  * keys itself. Other chunks: the preconditioned keys ([B,H,T,Dk] in the
  * storage dtype, rounded up to 256 bytes) followed by scratch shared by the
- * two phases (the larger of the two).
+ * two phases (the larger of the two). osdn_forward places its regions by the
+ * same rule, so this many bytes always cover what it touches.
  */
 size_t osdn_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                     int chunk, int dtype);
@@ -213,12 +217,13 @@ size_t gdn2_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
 int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype);
 
 /* Device workspace, in bytes, that osdn_gated_forward needs (0 if the sizes
- * are invalid or the call needs none). chunk = 64, where the engine's layout
- * with the preconditioned keys formed inside it fits (bf16 at every
- * supported Dk, Dv): osdn_precond_workspace_bytes followed by
- * gdn2_forward_workspace_bytes. Otherwise the preconditioned keys
- * ([B,H,T,Dk] in the storage dtype, rounded up to 256 bytes), then scratch
- * shared by the two phases (the larger of the two). */
+ * are invalid or unsupported, or the call needs none). chunk = 64, where the
+ * engine's layout with the preconditioned keys formed inside it fits (bf16 at
+ * every supported Dk, Dv; fp32 at Dk = 32, and at Dk = 64 with Dv = 32):
+ * osdn_precond_workspace_bytes followed by gdn2_forward_workspace_bytes.
+ * Otherwise the preconditioned keys ([B,H,T,Dk] in the storage dtype, rounded
+ * up to 256 bytes), then scratch shared by the two phases (the larger of the
+ * two). The call places its regions by the same rule. */
 size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
                                           int chunk, int dtype);
 
@@ -290,11 +295,13 @@ int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype,
                 float* S, float scale, void* o, void* stream);
 
 /*
- * Per-kernel timing for measurement harnesses (not thread-safe). While
- * enabled, every entry point records a HIP event on its stream before and
- * after each kernel it launches (two event records per kernel; events are
- * created on first use and kept). osdn_kernel_timing(1) enables and clears
- * the record, osdn_kernel_timing(0) disables.
+ * Per-kernel timing for measurement harnesses. While enabled, every entry
+ * point records a HIP event on its stream before and after each kernel it
+ * launches (two event records per kernel; events are created on first use
+ * and kept). osdn_kernel_timing(1) enables and clears the record,
+ * osdn_kernel_timing(0) disables. The record is process-global (shared by
+ * every thread and stream) and guarded by a lock; a harness that times one
+ * stream should not run other calls meanwhile.
  */
 void osdn_kernel_timing(int enable);
 

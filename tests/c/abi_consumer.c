@@ -40,6 +40,41 @@ int main(void) {
   CHECK(gdn2_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, OSDN_BF16) > 0);
   CHECK(osdn_precond_workspace_bytes(4, 16, 4096, 128, OSDN_BF16) > 0);
 
+  /* every supported size: the advertised workspace is the layout the header
+   * states (chunk 64: phase-1 scratch + phase-2 scratch; otherwise the
+   * preconditioned keys rounded up to 256 bytes + the larger of the two);
+   * unsupported sizes advertise 0 */
+  {
+    static const int dims[3] = {32, 64, 128}, chunks[3] = {16, 32, 64};
+    static const int shapes[3][3] = {{1, 1, 1}, {2, 3, 448}, {3, 1, 1000}};
+    for (int dt = 0; dt < 2; ++dt)
+      for (int a = 0; a < 3; ++a)
+        for (int b = 0; b < 3; ++b)
+          for (int c = 0; c < 3; ++c)
+            for (int s = 0; s < 3; ++s) {
+              const int Dk = dims[a], Dv = dims[b], Ch = chunks[c];
+              const int Bq = shapes[s][0], Hq = shapes[s][1], Tq = shapes[s][2];
+              const size_t got =
+                  osdn_forward_workspace_bytes(Bq, Hq, Tq, Dk, Dv, Ch, dt);
+              if (!osdn_forward_supported(Dk, Dv, Ch, dt)) {
+                CHECK(got == 0);
+                continue;
+              }
+              const size_t p1 = osdn_precond_workspace_bytes(Bq, Hq, Tq, Dk, dt);
+              const size_t p2 =
+                  osdn_chunk_workspace_bytes(Bq, Hq, Tq, Dk, Dv, Ch, dt);
+              size_t kt = (size_t)Bq * Hq * Tq * Dk * (dt ? 2 : 4);
+              kt = (kt + 255) / 256 * 256;
+              const size_t need =
+                  Ch == 64 ? p1 + p2 : kt + (p1 > p2 ? p1 : p2);
+              CHECK(got == need);
+            }
+  }
+  /* fp32, Dk = Dv = 64, chunk 64: the two regions side by side */
+  CHECK(osdn_forward_workspace_bytes(2, 3, 448, 64, 64, 64, OSDN_F32) ==
+        osdn_precond_workspace_bytes(2, 3, 448, 64, OSDN_F32) +
+            osdn_chunk_workspace_bytes(2, 3, 448, 64, 64, 64, OSDN_F32));
+
   /* validation happens on the host, before any launch (the fake device
    * addresses below are never dereferenced) */
   const int B = 1, H = 1, T = 64, Dk = 32, Dv = 32, C = 16;

@@ -286,3 +286,63 @@ def test_gated_forward_error_paths_and_workspace():
         == kt + max(p1, p2b)
     assert L.osdn_gated_forward_supported(128, 128, 64, 1) == 1
     assert L.osdn_gated_forward_supported(128, 128, 8, 1) == 0
+
+
+def _layout_bytes(L, B, H, T, Dk, Dv, C, dt, gated):
+    """Bytes a two-phase forward touches, by the layout rule the header
+    states: fused (chunk 64; for the gated forward where its fused engine
+    layout fits) = phase-1 scratch + phase-2 scratch; otherwise K~ (rounded
+    up to 256 bytes) + the larger of the two."""
+    r256 = lambda n: (n + 255) // 256 * 256
+    p1 = L.osdn_precond_workspace_bytes(B, H, T, Dk, dt)
+    if gated:
+        p2 = L.gdn2_forward_workspace_bytes(B, H, T, Dk, Dv, C, dt)
+        fused = C == 64 and (dt == 1 or Dk == 32 or (Dk == 64 and Dv == 32))
+    else:
+        p2 = L.osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, C, dt)
+        fused = C == 64
+    if fused:
+        return p1 + p2
+    return r256(B * H * T * Dk * (2 if dt == 1 else 4)) + max(p1, p2)
+
+
+@needs_lib
+@pytest.mark.parametrize("gated", [False, True])
+def test_workspace_covers_every_supported_size(gated):
+    """For every (Dk, Dv, chunk, dtype) with a kernel instance and several
+    (B, H, T), the advertised workspace equals the bytes the call's layout
+    places (so it covers every region it touches); unsupported sizes
+    advertise 0. This includes fp32 at chunk 64, whose query once chose the
+    gated engine's layout rule and came out short."""
+    L = osdn.load_library()
+    sup = L.osdn_gated_forward_supported if gated else L.osdn_forward_supported
+    query = (L.osdn_gated_forward_workspace_bytes if gated
+             else L.osdn_forward_workspace_bytes)
+    seen = 0
+    for dt in (0, 1):
+        for dk in (32, 64, 128):
+            for dv in (32, 64, 128):
+                for c in (16, 32, 64):
+                    for B, H, T in ((1, 1, 1), (2, 3, 448), (4, 16, 4096),
+                                    (1, 2, 63), (3, 1, 1000)):
+                        got = query(B, H, T, dk, dv, c, dt)
+                        if not sup(dk, dv, c, dt):
+                            assert got == 0, (dt, dk, dv, c)
+                            continue
+                        need = _layout_bytes(L, B, H, T, dk, dv, c, dt, gated)
+                        assert got == need, (dt, dk, dv, c, B, H, T, got, need)
+                        assert got % 256 == 0
+                        seen += 1
+    assert seen > 100
+
+
+@needs_lib
+def test_fp32_chunk64_workspace_regression():
+    """fp32, Dk = Dv = 64, chunk 64, B=2 H=3 T=448: the call keeps the
+    phase-1 records and the phase-2 operands side by side, 3,473,664 bytes."""
+    L = osdn.load_library()
+    assert L.osdn_forward_supported(64, 64, 64, 0) == 1
+    p1 = L.osdn_precond_workspace_bytes(2, 3, 448, 64, 0)
+    p2 = L.osdn_chunk_workspace_bytes(2, 3, 448, 64, 64, 64, 0)
+    assert p1 + p2 == 3473664
+    assert L.osdn_forward_workspace_bytes(2, 3, 448, 64, 64, 64, 0) == p1 + p2

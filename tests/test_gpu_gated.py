@@ -12,6 +12,7 @@ import torch
 import delta_rule_recurrent_scan_amd as osdn
 import workloads as W
 from oracle import recurrence as R
+from parity import check_full
 
 pytestmark = pytest.mark.gpu
 
@@ -115,14 +116,12 @@ def test_gated_initial_state_in_place():
     check((f64(o), f64(Sd), f64(dd)), ref, "bf16", "in place")
 
 
-def test_gated_full_size_sampled():
+def test_gated_full_size_all_streams():
     w = BASE
     inp = W.make_inputs(w)
     o, S, d = gpu(inp)
-    for b, h in [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 3)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        check((o[sl], S[sl], d[sl]), oracle(inp, sl), w.dtype,
-              "full b=%d h=%d" % (b, h))
+    ro, rS, rd = oracle(inp)
+    check_full("gated full size", w.dtype, o, ro, S, rS, d, rd)
 
 
 def test_gated_decode_continues_forward():
