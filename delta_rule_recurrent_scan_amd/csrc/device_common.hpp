@@ -168,6 +168,13 @@ struct Frag<KEXT, __bf16> {
                                : base + N32 * 512 + lane * 4;
     *reinterpret_cast<bf16x4*>(d) = h;
   }
+  // One element (accumulator value i) of store_acc_tile.
+  __device__ __forceinline__ static void store_acc_elem(__bf16* base, int b, int i, float a) {
+    const int lane = threadIdx.x & 63;
+    __bf16* d = (b >> 1) < N32 ? base + ((b >> 1) * 64 + lane) * 8 + 4 * (b & 1)
+                               : base + N32 * 512 + lane * 4;
+    d[i] = (__bf16)a;
+  }
   __device__ __forceinline__ void store_global(__bf16* base) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -229,6 +236,9 @@ struct Frag<KEXT, float> {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 4; ++i) base[(4 * b + i) * 64 + lane] = a[i];
+  }
+  __device__ __forceinline__ static void store_acc_elem(float* base, int b, int i, float a) {
+    base[(4 * b + i) * 64 + (threadIdx.x & 63)] = a;
   }
   __device__ __forceinline__ void store_global(float* base) const {
     const int lane = threadIdx.x & 63;

@@ -164,6 +164,74 @@ struct RawTile<float> {
   __device__ __forceinline__ float operator[](int i) const { return v[i]; }
 };
 
+// Scale the elements of an operand fragment in registers by a factor that
+// depends on the element's position along the fragment's K dimension:
+// row fragments (Frag::load: K = key channel) and k-major fragments in the
+// permuted order (Frag::load_kmajor_perm: K = token) or the plain order
+// (Frag::load_kmajor: K = token). f(k) gives the factor of index k.
+template <int KEXT, typename F>
+__device__ __forceinline__ void scale_row_frag(Frag<KEXT, __bf16>& fr, F f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < Frag<KEXT, __bf16>::N32; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fr.v[i][e] = (__bf16)((float)fr.v[i][e] * f(32 * i + 8 * g + e));
+  if constexpr (Frag<KEXT, __bf16>::R16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      fr.t[e] = (__bf16)((float)fr.t[e] * f(32 * Frag<KEXT, __bf16>::N32 + 4 * g + e));
+  }
+}
+template <int KEXT, typename F>
+__device__ __forceinline__ void scale_row_frag(Frag<KEXT, float>& fr, F f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < KEXT / 4; ++i) fr.v[i] *= f(4 * i + g);
+}
+template <int KEXT, typename F>
+__device__ __forceinline__ void scale_kperm_frag(Frag<KEXT, __bf16>& fr, F f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < Frag<KEXT, __bf16>::N32; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      fr.v[i][e] = (__bf16)((float)fr.v[i][e] *
+                            f(32 * i + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4)));
+  if constexpr (Frag<KEXT, __bf16>::R16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      fr.t[e] = (__bf16)((float)fr.t[e] * f(32 * Frag<KEXT, __bf16>::N32 + 4 * g + e));
+  }
+}
+template <int KEXT, typename F>
+__device__ __forceinline__ void scale_kperm_frag(Frag<KEXT, float>& fr, F f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int b = 0; b < KEXT / 16; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fr.v[4 * b + i] *= f(16 * b + 4 * g + i);
+}
+
+// Maximum over the 64 lanes of a wave; every lane receives it.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// Decay inside a chunk (variants whose operands carry a decay): with
+// lambda_t the inclusive prefix of log alpha over the chunk, every factor
+// exp(lambda_t - lambda_i), i <= t, is split at 16-token block boundaries so
+// that each stored factor is at most 1: read keys and queries relative to the
+// first token s_a of their block, write keys relative to the last token e_b
+// of theirs, and tile (a, b) of the Gram matrix and of the scores takes the
+// per-channel factor exp(lambda_{s_a} - lambda_{e_b}) on the write keys. That
+// factor is at most 1 off the diagonal; on a diagonal tile it is the inverse
+// decay over the block's 15 steps, which is used as is while its exponent
+// stays below kExactDiag, else the tile is summed exactly, element by
+// element, from the raw operands.
+constexpr float kExactDiag = 60.f;
+
 // ---------------------------------------------------------------------------
 // prep
 // ---------------------------------------------------------------------------
@@ -212,6 +280,14 @@ struct PrepCfg {
   // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
   static constexpr int TPC = NT / DK;
   static constexpr int TPT = C / TPC > 0 ? C / TPC : 1;
+  // decay variants: per 16-token block, lambda at its first and last token
+  // (fp32, [TB][DK] each), kept in the doubling scratch, which is dead from
+  // the decay pass until the doubling starts
+  static_assert(!kDecayVariant<V> ||
+                    (size_t)NW * (C / 2) * LDS16 * E >= (size_t)2 * TB * DK * 4,
+                "block decay table fits in the doubling scratch");
+  static_assert(!kDecayVariant<V> || kLaOwn || oLa + kLaBytes <= oYs,
+                "log alpha staged over the Gram buffers stays clear of the table");
 };
 
 // Raw operands of one chunk, fetched into registers while the previous chunk
@@ -412,14 +488,22 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     regs.store(Ys, Xs, Qs, Zs, smem);
     // the next chunk's raw operands (the last chunk again at the end)
     regs.load(p, chunk_of(min(pos + (int)gridDim.x, total - 1)), nchunks);
+    // Decay variants: lambda at the first and last token of each 16-token
+    // block (doubling scratch), and, for this wave's diagonal tile when its
+    // block decays too strongly for the factored form, the exact tile.
+    float* Lsb = reinterpret_cast<float*>(smem + G::oYs);  // [TB][DK]
+    float* Leb = Lsb + TB * DK;                             // [TB][DK]
+    bool ex_diag = false;  // wave-uniform: this wave's diagonal tile is exact
     auto decay_pass = [&]() {
       // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
       // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
       // staged log alpha into the inclusive prefix lambda in place and give
-      // the exit decay g = gamma_C. (2) Row pass: X = x/gamma, Y = gamma*y,
-      // Q = gamma*q with gamma = exp(lambda), VEC channels per access (GDN-2:
-      // x = k and y = b*k from the staged k and b; gated OSDN: x = k~ and
-      // y = beta*k as staged).
+      // the exit decay g = gamma_C. (2) Block table and exact diagonals.
+      // (3) Row pass, VEC channels per access, every factor <= 1:
+      // X = x exp(lambda_e - lambda_t), Y = y exp(lambda_t - lambda_s),
+      // Q = q exp(lambda_t - lambda_s) with s, e the first and last token of
+      // t's block (GDN-2: x = k and y = b*k from the staged k and b; gated
+      // OSDN: x = k~ and y = beta*k as staged).
       constexpr int TPC = G::TPC, TPT = G::TPT, CPW = 64 / TPC, LDA = G::LDA;
       float* La = reinterpret_cast<float*>(smem + G::oLa);
       __syncthreads();
@@ -445,9 +529,56 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         if (part == 0) gC[c] = __expf(total_la);
       }
       __syncthreads();
+      for (int e = tid; e < TB * DK; e += G::NT) {
+        const int b = e / DK, c = e - b * DK;
+        Lsb[e] = La[(16 * b) * LDA + c];
+        Leb[e] = La[(16 * b + 15) * LDA + c];
+      }
+      if (wave < TB) {
+        // wave a owns diagonal tile a in the Gram step
+        const int a = wave;
+        float m = -1.f;
+        for (int c = lane; c < DK; c += 64)
+          m = fmaxf(m, La[(16 * a) * LDA + c] - La[(16 * a + 15) * LDA + c]);
+        m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(m))));
+        ex_diag = m > kExactDiag;
+        if (ex_diag) {
+          // the tile from the raw operands, exp(lambda_t - lambda_i) per
+          // element, written where the Gram step would put it: A's block
+          // transposed into the fp32 diagonal buffer, the scores (as P^T,
+          // rows i, columns t) into the workspace
+          const int gq = lane >> 4, cq = lane & 15;
+          float* Ad = Am + a * 16 * G::LDD + cq * G::LDD + 4 * gq;
+          Tin* pd = wb.pp + (size_t)n * C * C + (size_t)a * 16 * C;
+#pragma unroll 1
+          for (int r = 0; r < 4; ++r) {
+            // A[t][i]: t = 4 gq + r, i = cq (strictly lower); P^T[i][t]:
+            // i = 4 gq + r, t = cq (i <= t)
+            const int tA = 16 * a + 4 * gq + r, iA = 16 * a + cq;
+            const int iP = tA, tP = iA;
+            float sa = 0.f, sp = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < DK; ++c) {
+              const float xi = to_f32(Xs[iA * LDK + c]), xp = to_f32(Xs[iP * LDK + c]);
+              if (iA < tA) {
+                float y = to_f32(Ys[tA * LDK + c]);
+                if constexpr (kGdn2) y *= to_f32(Xs[tA * LDK + c]);
+                sa += y * xi * __expf(La[tA * LDA + c] - La[iA * LDA + c]);
+              }
+              if (iP <= tP)
+                sp += to_f32(Qs[tP * LDK + c]) * xp *
+                      __expf(La[tP * LDA + c] - La[iP * LDA + c]);
+            }
+            Ad[r] = sa;
+            Frag<C, Tin>::store_acc_elem(pd, a, r, sp);
+          }
+        }
+      }
+      __syncthreads();  // the row pass overwrites the raw operands
       constexpr int VEC = G::VEC;
       for (int item = tid; item < C * (DK / VEC); item += G::NT) {
         const int t = item / (DK / VEC), c0 = (item % (DK / VEC)) * VEC;
+        const int tb = t >> 4;
         uint4 k4 = *reinterpret_cast<const uint4*>(Xs + t * LDK + c0);
         uint4 b4 = *reinterpret_cast<const uint4*>(Ys + t * LDK + c0);
         uint4 q4 = *reinterpret_cast<const uint4*>(Qs + t * LDK + c0);
@@ -457,15 +588,16 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         Tin xo[VEC], yo[VEC], qo[VEC];
 #pragma unroll
         for (int u = 0; u < VEC; ++u) {
-          const float gam = __expf(La[t * LDA + c0 + u]);
-          const float igam = __builtin_amdgcn_rcpf(gam);
+          const float lt = La[t * LDA + c0 + u];
+          const float fs = __expf(lt - Lsb[tb * DK + c0 + u]);  // <= 1
+          const float fe = __expf(Leb[tb * DK + c0 + u] - lt);  // <= 1
           const float kk = to_f32(kv[u]);
-          xo[u] = from_f32<Tin>(kk * igam);
+          xo[u] = from_f32<Tin>(kk * fe);
           if constexpr (kGdn2)
-            yo[u] = from_f32<Tin>(gam * to_f32(bv[u]) * kk);
+            yo[u] = from_f32<Tin>(fs * to_f32(bv[u]) * kk);
           else
-            yo[u] = from_f32<Tin>(gam * to_f32(bv[u]));
-          qo[u] = from_f32<Tin>(gam * to_f32(qv[u]));
+            yo[u] = from_f32<Tin>(fs * to_f32(bv[u]));
+          qo[u] = from_f32<Tin>(fs * to_f32(qv[u]));
         }
         *reinterpret_cast<uint4*>(Xs + t * LDK + c0) = *reinterpret_cast<const uint4*>(xo);
         *reinterpret_cast<uint4*>(Ys + t * LDK + c0) = *reinterpret_cast<const uint4*>(yo);
@@ -560,6 +692,13 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         fy.load(Ys + a * 16 * LDK, LDK);
         fq.load(Qs + a * 16 * LDK, LDK);
         fx.load(Xs + b * 16 * LDK, LDK);
+        if constexpr (kDecay) {
+          // exp(lambda_{s_a} - lambda_{e_b}) per key channel (exponent capped
+          // where an exact diagonal replaces the product anyway)
+          const float* ls = Lsb + a * DK;
+          const float* le = Leb + b * DK;
+          scale_row_frag(fx, [&](int c) { return __expf(fminf(ls[c] - le[c], 80.f)); });
+        }
         // A tile (a, b); the scores as their transpose, tile (b, a) of
         // P^T = X Q^T, whose accumulator lanes hold exactly the scan's
         // permuted-order fragment of P's row block a, step b (stored
@@ -582,19 +721,25 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
                                        f32x4{0.f, 0.f, 0.f, 0.f});
         } else {
           mma(aa, fy, fx);
-          // diagonal tile: A in fp32, transposed, strictly lower part only
-          float4 col;
-          col.x = acc_row(0) > acc_col() ? aa[0] : 0.f;
-          col.y = acc_row(1) > acc_col() ? aa[1] : 0.f;
-          col.z = acc_row(2) > acc_col() ? aa[2] : 0.f;
-          col.w = acc_row(3) > acc_col() ? aa[3] : 0.f;
           float* Ad = Am + a * 16 * G::LDD;
-          *reinterpret_cast<float4*>(Ad + acc_col() * G::LDD + acc_row(0)) = col;
-          // P^T element (t' = row, t = column) kept where t' <= t
-          f32x4 pm;
+          // (decay variants: a diagonal summed exactly in the decay pass is
+          // already in place, in the buffer and in the workspace)
+          bool from_mfma = true;
+          if constexpr (kDecay) from_mfma = !ex_diag;
+          if (from_mfma) {
+            // diagonal tile: A in fp32, transposed, strictly lower part only
+            float4 col;
+            col.x = acc_row(0) > acc_col() ? aa[0] : 0.f;
+            col.y = acc_row(1) > acc_col() ? aa[1] : 0.f;
+            col.z = acc_row(2) > acc_col() ? aa[2] : 0.f;
+            col.w = acc_row(3) > acc_col() ? aa[3] : 0.f;
+            *reinterpret_cast<float4*>(Ad + acc_col() * G::LDD + acc_row(0)) = col;
+            // P^T element (t' = row, t = column) kept where t' <= t
+            f32x4 pm;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pm[i] = acc_row(i) <= acc_col() ? pa[i] : 0.f;
-          Frag<C, Tin>::store_acc_tile(prow + (size_t)a * 16 * C, a, pm);
+            for (int i = 0; i < 4; ++i) pm[i] = acc_row(i) <= acc_col() ? pa[i] : 0.f;
+            Frag<C, Tin>::store_acc_tile(prow + (size_t)a * 16 * C, a, pm);
+          }
           // T's diagonal block by forward substitution: lane c < 16 owns
           // column c; pending sums are updated as soon as each entry is final.
           wave_lds_sync();
@@ -633,20 +778,13 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         Frag<C, Tin> fx;
         fx.load_kmajor_perm(Xs + db * 16, LDK);  // the scan's k order
         if constexpr (kDecay) {
-          const float gd = gC[db * 16 + (lane & 15)];
-          if constexpr (sizeof(Tin) == 2) {
+          // exit keys x_i gamma_C / gamma_i = X_i exp(lambda_C - lambda_{e_b})
+          const int c = db * 16 + (lane & 15);
+          float fb[TB];
 #pragma unroll
-            for (int i = 0; i < Frag<C, Tin>::N32; ++i)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) fx.v[i][e] = (__bf16)((float)fx.v[i][e] * gd);
-            if constexpr (Frag<C, Tin>::R16) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) fx.t[e] = (__bf16)((float)fx.t[e] * gd);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < C / 4; ++i) fx.v[i] *= gd;
-          }
+          for (int b2 = 0; b2 < TB; ++b2)
+            fb[b2] = __expf(Leb[(TB - 1) * DK + c] - Leb[b2 * DK + c]);
+          scale_kperm_frag(fx, [&](int t) { return fb[t >> 4]; });
         }
         fx.store_global(wb.xp + xoff + (size_t)db * 16 * C);
       }
@@ -655,6 +793,28 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       }
     }
     __syncthreads();
+    if constexpr (kDecay) {
+      // read keys and queries relative to the chunk start from here on (for
+      // Wk and the decayed queries): times exp(lambda_{s_b}) <= 1
+      constexpr int VEC = G::VEC;
+      for (int item = tid; item < C * (DK / VEC); item += G::NT) {
+        const int t = item / (DK / VEC), c0 = (item % (DK / VEC)) * VEC;
+        const float* ls = Lsb + (t >> 4) * DK + c0;
+        uint4 y4 = *reinterpret_cast<const uint4*>(Ys + t * LDK + c0);
+        uint4 q4 = *reinterpret_cast<const uint4*>(Qs + t * LDK + c0);
+        Tin* yv = reinterpret_cast<Tin*>(&y4);
+        Tin* qv = reinterpret_cast<Tin*>(&q4);
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+          const float f = __expf(ls[u]);
+          yv[u] = from_f32<Tin>(f * to_f32(yv[u]));
+          qv[u] = from_f32<Tin>(f * to_f32(qv[u]));
+        }
+        *reinterpret_cast<uint4*>(Ys + t * LDK + c0) = y4;
+        *reinterpret_cast<uint4*>(Qs + t * LDK + c0) = q4;
+      }
+      __syncthreads();  // the doubling overwrites the block table
+    }
 
 
     // ---- recursive doubling, T21 = -T22 (A21 T11) ----------------------------

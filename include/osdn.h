@@ -191,9 +191,11 @@ int gdn2_forward_supported(int Dk, int Dv, int chunk, int dtype);
  *   S0         [B,H,Dk,Dv] fp32     (NULL: zeros)
  *   o          [B,H,T,Dv] dtype     (required)
  *   S_T        [B,H,Dk,Dv] fp32     (NULL: not written)
- * Inside a chunk the decay is absorbed into the keys as k / gamma_t with
- * gamma_t the running product of alpha; the sum of log_alpha over one chunk
- * must stay above about -80 per channel so that 1/gamma_t is finite in fp32.
+ * Any log_alpha <= 0 is accepted ([GDN2-it] method part 3: the decay is
+ * absorbed into the erase and write factors): inside a chunk each factor
+ * gamma_t / gamma_i is split at 16-token block boundaries so that every
+ * stored factor is at most 1, and a block whose own decay exceeds e^-60 in
+ * some channel has its diagonal entries summed exactly, element by element.
  * S_T may be exactly S0; no other overlap is allowed.
  * workspace / workspace_bytes: device scratch of at least
  * gdn2_forward_workspace_bytes(...) bytes, 256-byte aligned, not overlapping
@@ -236,9 +238,8 @@ size_t osdn_gated_forward_workspace_bytes(int B, int H, int T, int Dk, int Dv,
  *   o_t = scale * S_t q_t,  k~_t = d_t*k_t,  d as in osdn_forward,
  * alpha_t = exp(log_alpha_t) per key channel (a per-head scalar decay is the
  * case of equal channels). Arguments as in osdn_forward, plus
- *   log_alpha [B,H,T,Dk] fp32 (required; <= 0 for a decay; its sum over one
- *             chunk must stay above about -80 per channel, as for
- *             gdn2_forward).
+ *   log_alpha [B,H,T,Dk] fp32 (required; <= 0 for a decay, of any
+ *             strength, as for gdn2_forward).
  * State [B,H,Dv,Dk] as in osdn_forward; S_T may be exactly S0 and d_T exactly
  * d0. Runs phase 1, then the chunked engine with the decay absorbed into the
  * keys (at chunk 64 the engine forms the preconditioned keys itself from the

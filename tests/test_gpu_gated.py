@@ -141,3 +141,26 @@ def test_gated_decode_continues_forward():
     ro, rS, rd = oracle(inp)
     check((f64(o), f64(S), f64(d)), (ro[:, :, cut:], rS, rd), "bf16",
           "gated forward then decode")
+
+
+@pytest.mark.parametrize("chunk,dtype", [(64, "bf16"), (16, "bf16"), (64, "f32")])
+def test_gated_strong_decay(chunk, dtype):
+    """OSDN on a decaying backbone with strong decays (log alpha = -2
+    everywhere; random in (-6, 0); blocks at -8 that take the exact
+    diagonal sums), at the fused chunk 64 and the materialised-K~ chunk 16."""
+    dk, dv = (128, 128) if dtype == "bf16" else (32, 32)
+    w = BASE.scaled(B=1, H=2, T=64 * 3 + 9, chunk=chunk, dtype=dtype, Dk=dk,
+                    Dv=dv)
+    inp = W.make_inputs(w)
+    la0 = inp["log_alpha"]
+    g = np.random.default_rng(12)
+    mixed = la0.clone()
+    for t0 in (16, 80, 144):
+        mixed[:, :, t0:t0 + 16] = -8.0
+    cases = [("log alpha = -2", torch.full_like(la0, -2.0)),
+             ("log alpha in (-6, 0)",
+              torch.from_numpy((-6.0 * g.random(la0.shape)).astype(np.float32))),
+             ("blocks at -8", mixed)]
+    for name, la in cases:
+        inp["log_alpha"] = la
+        check(gpu(inp), oracle(inp), dtype, "%s C=%d %s" % (name, chunk, dtype))

@@ -119,3 +119,40 @@ def test_gdn2_full_size_all_streams():
     o, S = run(inp)
     ro, rS = oracle(inp)
     check_full("gdn2 full size", "bf16", o, ro, S, rS)
+
+
+def _decay_cases(w, seed):
+    """Strong decays: log alpha = -2 on every token and channel (a chunk of
+    64 sums to -128); log alpha in (-6, 0) at random; and -8 on the tokens
+    of a few 16-token blocks (a block decays by e^-120 there, so its
+    diagonal tile is summed element by element) with the workload's decay
+    elsewhere."""
+    la0 = W.make_inputs(w)["log_alpha"]
+    g = np.random.default_rng(seed)
+    strong = torch.full_like(la0, -2.0)
+    rand = torch.from_numpy((-6.0 * g.random(la0.shape)).astype(np.float32))
+    mixed = la0.clone()
+    for t0 in (16, 80, 144):
+        if t0 < w.T:
+            mixed[:, :, t0:t0 + 16] = -8.0
+    mixed[:, 1:, :, : w.Dk // 2] = -8.0     # half the channels of head 1
+    return [("log alpha = -2", strong), ("log alpha in (-6, 0)", rand),
+            ("blocks at -8", mixed)]
+
+
+@pytest.mark.parametrize("chunk,dtype", [(64, "bf16"), (32, "bf16"), (16, "bf16"),
+                                         (16, "f32"), (64, "f32")])
+def test_gdn2_strong_decay(chunk, dtype):
+    """Any log alpha <= 0: the in-chunk decay is split at 16-token blocks so
+    every factor stays finite; the GPU matches the oracle to the usual
+    bound (decays too strong for the factored diagonal are summed exactly)."""
+    dk, dv = (128, 128) if dtype == "bf16" else (32, 32)
+    w = BASE.scaled(B=1, H=2, T=64 * 3 + 9, chunk=chunk, dtype=dtype, Dk=dk,
+                    Dv=dv)
+    if not osdn.load_library().gdn2_forward_supported(
+            dk, dv, chunk, 1 if dtype == "bf16" else 0):
+        pytest.skip("no kernel instance for this size")
+    inp = W.make_inputs(w)
+    for name, la in _decay_cases(w, 11):
+        inp["log_alpha"] = la
+        check(run(inp), oracle(inp), dtype, "%s C=%d %s" % (name, chunk, dtype))
