@@ -12,7 +12,8 @@ import os
 
 import torch
 
-__all__ = ["osdn_forward", "osdn_precond_scan", "osdn_chunk_forward",
+__all__ = ["osdn_forward", "osdn_forward_noalloc", "osdn_precond_scan",
+           "osdn_chunk_forward",
            "gdn2_forward", "osdn_gated_forward", "osdn_decode",
            "gdn2_decode",
            "workspace_bytes", "precond_workspace_bytes", "supported",
@@ -86,6 +87,9 @@ def load_library():
     L.osdn_decode.restype = I
     L.gdn2_decode.argtypes = [I] * 6 + [P, P, P, P, P, P, P, F, P, P]
     L.gdn2_decode.restype = I
+    L.osdn_forward_noalloc.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, F,
+                                                  P, P, P, P, P, P])
+    L.osdn_forward_noalloc.restype = I
     L.osdn_kernel_timing.argtypes = [I]
     L.osdn_kernel_timing.restype = None
     L.osdn_kernel_times.argtypes = [I, P, P, P]
@@ -203,6 +207,51 @@ def osdn_forward(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None, chunk=64,
         raise OsdnError(rc, "osdn_forward")
     if diagnostics:
         return o, S_T, d_T, rho, qg
+    return o, S_T, d_T
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # OSDN_NOALLOC_SCRATCH_BYTES
+
+
+def osdn_forward_noalloc(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None,
+                         chunk=64, scale=1.0, out=None):
+    """osdn_forward on the library's static per-device scratch (no workspace
+    argument, nothing allocated by the call itself when ``out`` is given):
+    returns (o, S_T, d_T). Raises OsdnError (workspace) when the sizes need
+    more than NOALLOC_SCRATCH_BYTES of scratch. Calls that overlap in time
+    on one device share that scratch and must be ordered by the caller."""
+    L = load_library()
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), torch.float32, dev)
+    _check(r, "r", (B, H, T), torch.float32, dev)
+    _check(d0, "d0", (B, H, Dk), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    if out is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+        d_T = torch.empty((B, H, Dk), dtype=torch.float32, device=dev)
+    else:
+        o, S_T, d_T = out
+    _check(o, "o", (B, H, T, Dv), dt, dev)
+    _check(S_T, "S_T", (B, H, Dv, Dk), torch.float32, dev)
+    _check(d_T, "d_T", (B, H, Dk), torch.float32, dev)
+    rc = L.osdn_forward_noalloc(B, H, T, Dk, Dv, chunk, _DTYPE_CODE[dt],
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                                float(eta), _ptr(d0), _ptr(S0), float(scale),
+                                _ptr(o), _ptr(S_T), _ptr(d_T), None, None,
+                                _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_forward_noalloc")
     return o, S_T, d_T
 
 

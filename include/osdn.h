@@ -123,6 +123,29 @@ int osdn_forward(int B, int H, int T, int Dk, int Dv, int chunk, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (work captured into HIP
+ * graphs, tight serving loops, harnesses that forbid hipMalloc):
+ * osdn_forward with the library's own static device scratch in place of a
+ * caller workspace. Arguments, layouts, results and status codes as in
+ * osdn_forward, without workspace / workspace_bytes. The scratch holds
+ * OSDN_NOALLOC_SCRATCH_BYTES bytes per device (held from library load until
+ * the process ends); sizes whose osdn_forward_workspace_bytes exceeds it
+ * return OSDN_ERR_WORKSPACE before anything is launched. Nothing is
+ * allocated: the first call on a device looks up that device's scratch
+ * address once. Every call on one device shares that device's scratch and
+ * leaves its contents behind (no call needs it cleared): calls that overlap
+ * in time on one device (other streams, other threads) race on it and must
+ * be ordered by the caller.
+ */
+#define OSDN_NOALLOC_SCRATCH_BYTES (128u << 20)
+int osdn_forward_noalloc(int B, int H, int T, int Dk, int Dv, int chunk,
+                         int dtype, const void* q, const void* k, const void* v,
+                         const float* beta, const float* r, float eta,
+                         const float* d0, const float* S0, float scale,
+                         void* o, float* S_T, float* d_T, float* rho,
+                         float* q_geo, void* stream);
+
+/*
  * Device scratch, in bytes, that osdn_precond_scan needs (0 if the sizes are
  * invalid or T = 0): per chunk of 64 tokens and (batch, head), a fp32 record
  * of the gate prefix, the step sizes and the 64 x 64 matrix that maps the

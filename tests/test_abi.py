@@ -346,3 +346,27 @@ def test_fp32_chunk64_workspace_regression():
     p2 = L.osdn_chunk_workspace_bytes(2, 3, 448, 64, 64, 64, 0)
     assert p1 + p2 == 3473664
     assert L.osdn_forward_workspace_bytes(2, 3, 448, 64, 64, 64, 0) == p1 + p2
+
+
+@needs_lib
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """osdn_forward_noalloc checks the size against its static scratch before
+    touching any device (the fake pointers below are never dereferenced)."""
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    I, F = ctypes.c_int, ctypes.c_float
+    L.osdn_forward_noalloc.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, F,
+                                                  P, P, P, P, P, P])
+    cap = osdn.NOALLOC_SCRATCH_BYTES
+    assert cap == 128 << 20
+    # the 1.3B-layer workload needs about 300 MB of scratch: rejected
+    assert L.osdn_forward_workspace_bytes(4, 16, 4096, 128, 128, 64, 1) > cap
+    args = (0x10000, 0x20000, 0x30000, 0x40000, None, 0.1, None, None, 1.0,
+            0x50000, None, None, None, None, None)
+    assert L.osdn_forward_noalloc(4, 16, 4096, 128, 128, 64, 1, *args) == WORKSPACE
+    assert L.osdn_forward_noalloc(1, 1, 64, 48, 32, 16, 1, *args) == UNSUPPORTED
+    assert L.osdn_forward_noalloc(1, 1, -1, 32, 32, 16, 1, *args) == BAD_DIMS
+    # nothing to do: no pointer needed, no device touched
+    assert L.osdn_forward_noalloc(0, 1, 64, 32, 32, 16, 1, *((None,) * 4),
+                                  None, 0.1, None, None, 1.0, *((None,) * 5),
+                                  None) == OK
