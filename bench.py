@@ -123,7 +123,7 @@ def kernel_bytes_per_token_head(w):
     s = _s(w)
     dk, dv, C, C1 = w.Dk, w.Dv, w.chunk, PRECOND_CHUNK
     gates = 4 + (4 if w.apf else 0)
-    rec = (2 * C1 + 4 + C1 * C1) * 4.0 / C1   # phase-1 chunk record
+    rec = (3 * C1 + 8 + C1 * C1) * 4.0 / C1   # phase-1 chunk record
     dent = dk * 4.0 / C1                       # d at each chunk entry
     frags = (2 * dk + dv + C) * s
     frags_g = frags + dk * s + 4.0 * dk / C

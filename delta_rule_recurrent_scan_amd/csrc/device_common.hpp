@@ -368,13 +368,14 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Sum over the lanes that share l % P (P = 4, 8, 16); every lane receives
-// the sum of its class. Rotations within each row of 16 lanes, then the
-// cross-row swaps.
+// Sum over the lanes that share l % P (P = 2, 4, 8, 16); every lane
+// receives the sum of its class. Rotations within each row of 16 lanes, then
+// the cross-row swaps.
 template <int P>
 __device__ __forceinline__ float strided_sum(float x) {
-  static_assert(P == 4 || P == 8 || P == 16, "stride");
-  if constexpr (P == 4) x += dpp_f<0x124>(x);  // row_ror:4
+  static_assert(P == 2 || P == 4 || P == 8 || P == 16, "stride");
+  if constexpr (P == 2) x += dpp_f<0x122>(x);  // row_ror:2
+  if constexpr (P <= 4) x += dpp_f<0x124>(x);  // row_ror:4
   if constexpr (P <= 8) x += dpp_f<0x128>(x);  // row_ror:8
   return add_swap32(add_swap16(x));
 }

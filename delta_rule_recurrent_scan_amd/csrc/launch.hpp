@@ -9,10 +9,16 @@ namespace osdn {
 
 // Phase-1 chunk length and the layout of its per-chunk fp32 record
 // {lp_0..lp_C (lp_t = log of the gate product before token t), 3 pad,
-// g (C step sizes), V (C x C)}; the entry values of d follow all records.
+// g (C step sizes), V (C x C), c_t = P_C / P_{t+1} (C gate ratios), P_C,
+// 3 pad}; the entry values of d follow all records. Every field starts on a
+// 16-byte boundary.
 constexpr int kPrecondChunk = 64;
 constexpr int kRecLp = 0, kRecG = kPrecondChunk + 4, kRecV = 2 * kPrecondChunk + 4;
-constexpr int kRecStride = 2 * kPrecondChunk + 4 + kPrecondChunk * kPrecondChunk;
+constexpr int kRecCf = kRecV + kPrecondChunk * kPrecondChunk;
+constexpr int kRecPc = kRecCf + kPrecondChunk;
+constexpr int kRecStride = kRecPc + 4;
+static_assert(kRecV % 4 == 0 && kRecCf % 4 == 0 && kRecStride % 4 == 0,
+              "record fields on 16-byte boundaries");
 
 struct PrecondArgs {
   int B, H, T, Dk;

@@ -48,7 +48,8 @@ struct P1Cfg {
   static_assert((C * NCB) % NT == 0, "whole key blocks per thread");
   // chunk record (fp32): lp_0..lp_C (lp_t = log P_t), g (g0 from prep,
   // replaced by g in the chain), V (C x C, zero above the diagonal)
-  static constexpr int R_LP = kRecLp, R_G = kRecG, R_V = kRecV;
+  static constexpr int R_LP = kRecLp, R_G = kRecG, R_V = kRecV, R_CF = kRecCf,
+                       R_PC = kRecPc;
   static constexpr int RS = kRecStride;
   // prep: split squares (bf16), then T and the doubling scratch in their place
   static constexpr int LDH = DK + 8;
@@ -298,8 +299,10 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
       }
     }
 
-    // ---- chunk record: lp, g0 = T e, V = T diag(h) ---------------------------
+    // ---- chunk record: lp, g0 = T e, V = T diag(h), gate ratios -------------
     for (int e = tid; e <= C; e += G::NT) out[G::R_LP + e] = lpv[e];
+    for (int e = tid; e < C; e += G::NT) out[G::R_CF + e] = expf(lpv[C] - lpv[e + 1]);
+    if (tid == 0) out[G::R_PC] = expf(lpv[C]);
     {
       // four threads per row, one 16-wide block each (zero above the diagonal)
       const int t = tid >> 2, q = tid & 3;
@@ -330,6 +333,16 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
 // ---------------------------------------------------------------------------
 // chain: the serial recurrence over the chunks of one (batch, head)
 // ---------------------------------------------------------------------------
+// Buffer resource over `bytes` bytes from `base` (raw, no stride); loads
+// through it take a per-chunk scalar base and 32-bit per-lane offsets that
+// stay the same from one chunk to the next.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Two consecutive key channels of one token as one LDS read (the d update
+// reads the keys by channel pair).
 template <typename Tin>
 struct KeyPair;
 template <>
@@ -359,46 +372,64 @@ struct ChainRegs {
   // the row of V.
   static constexpr int TPR = NT / C;
   static constexpr int SEG1 = DK / TPR;
-  static constexpr int NR1 = SEG1 * sizeof(Tin) / 16;
+  static constexpr int VEC = 16 / (int)sizeof(Tin);
+  static constexpr int NR1 = SEG1 / VEC;
   static constexpr int NV = C / TPR;
-  static_assert(NR1 >= 1 && NV % 4 == 0, "whole 16-byte loads");
+  static_assert(NR1 >= 1 && SEG1 % VEC == 0 && NV % 4 == 0, "whole 16-byte loads");
   // d update: wave w owns channels [w DK/NW, (w+1) DK/NW) as NP pairs; lane l
-  // takes pair l % NP over the token rows of segment l / NP.
+  // takes pair l % NP over the RS3 token rows of segment l / NP.
   static constexpr int NP = DK / (2 * NW), NSG = 64 / NP, RS3 = C / NSG;
   static_assert(NP == 4 || NP == 8 || NP == 16, "strided lane reduction");
   using Pair = typename KeyPair<Tin>::T;
+  static constexpr unsigned ES = sizeof(Tin);
+  // The chunk's raw keys, copied to LDS by the x section (which loads each
+  // row slice once) for the d update: DW dwords per row, unpadded, each row
+  // rotated by ROT dwords per d-update segment of its token, so that the 64
+  // lanes of a d-update read (NSG segments x NP pairs) meet 64 different
+  // banks; rotations are multiples of 4 dwords, so 16-byte writes stay
+  // aligned and whole.
+  static constexpr int DW = DK * (int)sizeof(Tin) / 4;
+  static constexpr int PDW = (int)sizeof(Tin) / 2;  // dwords per channel pair
+  static constexpr int ROT = NP * PDW;
+  static_assert(ROT % 4 == 0, "rotation keeps 16-byte pieces whole");
+  __device__ __forceinline__ static int kpos(int t, int dw) {
+    return t * DW + ((dw + ROT * (t / RS3)) & (DW - 1));
+  }
 
   uint4 kr[NR1];
-  Pair kc[RS3];
   float4 vr[NV / 4];
-  float g0, lpt1, lpC;
+  float g0, cf, pc;
 
-  // Loads are unconditional, so that the compiler can count them and a
-  // prefetch is only waited on where its data is used: rows past the end of
-  // the sequence read the last valid row instead (their g is zero, so they
-  // add nothing), and V is stored in full (zero above the diagonal blocks).
-  // kb: the keys of this (batch, head); r0: the chunk's first row; rc: the
-  // chunk's record. Offsets are 32-bit (a (batch, head) holds under 2^32
-  // elements), which keeps the per-lane address arithmetic short.
-  __device__ __forceinline__ void load(const Tin* kb, const float* rc, int r0,
-                                       int valid, int t, int q, int c3, int sg) {
-    const unsigned tr = (unsigned)(r0 + min(t, valid - 1));
+  // Chunk operands, through buffer resources based at the chunk's first key
+  // row (rk) and at its record (rr). TAIL: the chunk holds `valid` < C rows;
+  // rows past the end read the last valid row instead (their step size is
+  // zero, so they add nothing), which keeps the loads unconditional.
+  template <bool TAIL>
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rr,
+                                       int valid, int t, int q) {
+    const unsigned row = TAIL ? (unsigned)min(t, valid - 1) : (unsigned)t;
 #pragma unroll
     for (int i = 0; i < NR1; ++i)
-      kr[i] = *reinterpret_cast<const uint4*>(
-          kb + (tr * DK + (unsigned)(q * SEG1 + i * (16 / (int)sizeof(Tin)))));
+      kr[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rk, (row * DK + (unsigned)(q * SEG1 + i * VEC)) * ES, 0, 0));
+    // V is zero above its 16 x 16 block diagonal: only lanes whose columns
+    // reach row t's block load (the rest hold zeros)
+    const bool vlive = NV * q < 16 * (t / 16 + 1);
 #pragma unroll
-    for (int m = 0; m < RS3; ++m) {
-      const unsigned row = (unsigned)(r0 + min(sg * RS3 + m, valid - 1));
-      kc[m] = *reinterpret_cast<const Pair*>(kb + (row * DK + (unsigned)c3));
+    for (int i = 0; i < NV / 4; ++i) {
+      vr[i] = float4{0.f, 0.f, 0.f, 0.f};
+      if (vlive)
+        vr[i] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(
+                        rr, (unsigned)(G::R_V + t * C + NV * q + 4 * i) * 4u, 0, 0));
     }
-#pragma unroll
-    for (int i = 0; i < NV / 4; ++i)
-      vr[i] = *reinterpret_cast<const float4*>(
-          rc + (unsigned)(G::R_V + t * C + NV * q + 4 * i));
-    g0 = rc[(unsigned)(G::R_G + t)];
-    lpt1 = rc[(unsigned)(G::R_LP + t + 1)];
-    lpC = rc[G::R_LP + C];
+    g0 = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rr, (unsigned)(G::R_G + t) * 4u, 0, 0));
+    cf = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rr, (unsigned)(G::R_CF + t) * 4u, 0, 0));
+    pc = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rr, (unsigned)G::R_PC * 4u, 0, 0));
   }
 };
 
@@ -410,29 +441,45 @@ __global__ __launch_bounds__(64 * chain_waves<DK>()) void precond_chain_kernel(
   using R = ChainRegs<DK, Tin>;
   using KP = KeyPair<Tin>;
   constexpr int C = G::C, NT = R::NT, TPR = R::TPR;
-  __shared__ float dv[DK], xs[C], cgs[C];
+  __shared__ __attribute__((aligned(16))) float dv[DK];
+  __shared__ float xs[C], cgs[C];
+  __shared__ __attribute__((aligned(16))) unsigned Ks[C * R::DW];
   const int bh = blockIdx.x, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int t = tid / TPR, q = tid % TPR;
   const int sg = lane / R::NP;
   const int c3 = wave * (DK / R::NW) + 2 * (lane % R::NP);
 
-  for (int c = tid; c < DK; c += NT) dv[c] = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
+  const Tin* kb = k + (size_t)bh * T * DK;
+  float* recb = rec + (size_t)bh * nchunks * G::RS;
+  float* dentb = dent + (size_t)bh * nchunks * DK;
+  for (int c = tid; c < DK; c += NT) {
+    const float x = d0in ? d0in[(size_t)bh * DK + c] : 1.f;
+    dv[c] = x;
+    if (nchunks > 0) dentb[c] = x;  // d at the entry of chunk 0
+  }
   __syncthreads();
 
-  auto recp = [&](int jj) { return rec + ((size_t)bh * nchunks + jj) * G::RS; };
-  const Tin* kb = k + (size_t)bh * T * DK;
+  const int nfull = T / C;  // chunks with C valid rows
   auto fetch_chunk = [&](R& r, int jj) {
-    r.load(kb, recp(jj), jj * C, min(C, T - jj * C), t, q, c3, sg);
+    const int valid = min(C, T - jj * C);
+    const auto rk = chunk_rsrc(kb + (size_t)jj * C * DK, (unsigned)(valid * DK) * R::ES);
+    const auto rr = chunk_rsrc(recb + (size_t)jj * G::RS, (unsigned)G::RS * 4u);
+    if (jj < nfull)
+      r.template load<false>(rk, rr, C, t, q);
+    else
+      r.template load<true>(rk, rr, valid, t, q);
   };
   // One chunk: `cur` holds chunk jj (fetched two chunks before); chunk jj + 2
   // is fetched into `fetch` at the start (the last chunk again near the end).
   auto step = [&](int jj, R& fetch, const R& cur) {
     fetch_chunk(fetch, min(jj + 2, nchunks - 1));
-    float* rc = recp(jj);
-    if (tid < DK) dent[((size_t)bh * nchunks + jj) * DK + tid] = dv[tid];
-    // x_t = <d, a_t>
+    float* rc = recb + (size_t)jj * G::RS;
+    // x_t = <d, a_t>; the key row slice also goes to LDS for the d update
     {
       const Tin* kv = reinterpret_cast<const Tin*>(cur.kr);
+#pragma unroll
+      for (int i = 0; i < R::NR1; ++i)
+        *reinterpret_cast<uint4*>(Ks + R::kpos(t, (q * R::NR1 + i) * 4)) = cur.kr[i];
       const float* dq = dv + q * R::SEG1;
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -455,26 +502,31 @@ __global__ __launch_bounds__(64 * chain_waves<DK>()) void precond_chain_kernel(
       const float g = cur.g0 - s;
       if (q == 0) {
         rc[G::R_G + t] = g;
-        cgs[t] = expf(cur.lpC - cur.lpt1) * g;
+        cgs[t] = cur.cf * g;
       }
     }
     __syncthreads();
-    // d <- P_C d + sum_t a_t (c_t g_t)
+    // d <- P_C d + sum_t a_t (c_t g_t); the new d is the next chunk's entry
     {
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int m = 0; m < R::RS3; ++m) {
-        const float cg = cgs[sg * R::RS3 + m];
-        const float x0 = KP::lo(cur.kc[m]), x1 = KP::hi(cur.kc[m]);
+        const int tt = sg * R::RS3 + m;
+        const float cg = cgs[tt];
+        const typename R::Pair kp = *reinterpret_cast<const typename R::Pair*>(
+            Ks + R::kpos(tt, c3 * R::PDW / 2));
+        const float x0 = KP::lo(kp), x1 = KP::hi(kp);
         s0 += x0 * x0 * cg;
         s1 += x1 * x1 * cg;
       }
       s0 = strided_sum<R::NP>(s0);
       s1 = strided_sum<R::NP>(s1);
       if (sg == 0) {
-        const float PC = expf(cur.lpC);
-        dv[c3] = PC * dv[c3] + s0;
-        dv[c3 + 1] = PC * dv[c3 + 1] + s1;
+        const float2 od = *reinterpret_cast<const float2*>(dv + c3);
+        const float2 nd = float2{cur.pc * od.x + s0, cur.pc * od.y + s1};
+        *reinterpret_cast<float2*>(dv + c3) = nd;
+        if (jj + 1 < nchunks)
+          *reinterpret_cast<float2*>(dentb + (size_t)(jj + 1) * DK + c3) = nd;
       }
     }
     __syncthreads();

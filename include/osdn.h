@@ -148,8 +148,9 @@ int osdn_forward_noalloc(int B, int H, int T, int Dk, int Dv, int chunk,
 /*
  * Device scratch, in bytes, that osdn_precond_scan needs (0 if the sizes are
  * invalid or T = 0): per chunk of 64 tokens and (batch, head), a fp32 record
- * of the gate prefix, the step sizes and the 64 x 64 matrix that maps the
- * chunk's entry preconditioner to its step sizes, plus that entry value.
+ * of the gate prefix, the step sizes, the 64 x 64 matrix that maps the
+ * chunk's entry preconditioner to its step sizes and the gate ratios that
+ * carry each step to the chunk's end, plus that entry value.
  */
 size_t osdn_precond_workspace_bytes(int B, int H, int T, int Dk, int dtype);
 
