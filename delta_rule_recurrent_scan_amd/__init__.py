@@ -12,7 +12,7 @@ import os
 
 import torch
 
-__all__ = ["osdn_forward", "osdn_forward_noalloc", "osdn_precond_scan",
+__all__ = ["osdn_forward", "osdn_forward_noalloc", "osdn_backward", "osdn_precond_scan",
            "osdn_chunk_forward",
            "gdn2_forward", "osdn_gated_forward", "osdn_decode",
            "gdn2_decode",
@@ -90,6 +90,11 @@ def load_library():
     L.osdn_forward_noalloc.argtypes = ([I] * 7 + [P, P, P, P, P, F, P, P, F,
                                                   P, P, P, P, P, P])
     L.osdn_forward_noalloc.restype = I
+    L.osdn_backward_workspace_bytes.argtypes = [I] * 5
+    L.osdn_backward_workspace_bytes.restype = Z
+    L.osdn_backward.argtypes = ([I] * 6 + [P, P, P, P, P, F, P, P, F, P, P, P]
+                                + [P] * 8 + [P, Z, P])
+    L.osdn_backward.restype = I
     L.osdn_kernel_timing.argtypes = [I]
     L.osdn_kernel_timing.restype = None
     L.osdn_kernel_times.argtypes = [I, P, P, P]
@@ -253,6 +258,66 @@ def osdn_forward_noalloc(q, k, v, beta, r=None, eta=0.1, d0=None, S0=None,
     if rc != 0:
         raise OsdnError(rc, "osdn_forward_noalloc")
     return o, S_T, d_T
+
+
+def backward_workspace_bytes(B, H, T, Dk, Dv):
+    return int(load_library().osdn_backward_workspace_bytes(B, H, T, Dk, Dv))
+
+
+def osdn_backward(q, k, v, beta, dout, r=None, eta=0.1, d0=None, S0=None,
+                  dS_T=None, dd_T=None, scale=1.0, out=None, workspace=None):
+    """Backward of osdn_forward on the GPU: the gradient of
+    sum <dout, o> + <dS_T, S_T> + <dd_T, d_T> with respect to every input.
+
+    Inputs as in osdn_forward; dout [B,H,T,Dv] in the dtype of q; dS_T
+    [B,H,Dv,Dk] and dd_T [B,H,Dk] fp32 (None: zero). Returns a dict of fp32
+    tensors q, k, v [B,H,T,*], beta, r [B,H,T], eta [B,H] (per stream; sum
+    it for the shared scalar), d0 [B,H,Dk], S0 [B,H,Dv,Dk]. ``out`` may pass
+    such a dict preallocated and ``workspace`` a uint8 device buffer of
+    backward_workspace_bytes().
+    """
+    L = load_library()
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    f32 = torch.float32
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), f32, dev)
+    _check(r, "r", (B, H, T), f32, dev)
+    _check(d0, "d0", (B, H, Dk), f32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), f32, dev)
+    _check(dout, "dout", (B, H, T, Dv), dt, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), f32, dev)
+    _check(dd_T, "dd_T", (B, H, Dk), f32, dev)
+    shapes = dict(q=(B, H, T, Dk), k=(B, H, T, Dk), v=(B, H, T, Dv),
+                  beta=(B, H, T), r=(B, H, T), eta=(B, H), d0=(B, H, Dk),
+                  S0=(B, H, Dv, Dk))
+    g = out if out is not None else {
+        n: torch.empty(s, dtype=f32, device=dev) for n, s in shapes.items()}
+    for n, s in shapes.items():
+        if g.get(n) is None:
+            raise ValueError("out must hold a tensor for %s" % n)
+        _check(g[n], "out[%s]" % n, s, f32, dev)
+    need = L.osdn_backward_workspace_bytes(B, H, T, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = L.osdn_backward(B, H, T, Dk, Dv, _DTYPE_CODE[dt], _ptr(q), _ptr(k),
+                         _ptr(v), _ptr(beta), _ptr(r), float(eta), _ptr(d0),
+                         _ptr(S0), float(scale), _ptr(dout), _ptr(dS_T),
+                         _ptr(dd_T), _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]),
+                         _ptr(g["beta"]), _ptr(g["r"]), _ptr(g["eta"]),
+                         _ptr(g["d0"]), _ptr(g["S0"]), _ptr(workspace),
+                         workspace.numel(), _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_backward")
+    return g
 
 
 def precond_workspace_bytes(B, H, T, Dk, dtype):

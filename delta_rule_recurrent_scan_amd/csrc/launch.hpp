@@ -82,6 +82,31 @@ struct DecodeArgs {
   void* o;                  // [B,H,T,Dv]
 };
 
+// Arguments of the OSDN backward (the adjoint of the token recurrence):
+// inputs as in the forward plus the output adjoints; gradients fp32 in the
+// inputs' layouts, eta's per (batch, head).
+struct BackwardArgs {
+  int B, H, T, Dk, Dv;
+  int bf16;
+  const void* q;            // [B,H,T,Dk]
+  const void* k;            // [B,H,T,Dk]
+  const void* v;            // [B,H,T,Dv]
+  const float* beta;        // [B,H,T]
+  const float* r;           // [B,H,T] or null (ones)
+  float eta;
+  const float* d0;          // [B,H,Dk] or null (ones)
+  const float* S0;          // [B,H,Dv,Dk] or null (zeros)
+  float scale;
+  const void* dout;         // [B,H,T,Dv], dtype of q
+  const float* dST;         // [B,H,Dv,Dk] or null (zeros)
+  const float* ddT;         // [B,H,Dk] or null (zeros)
+  float *dq, *dk, *dv;      // [B,H,T,Dk], [B,H,T,Dk], [B,H,T,Dv]
+  float *dbeta, *dr;        // [B,H,T]
+  float* deta;              // [B,H]
+  float *dd0, *dS0;         // [B,H,Dk], [B,H,Dv,Dk]
+  void* ws;                 // backward_workspace_bytes
+};
+
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
 // (dims, dtype) combination has no kernel instance.
 int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
@@ -101,6 +126,10 @@ int launch_osdn_gated_fused(const ChunkArgs& a, hipStream_t s);
 bool gated_fused_supported(int Dk, int Dv, int bf16);
 int launch_gdn2_chunk(const ChunkArgs& a, hipStream_t s);
 int launch_decode(const DecodeArgs& a, hipStream_t s);
+// Device scratch of the backward: per token the residual u_t and the
+// preconditioner d_t, and the state every 64 tokens and after the last.
+size_t backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
+int launch_backward(const BackwardArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 // Device scratch of the chunk engine: per chunk, the S0-independent operands

@@ -366,6 +366,54 @@ int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype, const void* q,
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }
 
+size_t osdn_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return 0;
+  return osdn::backward_workspace_bytes(B, H, T, Dk, Dv);
+}
+
+int osdn_backward(int B, int H, int T, int Dk, int Dv, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* beta, const float* r, float eta,
+                  const float* d0, const float* S0, float scale,
+                  const void* dout, const float* dS_T, const float* dd_T,
+                  float* dq, float* dk, float* dv, float* dbeta, float* dr,
+                  float* deta, float* dd0, float* dS0, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  const size_t BH = (size_t)B * H;
+  if (BH > 0 && (!deta || !dd0 || !dS0)) return OSDN_ERR_NULL_ARG;
+  if (BH * T > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk || !dv ||
+                     !dbeta || !dr))
+    return OSDN_ERR_NULL_ARG;
+  if (!dim_ok(Dk) || !dim_ok(Dv) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return OSDN_ERR_UNSUPPORTED;
+  const size_t need = osdn_backward_workspace_bytes(B, H, T, Dk, Dv);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
+  if (BH == 0) return OSDN_OK;
+  const size_t es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(beta, BH * T * 4),
+                       rng(r, r ? BH * T * 4 : 0), rng(d0, d0 ? BH * Dk * 4 : 0),
+                       rng(S0, S0 ? BH * Dv * Dk * 4 : 0),
+                       rng(dout, BH * T * Dv * es),
+                       rng(dS_T, dS_T ? BH * Dv * Dk * 4 : 0),
+                       rng(dd_T, dd_T ? BH * Dk * 4 : 0)};
+  const Range outs[] = {rng(dq, BH * T * Dk * 4), rng(dk, BH * T * Dk * 4),
+                        rng(dv, BH * T * Dv * 4), rng(dbeta, BH * T * 4),
+                        rng(dr, BH * T * 4), rng(deta, BH * 4),
+                        rng(dd0, BH * Dk * 4), rng(dS0, BH * Dv * Dk * 4),
+                        rng(workspace, need)};
+  if (!aliasing_ok(outs, ins, nullptr, 0)) return OSDN_ERR_ALIASING;
+  osdn::BackwardArgs a{B, H, T, Dk, Dv, dtype == OSDN_BF16, q, k, v, beta, r,
+                       eta, d0, S0, scale, dout, dS_T, dd_T, dq, dk, dv, dbeta,
+                       dr, deta, dd0, dS0, workspace};
+  const int rc = osdn::launch_backward(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
 int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype) {
   return gdn2_forward_supported(Dk, Dv, chunk, dtype);
 }

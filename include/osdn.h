@@ -320,6 +320,51 @@ int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype,
                 float* S, float scale, void* o, void* stream);
 
 /*
+ * Backward of the OSDN forward: the reverse-mode adjoint of the token
+ * recurrence of [OSDN-it] sections 2.1-2.3 (the memory update with the
+ * preconditioned key k~ = d * k, and the online learner of d with its
+ * forgetting gate), the same rule osdn_forward and osdn_decode compute.
+ * Given the adjoints of the outputs it returns the gradient of
+ *   L = sum <do, o> + <dS_T, S_T> + <dd_T, d_T>
+ * with respect to every input, the phase-1 preconditioner scan included.
+ *
+ *   q, k, v, beta, r, eta, d0, S0, scale   as in osdn_forward (r NULL: ones;
+ *            d0 NULL: ones; S0 NULL: zeros)
+ *   dout     [B,H,T,Dv]  dtype of q       adjoint of o (required)
+ *   dS_T     [B,H,Dv,Dk] fp32             adjoint of S_T (NULL: zero)
+ *   dd_T     [B,H,Dk]    fp32             adjoint of d_T (NULL: zero)
+ *   dq, dk   [B,H,T,Dk]  fp32 OUT         (required)
+ *   dv       [B,H,T,Dv]  fp32 OUT         (required)
+ *   dbeta    [B,H,T]     fp32 OUT         (required)
+ *   dr       [B,H,T]     fp32 OUT         (required; the gradient at r = 1
+ *                                          when r is NULL)
+ *   deta     [B,H]       fp32 OUT         eta's gradient per (batch, head);
+ *                                          a caller sums it (required)
+ *   dd0      [B,H,Dk]    fp32 OUT         (required)
+ *   dS0      [B,H,Dv,Dk] fp32 OUT         (required)
+ *   workspace  device scratch of osdn_backward_workspace_bytes() bytes,
+ *            256-byte aligned; caller-owned, contents on entry ignored:
+ *            per token the residual v - S k and the preconditioner, and the
+ *            state every 64 tokens and after the last
+ * Where a key is all zero the learner takes no step (as in the forward) and
+ * no gradient flows through its step size. Gradients are fp32 whatever the
+ * input dtype (bf16 inputs are widened; the recurrence runs in fp32). No
+ * output may overlap another output, an input or the workspace
+ * (OSDN_ERR_ALIASING). Dk, Dv in {32, 64, 128}; B*H workgroups, each holding
+ * one (batch, head) state and its adjoint in registers; two kernels (the
+ * forward storing what the reverse needs, then the reverse walk).
+ */
+size_t osdn_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
+int osdn_backward(int B, int H, int T, int Dk, int Dv, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* beta, const float* r, float eta,
+                  const float* d0, const float* S0, float scale,
+                  const void* dout, const float* dS_T, const float* dd_T,
+                  float* dq, float* dk, float* dv, float* dbeta, float* dr,
+                  float* deta, float* dd0, float* dS0, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing for measurement harnesses. While enabled, every entry
  * point records a HIP event on its stream before and after each kernel it
  * launches (two event records per kernel; events are created on first use
@@ -340,7 +385,8 @@ void osdn_kernel_timing(int enable);
  * preconditioned keys itself), wy_scan (phase 2), gdn2_prep, gdn2_scan
  * (GDN-2), gated_prep, gated_prep_fused, gated_scan (OSDN on a decaying
  * backbone),
- * osdn_decode, gdn2_decode (recurrent decode).
+ * osdn_decode, gdn2_decode (recurrent decode), osdn_bwd_record, osdn_bwd
+ * (backward).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

@@ -374,3 +374,47 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     assert L.osdn_forward_noalloc(0, 1, 64, 32, 32, 16, 1, *((None,) * 4),
                                   None, 0.1, None, None, 1.0, *((None,) * 5),
                                   None) == OK
+
+
+@needs_lib
+def test_backward_error_paths_and_workspace():
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    I, F, Z = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.osdn_backward.argtypes = ([I] * 6 + [P, P, P, P, P, F, P, P, F, P, P, P]
+                                + [P] * 8 + [P, Z, P])
+    L.osdn_backward_workspace_bytes.argtypes = [I] * 5
+    L.osdn_backward_workspace_bytes.restype = Z
+    # per token u (Dv) and d (Dk), a state every 64 tokens and after the last
+    for B, H, T, Dk, Dv in ((1, 1, 1, 32, 32), (2, 3, 64, 64, 128),
+                            (1, 2, 65, 128, 32), (2, 1, 0, 32, 64)):
+        nck = (T + 63) // 64
+        want = B * H * (T * (Dk + Dv) + (nck + 1) * Dv * Dk) * 4
+        assert L.osdn_backward_workspace_bytes(B, H, T, Dk, Dv) == want
+    assert L.osdn_backward_workspace_bytes(1, 1, 8, 48, 32) == 0
+    assert L.osdn_backward_workspace_bytes(-1, 1, 8, 32, 32) == 0
+
+    ws_at = 0x4000000
+    need = L.osdn_backward_workspace_bytes(1, 1, 4, 32, 32)
+
+    def bwd(B=1, T=4, Dk=32, q=0x10000, dout=0x60000, dq=0x100000,
+            dS0=0x900000, ws=ws_at, wsb=need, beta=0x40000, dST=None):
+        return L.osdn_backward(B, 1, T, Dk, 32, 1, q, 0x20000, 0x30000, beta,
+                               None, 0.1, None, None, 1.0, dout, dST, None,
+                               dq, 0x200000, 0x300000, 0x400000, 0x500000,
+                               0x600000, 0x700000, dS0, ws, wsb, None)
+    assert bwd(q=None) == NULL_ARG
+    assert bwd(dout=None) == NULL_ARG
+    assert bwd(dS0=None) == NULL_ARG
+    assert bwd(T=-1) == BAD_DIMS
+    assert bwd(Dk=48) == UNSUPPORTED
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(wsb=need - 4) == WORKSPACE
+    assert bwd(ws=ws_at + 16) == WORKSPACE       # not 256-byte aligned
+    assert bwd(dq=0x10000 + 4) == ALIASING       # dq over q
+    assert bwd(dq=0x200000 + 64) == ALIASING     # dq over dk
+    assert bwd(dST=0x900000) == ALIASING         # dS0 over dS_T
+    assert bwd(dS0=ws_at + 256) == ALIASING      # dS0 inside the workspace
+    # no streams: nothing to do, no pointer needed
+    assert bwd(B=0, q=None, dout=None, dq=None, dS0=None, ws=None,
+               beta=None) == OK

@@ -176,6 +176,24 @@ def make_inputs(w: Workload):
     return out
 
 
+def make_cotangents(w: Workload, state=True):
+    """Seeded adjoints of the OSDN outputs for backward tests: dict(do,
+    dS_T, dd_T) as CPU tensors. do [B,H,T,Dv] ~ N(0,1) in the storage dtype;
+    with ``state``, dS_T [B,H,Dv,Dk] ~ N(0,1)/sqrt(Dk) and dd_T [B,H,Dk] ~
+    N(0,1) in fp32 (else None). Drawn from SeedSequence(seed) children 10-12,
+    after the ten of make_inputs."""
+    ch = [np.random.default_rng(s)
+          for s in np.random.SeedSequence(w.seed).spawn(13)[10:]]
+    B, H, T, Dk, Dv = w.B, w.H, w.T, w.Dk, w.Dv
+    out = dict(do=_store(ch[0].standard_normal((B, H, T, Dv)), w.dtype),
+               dS_T=None, dd_T=None)
+    if state:
+        out["dS_T"] = _store(ch[1].standard_normal((B, H, Dv, Dk))
+                             / np.sqrt(Dk), "f32")
+        out["dd_T"] = _store(ch[2].standard_normal((B, H, Dk)), "f32")
+    return out
+
+
 def to_f64(t):
     """Exact widening of a (possibly bf16) CPU/GPU tensor to float64 NumPy."""
     if t is None:
