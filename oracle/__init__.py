@@ -21,9 +21,11 @@ Modules:
 * ``recurrence``  fp64 NumPy token-by-token recurrences (OSDN, phase 1 alone,
   GDN-2, OSDN on a per-channel-decay backbone), the surrogate h_t, by definition and in closed form, and the
   residual contraction ratios with their geometric mean q_geo.
-* ``backward``  the fp64 reverse-mode adjoint of the OSDN token recurrence
-  (the gradients of every input, the preconditioner learner's included),
-  pinned by central differences of ``osdn_ref``.
+* ``backward``  the fp64 reverse-mode adjoints of the OSDN token recurrence
+  (the gradients of every input, the preconditioner learner's included), of
+  OSDN on a per-channel-decay backbone and of GDN-2 (gate-aware: decay,
+  erase and write gates), pinned by central differences of ``osdn_ref``,
+  ``osdn_gated_ref`` and ``gdn2_ref`` in ``tests/test_oracle_backward.py``.
 * ``exact``     the same recurrences in exact rational arithmetic
   (``fractions.Fraction``) plus an independent closed-form unrolling of the
   state as a sum of products of transition matrices, for tiny inputs.
@@ -47,4 +49,8 @@ from .recurrence import (  # noqa: F401
     grad_h_closed_form,
     regression_loss,
 )
-from .backward import osdn_backward_ref  # noqa: F401
+from .backward import (  # noqa: F401
+    osdn_backward_ref,
+    osdn_gated_backward_ref,
+    gdn2_backward_ref,
+)
