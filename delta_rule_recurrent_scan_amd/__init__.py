@@ -12,7 +12,8 @@ import os
 
 import torch
 
-__all__ = ["osdn_forward", "osdn_forward_noalloc", "osdn_backward", "osdn_precond_scan",
+__all__ = ["osdn_forward", "osdn_forward_noalloc", "osdn_backward",
+           "osdn_gated_backward", "gdn2_backward", "osdn_precond_scan",
            "osdn_chunk_forward",
            "gdn2_forward", "osdn_gated_forward", "osdn_decode",
            "gdn2_decode",
@@ -95,6 +96,16 @@ def load_library():
     L.osdn_backward.argtypes = ([I] * 6 + [P, P, P, P, P, F, P, P, F, P, P, P]
                                 + [P] * 8 + [P, Z, P])
     L.osdn_backward.restype = I
+    L.osdn_gated_backward_workspace_bytes.argtypes = [I] * 5
+    L.osdn_gated_backward_workspace_bytes.restype = Z
+    L.osdn_gated_backward.argtypes = ([I] * 6 + [P, P, P, P, P, F, P, P, P, F,
+                                                 P, P, P] + [P] * 9 + [P, Z, P])
+    L.osdn_gated_backward.restype = I
+    L.gdn2_backward_workspace_bytes.argtypes = [I] * 5
+    L.gdn2_backward_workspace_bytes.restype = Z
+    L.gdn2_backward.argtypes = ([I] * 6 + [P] * 7 + [F, P, P] + [P] * 7
+                                + [P, Z, P])
+    L.gdn2_backward.restype = I
     L.osdn_kernel_timing.argtypes = [I]
     L.osdn_kernel_timing.restype = None
     L.osdn_kernel_times.argtypes = [I, P, P, P]
@@ -317,6 +328,107 @@ def osdn_backward(q, k, v, beta, dout, r=None, eta=0.1, d0=None, S0=None,
                          workspace.numel(), _stream(dev))
     if rc != 0:
         raise OsdnError(rc, "osdn_backward")
+    return g
+
+
+def _grad_outputs(out, shapes, dev):
+    f32 = torch.float32
+    g = out if out is not None else {
+        n: torch.empty(s, dtype=f32, device=dev) for n, s in shapes.items()}
+    for n, s in shapes.items():
+        if g.get(n) is None:
+            raise ValueError("out must hold a tensor for %s" % n)
+        _check(g[n], "out[%s]" % n, s, f32, dev)
+    return g
+
+
+def osdn_gated_backward(q, k, v, beta, log_alpha, dout, r=None, eta=0.1,
+                        d0=None, S0=None, dS_T=None, dd_T=None, scale=1.0,
+                        out=None, workspace=None):
+    """Backward of osdn_gated_forward on the GPU: as osdn_backward, with the
+    per-channel decay log_alpha [B,H,T,Dk] fp32; the returned dict also holds
+    log_alpha's gradient."""
+    L = load_library()
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    f32 = torch.float32
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(beta, "beta", (B, H, T), f32, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, Dk), f32, dev)
+    _check(r, "r", (B, H, T), f32, dev)
+    _check(d0, "d0", (B, H, Dk), f32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), f32, dev)
+    _check(dout, "dout", (B, H, T, Dv), dt, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), f32, dev)
+    _check(dd_T, "dd_T", (B, H, Dk), f32, dev)
+    g = _grad_outputs(out, dict(q=(B, H, T, Dk), k=(B, H, T, Dk),
+                                v=(B, H, T, Dv), beta=(B, H, T), r=(B, H, T),
+                                eta=(B, H), log_alpha=(B, H, T, Dk),
+                                d0=(B, H, Dk), S0=(B, H, Dv, Dk)), dev)
+    need = L.osdn_gated_backward_workspace_bytes(B, H, T, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = L.osdn_gated_backward(
+        B, H, T, Dk, Dv, _DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v),
+        _ptr(beta), _ptr(r), float(eta), _ptr(log_alpha), _ptr(d0), _ptr(S0),
+        float(scale), _ptr(dout), _ptr(dS_T), _ptr(dd_T), _ptr(g["q"]),
+        _ptr(g["k"]), _ptr(g["v"]), _ptr(g["beta"]), _ptr(g["r"]),
+        _ptr(g["eta"]), _ptr(g["log_alpha"]), _ptr(g["d0"]), _ptr(g["S0"]),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "osdn_gated_backward")
+    return g
+
+
+def gdn2_backward(q, k, v, log_alpha, b, w, dout, S0=None, dS_T=None,
+                  scale=1.0, out=None, workspace=None):
+    """Backward of gdn2_forward on the GPU: the gradient of
+    sum <dout, o> + <dS_T, S_T>. Inputs as in gdn2_forward; dout [B,H,T,Dv]
+    in the dtype of q, dS_T [B,H,Dk,Dv] fp32 (None: zero). Returns a dict of
+    fp32 tensors q, k, log_alpha, b [B,H,T,Dk], v, w [B,H,T,Dv] and S0
+    [B,H,Dk,Dv]."""
+    L = load_library()
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dt = q.dtype
+    f32 = torch.float32
+    _check(q, "q", (B, H, T, Dk), dt, dev)
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, Dk), f32, dev)
+    _check(b, "b", (B, H, T, Dk), dt, dev)
+    _check(w, "w", (B, H, T, Dv), dt, dev)
+    _check(S0, "S0", (B, H, Dk, Dv), f32, dev)
+    _check(dout, "dout", (B, H, T, Dv), dt, dev)
+    _check(dS_T, "dS_T", (B, H, Dk, Dv), f32, dev)
+    g = _grad_outputs(out, dict(q=(B, H, T, Dk), k=(B, H, T, Dk),
+                                v=(B, H, T, Dv), log_alpha=(B, H, T, Dk),
+                                b=(B, H, T, Dk), w=(B, H, T, Dv),
+                                S0=(B, H, Dk, Dv)), dev)
+    need = L.gdn2_backward_workspace_bytes(B, H, T, Dk, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = L.gdn2_backward(
+        B, H, T, Dk, Dv, _DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(v),
+        _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0), float(scale),
+        _ptr(dout), _ptr(dS_T), _ptr(g["q"]), _ptr(g["k"]), _ptr(g["v"]),
+        _ptr(g["log_alpha"]), _ptr(g["b"]), _ptr(g["w"]), _ptr(g["S0"]),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if rc != 0:
+        raise OsdnError(rc, "gdn2_backward")
     return g
 
 

@@ -107,6 +107,30 @@ struct BackwardArgs {
   void* ws;                 // backward_workspace_bytes
 };
 
+// Arguments of the gate-aware backward (GDN-2, or OSDN on a per-channel-
+// decay backbone): the forward's inputs plus the output adjoints; gradients
+// fp32 in the inputs' layouts. OSDN: beta, r, eta, d0 and their gradients,
+// state [B,H,Dv,Dk]; GDN-2: b, w and theirs, state [B,H,Dk,Dv].
+struct GatedBackwardArgs {
+  int B, H, T, Dk, Dv;
+  int bf16;
+  int gdn2;
+  const void *q, *k, *v;    // [B,H,T,Dk], [B,H,T,Dk], [B,H,T,Dv]
+  const float* log_alpha;   // [B,H,T,Dk]
+  const void *b, *w;        // GDN-2: [B,H,T,Dk], [B,H,T,Dv]
+  const float *beta, *r;    // OSDN: [B,H,T] (r null: ones)
+  float eta;
+  const float *d0, *S0;     // OSDN d0 [B,H,Dk] or null; S0 or null
+  float scale;
+  const void* dout;         // [B,H,T,Dv], dtype of q
+  const float *dST, *ddT;   // or null (zeros); ddT OSDN only
+  float *dq, *dk, *dv, *dla;
+  float *db, *dw;           // GDN-2
+  float *dbeta, *dr, *deta, *dd0;  // OSDN
+  float* dS0;
+  void* ws;                 // gated_backward_workspace_bytes
+};
+
 // Each returns a hipError_t-compatible code (0 = success) or -1 when the
 // (dims, dtype) combination has no kernel instance.
 int launch_precond_scan(const PrecondArgs& a, hipStream_t s);
@@ -130,6 +154,11 @@ int launch_decode(const DecodeArgs& a, hipStream_t s);
 // preconditioner d_t, and the state every 64 tokens and after the last.
 size_t backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
 int launch_backward(const BackwardArgs& a, hipStream_t s);
+// Device scratch of the gate-aware backward: per token the preconditioner
+// (OSDN only), the state every 64 tokens and after the last, and one
+// 64-token interval of states per stream.
+size_t gated_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv, int gdn2);
+int launch_gated_backward(const GatedBackwardArgs& a, hipStream_t s);
 bool osdn_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 bool gdn2_chunk_supported(int Dk, int Dv, int chunk, int bf16);
 // Device scratch of the chunk engine: per chunk, the S0-independent operands

@@ -414,6 +414,114 @@ int osdn_backward(int B, int H, int T, int Dk, int Dv, int dtype,
   return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
 }
 
+size_t osdn_gated_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return 0;
+  return osdn::gated_backward_workspace_bytes(B, H, T, Dk, Dv, 0);
+}
+
+int osdn_gated_backward(int B, int H, int T, int Dk, int Dv, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* beta, const float* r, float eta,
+                        const float* log_alpha, const float* d0,
+                        const float* S0, float scale, const void* dout,
+                        const float* dS_T, const float* dd_T, float* dq,
+                        float* dk, float* dv, float* dbeta, float* dr,
+                        float* deta, float* dlog_alpha, float* dd0,
+                        float* dS0, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  const size_t BH = (size_t)B * H;
+  if (BH > 0 && (!deta || !dd0 || !dS0)) return OSDN_ERR_NULL_ARG;
+  if (BH * T > 0 && (!q || !k || !v || !beta || !log_alpha || !dout || !dq ||
+                     !dk || !dv || !dbeta || !dr || !dlog_alpha))
+    return OSDN_ERR_NULL_ARG;
+  if (!dim_ok(Dk) || !dim_ok(Dv) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return OSDN_ERR_UNSUPPORTED;
+  const size_t need = osdn_gated_backward_workspace_bytes(B, H, T, Dk, Dv);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
+  if (BH == 0) return OSDN_OK;
+  const size_t es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(beta, BH * T * 4),
+                       rng(r, r ? BH * T * 4 : 0), rng(log_alpha, BH * T * Dk * 4),
+                       rng(d0, d0 ? BH * Dk * 4 : 0),
+                       rng(S0, S0 ? BH * Dv * Dk * 4 : 0),
+                       rng(dout, BH * T * Dv * es),
+                       rng(dS_T, dS_T ? BH * Dv * Dk * 4 : 0),
+                       rng(dd_T, dd_T ? BH * Dk * 4 : 0)};
+  const Range outs[] = {rng(dq, BH * T * Dk * 4), rng(dk, BH * T * Dk * 4),
+                        rng(dv, BH * T * Dv * 4), rng(dbeta, BH * T * 4),
+                        rng(dr, BH * T * 4), rng(deta, BH * 4),
+                        rng(dlog_alpha, BH * T * Dk * 4),
+                        rng(dd0, BH * Dk * 4), rng(dS0, BH * Dv * Dk * 4),
+                        rng(workspace, need)};
+  if (!aliasing_ok(outs, ins, nullptr, 0)) return OSDN_ERR_ALIASING;
+  osdn::GatedBackwardArgs a{};
+  a.B = B; a.H = H; a.T = T; a.Dk = Dk; a.Dv = Dv;
+  a.bf16 = dtype == OSDN_BF16; a.gdn2 = 0;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha;
+  a.beta = beta; a.r = r; a.eta = eta; a.d0 = d0; a.S0 = S0; a.scale = scale;
+  a.dout = dout; a.dST = dS_T; a.ddT = dd_T;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha;
+  a.dbeta = dbeta; a.dr = dr; a.deta = deta; a.dd0 = dd0; a.dS0 = dS0;
+  a.ws = workspace;
+  const int rc = osdn::launch_gated_backward(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
+size_t gdn2_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv) {
+  if (B < 0 || H < 0 || T < 0 || !dim_ok(Dk) || !dim_ok(Dv)) return 0;
+  return osdn::gated_backward_workspace_bytes(B, H, T, Dk, Dv, 1);
+}
+
+int gdn2_backward(int B, int H, int T, int Dk, int Dv, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* log_alpha, const void* b, const void* w,
+                  const float* S0, float scale, const void* dout,
+                  const float* dS_T, float* dq, float* dk, float* dv,
+                  float* dlog_alpha, float* db, float* dw, float* dS0,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || T < 0) return OSDN_ERR_BAD_DIMS;
+  const size_t BH = (size_t)B * H;
+  if (BH > 0 && !dS0) return OSDN_ERR_NULL_ARG;
+  if (BH * T > 0 && (!q || !k || !v || !log_alpha || !b || !w || !dout ||
+                     !dq || !dk || !dv || !dlog_alpha || !db || !dw))
+    return OSDN_ERR_NULL_ARG;
+  if (!dim_ok(Dk) || !dim_ok(Dv) || (dtype != OSDN_F32 && dtype != OSDN_BF16))
+    return OSDN_ERR_UNSUPPORTED;
+  const size_t need = gdn2_backward_workspace_bytes(B, H, T, Dk, Dv);
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   ((uintptr_t)workspace & 255) != 0))
+    return OSDN_ERR_WORKSPACE;
+  if (BH == 0) return OSDN_OK;
+  const size_t es = elem(dtype);
+  const Range ins[] = {rng(q, BH * T * Dk * es), rng(k, BH * T * Dk * es),
+                       rng(v, BH * T * Dv * es), rng(log_alpha, BH * T * Dk * 4),
+                       rng(b, BH * T * Dk * es), rng(w, BH * T * Dv * es),
+                       rng(S0, S0 ? BH * Dk * Dv * 4 : 0),
+                       rng(dout, BH * T * Dv * es),
+                       rng(dS_T, dS_T ? BH * Dk * Dv * 4 : 0)};
+  const Range outs[] = {rng(dq, BH * T * Dk * 4), rng(dk, BH * T * Dk * 4),
+                        rng(dv, BH * T * Dv * 4),
+                        rng(dlog_alpha, BH * T * Dk * 4),
+                        rng(db, BH * T * Dk * 4), rng(dw, BH * T * Dv * 4),
+                        rng(dS0, BH * Dk * Dv * 4), rng(workspace, need)};
+  if (!aliasing_ok(outs, ins, nullptr, 0)) return OSDN_ERR_ALIASING;
+  osdn::GatedBackwardArgs a{};
+  a.B = B; a.H = H; a.T = T; a.Dk = Dk; a.Dv = Dv;
+  a.bf16 = dtype == OSDN_BF16; a.gdn2 = 1;
+  a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.b = b; a.w = w;
+  a.S0 = S0; a.scale = scale; a.dout = dout; a.dST = dS_T;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dla = dlog_alpha; a.db = db; a.dw = dw;
+  a.dS0 = dS0; a.ws = workspace;
+  const int rc = osdn::launch_gated_backward(a, (hipStream_t)stream);
+  if (rc == -1) return OSDN_ERR_UNSUPPORTED;
+  return rc == 0 ? OSDN_OK : OSDN_ERR_HIP;
+}
+
 int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype) {
   return gdn2_forward_supported(Dk, Dv, chunk, dtype);
 }

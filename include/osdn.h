@@ -365,6 +365,59 @@ int osdn_backward(int B, int H, int T, int Dk, int Dv, int dtype,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * Gate-aware backward of osdn_gated_forward: the adjoint of OSDN on a
+ * per-key-channel-decay backbone (the decay applied to the state before the
+ * token's step, as in osdn_gated_forward; [OSDN-it] section 4 with the
+ * preconditioner learner of sections 2.1-2.3). Arguments as in
+ * osdn_backward, plus
+ *   log_alpha  [B,H,T,Dk] fp32           the decay (required)
+ *   dlog_alpha [B,H,T,Dk] fp32 OUT       its gradient (required)
+ * workspace: osdn_gated_backward_workspace_bytes() bytes, 256-byte aligned,
+ * caller-owned: per token the preconditioner, the state every 64 tokens and
+ * after the last, and one interval of min(T, 64) states per (batch, head)
+ * (the reverse pass recomputes each interval from its stored state rather
+ * than undo the decay). Other rules as in osdn_backward.
+ */
+size_t osdn_gated_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
+int osdn_gated_backward(int B, int H, int T, int Dk, int Dv, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* beta, const float* r, float eta,
+                        const float* log_alpha, const float* d0,
+                        const float* S0, float scale, const void* dout,
+                        const float* dS_T, const float* dd_T, float* dq,
+                        float* dk, float* dv, float* dbeta, float* dr,
+                        float* deta, float* dlog_alpha, float* dd0,
+                        float* dS0, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Gate-aware backward of gdn2_forward ([GDN2-it] method, part 1, and the
+ * gate-aware backward of its method part 3, here in token form): the
+ * gradient of L = sum <dout, o> + <dS_T, S_T> with respect to q, k, v, the
+ * decay log_alpha, the erase gate b, the write gate w and S0.
+ *
+ *   q, k, v, log_alpha, b, w, S0, scale   as in gdn2_forward (S0 NULL: zeros)
+ *   dout     [B,H,T,Dv]  dtype of q       (required)
+ *   dS_T     [B,H,Dk,Dv] fp32             (NULL: zero)
+ *   dq, dk, dlog_alpha, db  [B,H,T,Dk] fp32 OUT   (required)
+ *   dv, dw   [B,H,T,Dv]  fp32 OUT         (required)
+ *   dS0      [B,H,Dk,Dv] fp32 OUT         (required)
+ *   workspace  gdn2_backward_workspace_bytes() bytes, 256-byte aligned,
+ *            caller-owned: the state every 64 tokens and after the last, and
+ *            one interval of min(T, 64) states per (batch, head)
+ * No output may overlap another output, an input or the workspace. Dk, Dv in
+ * {32, 64, 128}; gradients fp32 whatever the input dtype.
+ */
+size_t gdn2_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
+int gdn2_backward(int B, int H, int T, int Dk, int Dv, int dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* log_alpha, const void* b, const void* w,
+                  const float* S0, float scale, const void* dout,
+                  const float* dS_T, float* dq, float* dk, float* dv,
+                  float* dlog_alpha, float* db, float* dw, float* dS0,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing for measurement harnesses. While enabled, every entry
  * point records a HIP event on its stream before and after each kernel it
  * launches (two event records per kernel; events are created on first use
@@ -386,7 +439,8 @@ void osdn_kernel_timing(int enable);
  * (GDN-2), gated_prep, gated_prep_fused, gated_scan (OSDN on a decaying
  * backbone),
  * osdn_decode, gdn2_decode (recurrent decode), osdn_bwd_record, osdn_bwd
- * (backward).
+ * (backward), gated_bwd_record, gated_bwd, gdn2_bwd_record, gdn2_bwd
+ * (gate-aware backward).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

@@ -418,3 +418,55 @@ def test_backward_error_paths_and_workspace():
     # no streams: nothing to do, no pointer needed
     assert bwd(B=0, q=None, dout=None, dq=None, dS0=None, ws=None,
                beta=None) == OK
+
+
+@needs_lib
+@pytest.mark.parametrize("gdn2", [False, True])
+def test_gated_backward_error_paths_and_workspace(gdn2):
+    L = osdn.load_library()
+    P = ctypes.c_void_p
+    I, F, Z = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.osdn_gated_backward.argtypes = ([I] * 6 + [P, P, P, P, P, F, P, P, P, F,
+                                                 P, P, P] + [P] * 9 + [P, Z, P])
+    L.gdn2_backward.argtypes = [I] * 6 + [P] * 7 + [F, P, P] + [P] * 7 + [P, Z, P]
+    wsq = (L.gdn2_backward_workspace_bytes if gdn2
+           else L.osdn_gated_backward_workspace_bytes)
+    wsq.argtypes = [I] * 5
+    wsq.restype = Z
+    # OSDN: per token d (Dk); both: a state every 64 tokens and after the
+    # last, and an interval of min(T, 64) states
+    for B, H, T, Dk, Dv in ((1, 1, 1, 32, 32), (2, 3, 64, 64, 128),
+                            (1, 2, 130, 128, 32), (2, 1, 0, 32, 64)):
+        nck = (T + 63) // 64
+        per = (0 if gdn2 else T * Dk) + (nck + 1 + min(T, 64)) * Dv * Dk
+        assert wsq(B, H, T, Dk, Dv) == B * H * per * 4
+    assert wsq(1, 1, 8, 48, 32) == 0
+    need = wsq(1, 1, 4, 32, 32)
+    ws_at = 0x4000000
+
+    def call(B=1, T=4, Dk=32, q=0x10000, la=0x80000, dq=0x100000,
+             dS0=0x900000, ws=ws_at, wsb=need, dla=0xa00000):
+        if gdn2:
+            return L.gdn2_backward(B, 1, T, Dk, 32, 1, q, 0x20000, 0x30000, la,
+                                   0x90000, 0x98000, None, 1.0, 0x60000, None,
+                                   dq, 0x200000, 0x300000, dla, 0x400000,
+                                   0x500000, dS0, ws, wsb, None)
+        return L.osdn_gated_backward(B, 1, T, Dk, 32, 1, q, 0x20000, 0x30000,
+                                     0x40000, None, 0.1, la, None, None, 1.0,
+                                     0x60000, None, None, dq, 0x200000,
+                                     0x300000, 0x400000, 0x500000, 0x600000,
+                                     dla, 0x700000, dS0, ws, wsb, None)
+    assert call(q=None) == NULL_ARG
+    assert call(la=None) == NULL_ARG
+    assert call(dla=None) == NULL_ARG
+    assert call(dS0=None) == NULL_ARG
+    assert call(T=-1) == BAD_DIMS
+    assert call(Dk=16) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=need - 4) == WORKSPACE
+    assert call(ws=ws_at + 64) == WORKSPACE
+    assert call(dq=0x10000 + 8) == ALIASING       # dq over q
+    assert call(dla=0x80000) == ALIASING          # gradient over the decay
+    assert call(dS0=ws_at) == ALIASING            # dS0 over the workspace
+    assert call(B=0, q=None, la=None, dq=None, dS0=None, ws=None,
+                dla=None) == OK

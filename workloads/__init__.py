@@ -177,20 +177,22 @@ def make_inputs(w: Workload):
 
 
 def make_cotangents(w: Workload, state=True):
-    """Seeded adjoints of the OSDN outputs for backward tests: dict(do,
-    dS_T, dd_T) as CPU tensors. do [B,H,T,Dv] ~ N(0,1) in the storage dtype;
-    with ``state``, dS_T [B,H,Dv,Dk] ~ N(0,1)/sqrt(Dk) and dd_T [B,H,Dk] ~
-    N(0,1) in fp32 (else None). Drawn from SeedSequence(seed) children 10-12,
-    after the ten of make_inputs."""
+    """Seeded adjoints of the outputs for backward tests: dict(do, dS_T,
+    dd_T) as CPU tensors. do [B,H,T,Dv] ~ N(0,1) in the storage dtype; with
+    ``state``, dS_T ~ N(0,1)/sqrt(Dk) in fp32, of the state's shape ([B,H,Dv,
+    Dk] for OSDN, [B,H,Dk,Dv] for GDN-2), and for OSDN dd_T [B,H,Dk] ~ N(0,1)
+    (else None). Drawn from SeedSequence(seed) children 10-12, after the ten
+    of make_inputs."""
     ch = [np.random.default_rng(s)
           for s in np.random.SeedSequence(w.seed).spawn(13)[10:]]
     B, H, T, Dk, Dv = w.B, w.H, w.T, w.Dk, w.Dv
     out = dict(do=_store(ch[0].standard_normal((B, H, T, Dv)), w.dtype),
                dS_T=None, dd_T=None)
     if state:
-        out["dS_T"] = _store(ch[1].standard_normal((B, H, Dv, Dk))
-                             / np.sqrt(Dk), "f32")
-        out["dd_T"] = _store(ch[2].standard_normal((B, H, Dk)), "f32")
+        shape = (B, H, Dk, Dv) if w.kind == "gdn2" else (B, H, Dv, Dk)
+        out["dS_T"] = _store(ch[1].standard_normal(shape) / np.sqrt(Dk), "f32")
+        if w.kind != "gdn2":
+            out["dd_T"] = _store(ch[2].standard_normal((B, H, Dk)), "f32")
     return out
 
 
