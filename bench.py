@@ -1,11 +1,15 @@
 """Benchmark of the OSDN forward hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--backward]
 
 One step = one full forward (osdn_forward: phase 1 preconditioner scan and
 phase 2 chunked WY delta rule) over the workload's synthetic batch, inputs
 resident in HBM, outputs and workspace preallocated. Other workloads time
 gdn2_forward, osdn_gated_forward or one recurrent decode call the same way.
+With --backward a step is the backward of the workload's forward instead
+(osdn_backward, osdn_gated_backward or gdn2_backward: every input's gradient
+from seeded output adjoints).
 
 Prints one JSON line: throughput (tokens/s = B*T per step time), the HBM
 roofline of the whole step (algorithmic bytes of the forward per its step
@@ -48,6 +52,12 @@ _KERNEL_SOURCES = {
     "gated_scan": ["wy_chunk.hip"],
     "osdn_decode": ["decode.hip"],
     "gdn2_decode": ["decode.hip"],
+    "osdn_bwd_record": ["backward.hip", "row_state.hpp"],
+    "osdn_bwd": ["backward.hip", "row_state.hpp"],
+    "gated_bwd_record": ["backward_gated.hip", "row_state.hpp"],
+    "gated_bwd": ["backward_gated.hip", "row_state.hpp"],
+    "gdn2_bwd_record": ["backward_gated.hip", "row_state.hpp"],
+    "gdn2_bwd": ["backward_gated.hip", "row_state.hpp"],
 }
 PRECOND_CHUNK = 64  # phase-1 chunk length (fixed in the library)
 
@@ -60,17 +70,17 @@ def source_sha(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, run):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs (scaled by the copy-kernel calibration), or None when
-    they were taken on another workload or on kernel sources that have
-    changed since."""
+    WRITE_SIZE runs (scaled by the copy-kernel calibration) of this run
+    (the workload name, with "-backward" for the backward), or None when
+    there are none or the kernel's sources have changed since."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
-        rec = json.load(open(path))["kernels"][kernel]
+        rec = json.load(open(path))["runs"][run][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha") != source_sha(kernel) or rec.get("workload") != workload:
+    if rec.get("source_sha") != source_sha(kernel):
         return None
     return rec["bytes"]
 
@@ -101,6 +111,25 @@ def path_bytes(w):
         return th * tok + bh * dk * dv * 4
     tok = (2 * dk + dv) * s + dv * s + gates + (4 * dk if w.decay else 0)
     return th * tok + bh * (dk * dv * 4 + 2 * dk * 4)
+
+
+def backward_bytes(w):
+    """Algorithmic HBM bytes of one backward call: every forward input read
+    once (path_bytes' token inputs, without o), the output adjoint do read
+    (Dv, dtype), every gradient written once in fp32 (per token-head: OSDN
+    q, k, v, beta, r; gated OSDN adds log alpha; GDN-2 q, k, v, log alpha,
+    b, w), and per stream the state's adjoint read and S0's gradient written
+    (fp32), with OSDN's d adjoints and eta's gradient."""
+    s, dk, dv = _s(w), w.Dk, w.Dv
+    th, bh = w.B * w.H * w.T, w.B * w.H
+    if w.kind == "gdn2":
+        tok_in = (3 * dk + 2 * dv) * s + 4 * dk + dv * s
+        tok_out = (4 * dk + 2 * dv) * 4
+        return th * (tok_in + tok_out) + bh * 2 * dk * dv * 4
+    gates = 4 + (4 if w.apf else 0)
+    tok_in = (2 * dk + dv) * s + gates + (4 * dk if w.decay else 0) + dv * s
+    tok_out = (2 * dk + dv + 2) * 4 + (4 * dk if w.decay else 0)
+    return th * (tok_in + tok_out) + bh * (2 * dk * dv * 4 + 2 * dk * 4 + 4)
 
 
 def decode_bytes_per_head(w):
@@ -172,7 +201,22 @@ def _oracle_unit(i):
         sl = (slice(b, b + 1), slice(h, h + 1))
     a = {k: (None if v is None else v[sl]) for k, v in arrs.items()}
     t0 = time.perf_counter()
-    if w.kind == "gdn2":
+    if _UNITS.get("backward"):
+        from oracle import backward as BW
+        if w.kind == "gdn2":
+            BW.gdn2_backward_ref(a["q"], a["k"], a["v"], a["log_alpha"],
+                                 a["b"], a["w"], a.get("S0"), a["do"],
+                                 a.get("dS_T"))
+        elif w.decay:
+            BW.osdn_gated_backward_ref(a["q"], a["k"], a["v"], a["beta"],
+                                       a["log_alpha"], a["r"], w.eta,
+                                       a.get("d0"), a.get("S0"), a["do"],
+                                       a.get("dS_T"), a.get("dd_T"))
+        else:
+            BW.osdn_backward_ref(a["q"], a["k"], a["v"], a["beta"], a["r"],
+                                 w.eta, a.get("d0"), a.get("S0"), a["do"],
+                                 a.get("dS_T"), a.get("dd_T"))
+    elif w.kind == "gdn2":
         R.gdn2_ref(a["q"], a["k"], a["v"], a["log_alpha"], a["b"], a["w"],
                    a.get("S0"))
     elif w.decay:
@@ -194,7 +238,7 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, inp, budget_s=10.0):
+def cpu_baseline(w, inp, budget_s=10.0, cot=None):
     """The fp64 NumPy oracle as it stands, on a bounded sample of the
     workload: (1) one thread, whole units in turn until budget_s is spent;
     (2) a fork pool of min(16, cpu_count) processes (started before the
@@ -204,8 +248,13 @@ def cpu_baseline(w, inp, budget_s=10.0):
     `value` is the pool figure; `cores` the processes it used."""
     keys = ("q", "k", "v", "beta", "r", "log_alpha", "b", "w", "S0", "d0")
     _UNITS["w"] = w
+    _UNITS["backward"] = cot is not None
     _UNITS["arrs"] = {k: W.to_f64(inp[k]) for k in keys
                       if isinstance(inp.get(k), torch.Tensor)}
+    if cot is not None:
+        keys += ("do", "dS_T", "dd_T")
+        _UNITS["arrs"].update({k: W.to_f64(v) for k, v in cot.items()
+                               if isinstance(v, torch.Tensor)})
     for k in keys:
         _UNITS["arrs"].setdefault(k, None)
     n_units = w.B if w.state else w.B * w.H
@@ -229,7 +278,10 @@ def cpu_baseline(w, inp, budget_s=10.0):
     pooled = w.B * w.T / (wall * n_units / n_pool)
     return {"value": pooled, "unit": "tokens/s", "cores": procs,
             "kind": "oracle",
-            "sample": "fp64 NumPy token recurrence; %d of %d units (one unit "
+            "sample": ("fp64 NumPy adjoint of the token recurrence"
+                       if cot is not None else
+                       "fp64 NumPy token recurrence")
+            + "; %d of %d units (one unit "
                       "= one %s at T=%d) on a fork pool of %d processes, "
                       "scaled to the whole workload" % (n_pool, n_units, unit,
                                                         w.T, procs),
@@ -303,7 +355,7 @@ def timed_steps(step, args):
     return wall * 1e3 / args.steps, per_step, kt, cold_q
 
 
-def roofline(w, ms_step, kt):
+def roofline(w, ms_step, kt, backward=False):
     """HBM roofline of the whole step: the forward's algorithmic bytes (see
     path_bytes) over the measured step time, against the 8 TB/s peak.
     `traffic` is the HBM bytes all kernels of a step move (rocprofv3
@@ -311,11 +363,12 @@ def roofline(w, ms_step, kt):
     counters match its current sources. The dominant (longest) kernel is
     reported beside it: its mean launch duration, its own interface bytes
     per launch over that duration, and the path's bytes over it."""
-    alg = path_bytes(w)
+    alg = backward_bytes(w) if backward else path_bytes(w)
     achieved = alg / (ms_step * 1e-3) / 1e9
+    run = w.name + ("-backward" if backward else "")
     traffic = 0.0
     for n, k in kt.items():
-        b = measured_traffic(n, w.name)
+        b = measured_traffic(n, run)
         if b is None:
             traffic = None
             break
@@ -336,7 +389,7 @@ def roofline(w, ms_step, kt):
                             else iface / (kd["mean_launch_ms"] * 1e-3) / 1e9),
           "path_bytes_frac": alg / kd["launches_per_step"]
           / (kd["mean_launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-          "traffic": measured_traffic(dom, w.name)}
+          "traffic": measured_traffic(dom, run)}
     return {"scope": "whole step", "bound": "hbm", "achieved": achieved,
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -403,7 +456,46 @@ def make_step(w, x, dt, dev):
     return step
 
 
-def metric_name(w):
+def make_backward_step(w, x, c, dev):
+    """One backward call over the whole workload, gradients and workspace
+    preallocated."""
+    import delta_rule_recurrent_scan_amd as osdn
+    f32 = torch.float32
+    B, H, T, Dk, Dv = w.B, w.H, w.T, w.Dk, w.Dv
+    e = lambda *shape: torch.empty(shape, dtype=f32, device=dev)
+    if w.kind == "gdn2":
+        g = dict(q=e(B, H, T, Dk), k=e(B, H, T, Dk), v=e(B, H, T, Dv),
+                 log_alpha=e(B, H, T, Dk), b=e(B, H, T, Dk), w=e(B, H, T, Dv),
+                 S0=e(B, H, Dk, Dv))
+        n = osdn.gdn2_backward_workspace_bytes(B, H, T, Dk, Dv)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        return lambda: osdn.gdn2_backward(
+            x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], c["do"],
+            dS_T=c["dS_T"], out=g, workspace=ws)
+    g = dict(q=e(B, H, T, Dk), k=e(B, H, T, Dk), v=e(B, H, T, Dv),
+             beta=e(B, H, T), r=e(B, H, T), eta=e(B, H), d0=e(B, H, Dk),
+             S0=e(B, H, Dv, Dk))
+    if w.decay:
+        g["log_alpha"] = e(B, H, T, Dk)
+        n = osdn.gated_backward_workspace_bytes(B, H, T, Dk, Dv)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        return lambda: osdn.osdn_gated_backward(
+            x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], c["do"],
+            r=x["r"], eta=x["eta"], dS_T=c["dS_T"], dd_T=c["dd_T"], out=g,
+            workspace=ws)
+    n = osdn.backward_workspace_bytes(B, H, T, Dk, Dv)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    return lambda: osdn.osdn_backward(
+        x["q"], x["k"], x["v"], x["beta"], c["do"], r=x["r"], eta=x["eta"],
+        dS_T=c["dS_T"], dd_T=c["dd_T"], out=g, workspace=ws)
+
+
+def metric_name(w, backward=False):
+    if backward:
+        label = ("GDN-2" if w.kind == "gdn2" else
+                 "OSDN on a per-channel-decay backbone" if w.decay else "OSDN")
+        return ("%s backward tokens/s + %% HBM roofline, H=16 d=128 T=4096, "
+                "1 GPU" % label)
     if w.state:
         label = "OSDN" if w.kind == "osdn" else "GDN-2"
         return ("%s recurrent decode tokens/s + %% HBM roofline, B=%d H=%d "
@@ -441,6 +533,8 @@ def main():
     ap.add_argument("--workload", default="osdn-1.3b-apf",
                     choices=[w.name for w in W.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the workload's forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain fp32 scale-by-one kernel over 512 MiB "
                          "(reads and writes exactly 512 MiB each per step), "
@@ -459,8 +553,14 @@ def main():
         return
 
     w = W.BY_NAME[args.workload]
+    if args.backward and w.state:
+        print("--backward times a whole-sequence backward; pick a forward "
+              "workload", file=sys.stderr)
+        sys.exit(2)
     inp = W.make_inputs(w)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp)
+    cot = W.make_cotangents(w) if args.backward else None
+    cpu = (None if args.no_cpu_baseline
+           else cpu_baseline(w, inp, cot=cot))
 
     import delta_rule_recurrent_scan_amd as osdn
     osdn.load_library()
@@ -468,7 +568,12 @@ def main():
     x = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
          for k, v in inp.items()}
     dt = W.torch_dtype(w.dtype)
-    step = make_step(w, x, dt, dev)
+    if args.backward:
+        c = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+             for k, v in cot.items()}
+        step = make_backward_step(w, x, c, dev)
+    else:
+        step = make_step(w, x, dt, dev)
     ms_step, per_step, kt, cold = timed_steps(step, args)
 
     config = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "Dk": w.Dk,
@@ -478,7 +583,7 @@ def main():
     if w.kind == "osdn":
         config.update(forgetting_gate=w.apf, eta=w.eta)
     rec = {
-        "metric": metric_name(w),
+        "metric": metric_name(w, args.backward),
         "value": w.B * w.T / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -491,12 +596,19 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": config,
-        "roofline": roofline(w, ms_step, kt),
+        "roofline": roofline(w, ms_step, kt, args.backward),
         "step_ms": per_step,
         "cold_step": cold,
         "kernels": kt,
     }
-    if not w.state:
+    if args.backward:
+        config["pass"] = "backward"
+        alg = backward_bytes(w)
+        rec["roofline_cold"] = {
+            "achieved": alg / (cold["median_ms"] * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": alg / (cold["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    elif not w.state:
         flops = flops_per_token_head(w) * w.B * w.H * w.T
         rec["mfma"] = {"chunk_form_flops": flops,
                        "TFLOPs": flops / (ms_step * 1e-3) / 1e12,

@@ -342,6 +342,15 @@ def _grad_outputs(out, shapes, dev):
     return g
 
 
+def gated_backward_workspace_bytes(B, H, T, Dk, Dv):
+    return int(load_library().osdn_gated_backward_workspace_bytes(B, H, T, Dk,
+                                                                  Dv))
+
+
+def gdn2_backward_workspace_bytes(B, H, T, Dk, Dv):
+    return int(load_library().gdn2_backward_workspace_bytes(B, H, T, Dk, Dv))
+
+
 def osdn_gated_backward(q, k, v, beta, log_alpha, dout, r=None, eta=0.1,
                         d0=None, S0=None, dS_T=None, dd_T=None, scale=1.0,
                         out=None, workspace=None):

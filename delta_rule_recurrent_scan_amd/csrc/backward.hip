@@ -78,20 +78,36 @@ __global__ __launch_bounds__(kDecThreads) void osdn_bwd_record_kernel(
     for (int j = 0; j < NC; ++j) dv[j] = 1.f;
   }
 
+  // the next token's inputs are loaded one token ahead, off the chain
   const size_t tb = (size_t)bh * T;
+  float kn[NC], vn[NR], bn = 0.f, rn = 1.f;
+  if (T > 0) {
+    load_cols<DK, Tin>(k + tb * DK, cl, kn);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) vn[i] = to_f32(v[tb * DV + rg + 16 * i]);
+    bn = beta[tb];
+    rn = r ? r[tb] : 1.f;
+  }
   for (int t = 0; t < T; ++t) {
     if (t % kCkpt == 0) {
       float* C = Cb + (size_t)(t / kCkpt) * DV * DK;
 #pragma unroll
       for (int i = 0; i < NR; ++i) store_cols<DK>(C + (size_t)(rg + 16 * i) * DK, cl, s[i]);
     }
-    const size_t tt = tb + t;
     float kk[NC], vv[NR];
-    load_cols<DK, Tin>(k + tt * DK, cl, kk);
 #pragma unroll
-    for (int i = 0; i < NR; ++i) vv[i] = to_f32(v[tt * DV + rg + 16 * i]);
-    const float bt = beta[tt];
-    const float rt = r ? r[tt] : 1.f;
+    for (int j = 0; j < NC; ++j) kk[j] = kn[j];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) vv[i] = vn[i];
+    const float bt = bn, rt = rn;
+    if (t + 1 < T) {
+      const size_t tn = tb + t + 1;
+      load_cols<DK, Tin>(k + tn * DK, cl, kn);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) vn[i] = to_f32(v[tn * DV + rg + 16 * i]);
+      bn = beta[tn];
+      rn = r ? r[tn] : 1.f;
+    }
     float n = 0.f, c = 0.f, kt[NC], p[NR];
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -169,20 +185,39 @@ __global__ __launch_bounds__(kDecThreads) void osdn_bwd_kernel(
   }
   float eta_acc = 0.f;
 
+  // the previous token's inputs are loaded one token ahead, off the chain
   const size_t tb = (size_t)bh * T;
+  float kn[NC], qn[NC], dn_[NC], don[NR], un[NR], bn = 0.f, rn = 1.f;
+  auto prefetch = [&](int t) {
+    const size_t tt = tb + t;
+    load_cols<DK, Tin>(k + tt * DK, cl, kn);
+    load_cols<DK, Tin>(q + tt * DK, cl, qn);
+    load_cols<DK, float>(Db + (size_t)t * DK, cl, dn_);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      don[i] = to_f32(dout[tt * DV + rg + 16 * i]);
+      un[i] = Ub[(size_t)t * DV + rg + 16 * i];
+    }
+    bn = beta[tt];
+    rn = r ? r[tt] : 1.f;
+  };
+  if (T > 0) prefetch(T - 1);
   for (int t = T - 1; t >= 0; --t) {
     const size_t tt = tb + t;
     float kk[NC], qq[NC], dt[NC], dov[NR], uu[NR];
-    load_cols<DK, Tin>(k + tt * DK, cl, kk);
-    load_cols<DK, Tin>(q + tt * DK, cl, qq);
-    load_cols<DK, float>(Db + (size_t)t * DK, cl, dt);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      kk[j] = kn[j];
+      qq[j] = qn[j];
+      dt[j] = dn_[j];
+    }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      dov[i] = to_f32(dout[tt * DV + rg + 16 * i]);
-      uu[i] = Ub[(size_t)t * DV + rg + 16 * i];
+      dov[i] = don[i];
+      uu[i] = un[i];
     }
-    const float bt = beta[tt];
-    const float rt = r ? r[tt] : 1.f;
+    const float bt = bn, rt = rn;
+    if (t > 0) prefetch(t - 1);
     float n = 0.f, c = 0.f, a[NC], kt[NC];
 #pragma unroll
     for (int j = 0; j < NC; ++j) {

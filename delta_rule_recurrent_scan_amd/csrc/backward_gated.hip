@@ -122,45 +122,69 @@ struct Tok {
   float n, cc, bt, rt;  // OSDN: ||k||^2, <d, k*k>, beta, r
 };
 
+// A token's inputs as loaded (widened to fp32), before anything that
+// depends on the recurrence: loaded one token ahead of their use.
+template <int DK, int DV>
+struct Raw {
+  float kk[DK / 16], la[DK / 16], b[DK / 16], v[DV / 16], w[DV / 16];
+  float bt, rt;
+};
+
 template <int DK, int DV, typename Tin, bool G2>
-__device__ __forceinline__ void load_tok(const GParams& p, size_t tt, int rg, int cl,
-                                         const float (&dt)[DK / 16], Tok<DK, DV>& o) {
-  constexpr int NC = DK / 16, NR = DV / 16;
+__device__ __forceinline__ void raw_load(const GParams& p, size_t tt, int rg, int cl,
+                                         Raw<DK, DV>& o) {
+  constexpr int NR = DV / 16;
   load_cols<DK, Tin>((const Tin*)p.k + tt * DK, cl, o.kk);
-  load_cols<DK, float>(p.la + tt * DK, cl, o.al);
+  load_cols<DK, float>(p.la + tt * DK, cl, o.la);
 #pragma unroll
-  for (int j = 0; j < NC; ++j) o.al[j] = expf(o.al[j]);
+  for (int i = 0; i < NR; ++i) o.v[i] = to_f32(((const Tin*)p.v)[tt * DV + rg + 16 * i]);
   if constexpr (G2) {
-    float b[NC];
-    load_cols<DK, Tin>((const Tin*)p.bg + tt * DK, cl, b);
+    load_cols<DK, Tin>((const Tin*)p.bg + tt * DK, cl, o.b);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) o.w[i] = to_f32(((const Tin*)p.wg)[tt * DV + rg + 16 * i]);
+  } else {
+    o.bt = p.beta[tt];
+    o.rt = p.r ? p.r[tt] : 1.f;
+  }
+}
+
+// The unified operands x, z, y, c (and OSDN's key statistics) from a token's
+// inputs and, for OSDN, its preconditioner dt.
+template <int DK, int DV, bool G2>
+__device__ __forceinline__ void make_tok(const Raw<DK, DV>& r, const float (&dt)[DK / 16],
+                                         Tok<DK, DV>& o) {
+  constexpr int NC = DK / 16, NR = DV / 16;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    o.kk[j] = r.kk[j];
+    o.al[j] = expf(r.la[j]);
+  }
+  if constexpr (G2) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      o.x[j] = b[j] * o.kk[j];
-      o.z[j] = o.kk[j];
+      o.x[j] = r.b[j] * r.kk[j];
+      o.z[j] = r.kk[j];
     }
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const size_t e = tt * DV + rg + 16 * i;
-      o.y[i] = to_f32(((const Tin*)p.wg)[e]) * to_f32(((const Tin*)p.v)[e]);
-    }
+    for (int i = 0; i < NR; ++i) o.y[i] = r.w[i] * r.v[i];
     o.c = 1.f;
   } else {
     float n = 0.f, c = 0.f;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      const float a = o.kk[j] * o.kk[j];
+      const float a = r.kk[j] * r.kk[j];
       n += a;
       c += dt[j] * a;
-      o.x[j] = o.kk[j];
-      o.z[j] = dt[j] * o.kk[j];
+      o.x[j] = r.kk[j];
+      o.z[j] = dt[j] * r.kk[j];
     }
     o.n = row16_sum(n);
     o.cc = row16_sum(c);
 #pragma unroll
-    for (int i = 0; i < NR; ++i) o.y[i] = to_f32(((const Tin*)p.v)[tt * DV + rg + 16 * i]);
-    o.bt = p.beta[tt];
-    o.rt = p.r ? p.r[tt] : 1.f;
-    o.c = o.bt;
+    for (int i = 0; i < NR; ++i) o.y[i] = r.v[i];
+    o.bt = r.bt;
+    o.rt = r.rt;
+    o.c = r.bt;
   }
 }
 
@@ -213,12 +237,16 @@ __global__ __launch_bounds__(kDecThreads) void gated_bwd_record_kernel(GParams p
   for (int j = 0; j < NC; ++j) dv[j] = 1.f;
   if (!G2 && p.d0) load_cols<DK, float>(p.d0 + (size_t)bh * DK, cl, dv);
 
+  const size_t tb = (size_t)bh * T;
+  Raw<DK, DV> nx;
+  if (T > 0) raw_load<DK, DV, Tin, G2>(p, tb, rg, cl, nx);
   for (int t = 0; t < T; ++t) {
     if (t % kGCkpt == 0) store_rows<DK, DV>(Cb + (size_t)(t / kGCkpt) * DV * DK, rg, cl, s);
-    const size_t tt = (size_t)bh * T + t;
     if (!G2 && rg == 0) store_cols<DK>(Db + (size_t)t * DK, cl, dv);
+    const Raw<DK, DV> cur = nx;
+    if (t + 1 < T) raw_load<DK, DV, Tin, G2>(p, tb + t + 1, rg, cl, nx);
     Tok<DK, DV> tk;
-    load_tok<DK, DV, Tin, G2>(p, tt, rg, cl, dv, tk);
+    make_tok<DK, DV, G2>(cur, dv, tk);
     fwd_step<DK, DV>(s, tk);
     if constexpr (!G2) learner_step<DK, DV>(dv, tk, p.eta);
   }
@@ -257,29 +285,58 @@ __global__ __launch_bounds__(kDecThreads) void gated_bwd_kernel(GParams p) {
   float eta_acc = 0.f;
   int par = 0;
 
+  const size_t tb = (size_t)bh * T;
   for (int iv = nck - 1; iv >= 0; --iv) {
     const int t0 = iv * kGCkpt, t1 = min(T, t0 + kGCkpt) - 1;
     // the interval forward: the state before each of its tokens but the last
+    // (inputs one token ahead)
     load_rows<DK, DV>(Cb + (size_t)iv * DV * DK, rg, cl, s);
+    Raw<DK, DV> nx;
+    float dn[NC];
+    if (t0 < t1) {
+      raw_load<DK, DV, Tin, G2>(p, tb + t0, rg, cl, nx);
+      if constexpr (!G2) load_cols<DK, float>(Db + (size_t)t0 * DK, cl, dn);
+    }
     for (int t = t0; t < t1; ++t) {
       store_rows<DK, DV>(Sb + (size_t)(t - t0) * DV * DK, rg, cl, s);
+      const Raw<DK, DV> cur = nx;
       float dt[NC];
-      if constexpr (!G2) load_cols<DK, float>(Db + (size_t)t * DK, cl, dt);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) dt[j] = dn[j];
+      if (t + 1 < t1) {
+        raw_load<DK, DV, Tin, G2>(p, tb + t + 1, rg, cl, nx);
+        if constexpr (!G2) load_cols<DK, float>(Db + (size_t)(t + 1) * DK, cl, dn);
+      }
       Tok<DK, DV> tk;
-      load_tok<DK, DV, Tin, G2>(p, (size_t)bh * T + t, rg, cl, dt, tk);
+      make_tok<DK, DV, G2>(cur, dt, tk);
       fwd_step<DK, DV>(s, tk);
     }
-    // and backwards through it
+    // and backwards through it (inputs one token ahead)
+    float qn[NC], don[NR];
+    auto prefetch = [&](int t) {
+      const size_t tt = tb + t;
+      raw_load<DK, DV, Tin, G2>(p, tt, rg, cl, nx);
+      if constexpr (!G2) load_cols<DK, float>(Db + (size_t)t * DK, cl, dn);
+      load_cols<DK, Tin>(q + tt * DK, cl, qn);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) don[i] = to_f32(dout[tt * DV + rg + 16 * i]);
+    };
+    prefetch(t1);
     for (int t = t1; t >= t0; --t) {
       if (t < t1) load_rows<DK, DV>(Sb + (size_t)(t - t0) * DV * DK, rg, cl, s);
-      const size_t tt = (size_t)bh * T + t;
+      const size_t tt = tb + t;
       float dt[NC], qq[NC], dov[NR];
-      if constexpr (!G2) load_cols<DK, float>(Db + (size_t)t * DK, cl, dt);
-      Tok<DK, DV> tk;
-      load_tok<DK, DV, Tin, G2>(p, tt, rg, cl, dt, tk);
-      load_cols<DK, Tin>(q + tt * DK, cl, qq);
+      const Raw<DK, DV> cur = nx;
 #pragma unroll
-      for (int i = 0; i < NR; ++i) dov[i] = to_f32(dout[tt * DV + rg + 16 * i]);
+      for (int j = 0; j < NC; ++j) {
+        dt[j] = dn[j];
+        qq[j] = qn[j];
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) dov[i] = don[i];
+      if (t > t0) prefetch(t - 1);
+      Tok<DK, DV> tk;
+      make_tok<DK, DV, G2>(cur, dt, tk);
 
       // S_dec, u = y - S_dec x; dS += scale do q^T; w = dS z (row sums)
       float u[NR], w[NR];
@@ -388,11 +445,10 @@ __global__ __launch_bounds__(kDecThreads) void gated_bwd_kernel(GParams p) {
       }
       if constexpr (G2) {
         // x = b*k, z = k, y = w*v
-        float gk[NC], gb[NC], bb[NC];
-        load_cols<DK, Tin>((const Tin*)p.bg + tt * DK, cl, bb);
+        float gk[NC], gb[NC];
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
-          gk[j] = gz[j] + bb[j] * gx[j];
+          gk[j] = gz[j] + cur.b[j] * gx[j];
           gb[j] = tk.kk[j] * gx[j];
         }
         if (rg == 0) {
@@ -403,8 +459,8 @@ __global__ __launch_bounds__(kDecThreads) void gated_bwd_kernel(GParams p) {
         for (int i = 0; i < NR; ++i) {
           if (cl == (i & 15)) {
             const size_t e = tt * DV + rg + 16 * i;
-            p.dv[e] = to_f32(((const Tin*)p.wg)[e]) * w[i];
-            p.dw[e] = to_f32(((const Tin*)p.v)[e]) * w[i];
+            p.dv[e] = cur.w[i] * w[i];
+            p.dw[e] = cur.v[i] * w[i];
           }
         }
       } else {

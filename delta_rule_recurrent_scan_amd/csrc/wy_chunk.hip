@@ -494,6 +494,12 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     float* Lsb = reinterpret_cast<float*>(smem + G::oYs);  // [TB][DK]
     float* Leb = Lsb + TB * DK;                             // [TB][DK]
     bool ex_diag = false;  // wave-uniform: this wave's diagonal tile is exact
+    // workgroup-uniform: the whole chunk decays by at most e^-kExactDiag in
+    // every channel, so factors relative to the chunk start stay finite
+    // (read keys and queries times gamma_t <= 1, write keys over gamma_t
+    // <= e^kExactDiag) and the per-tile factors of the block split are not
+    // needed
+    bool fast = true;
     auto decay_pass = [&]() {
       // Decay pass. (1) Column scan: TPC threads per channel c (lanes l and
       // l + 64/TPC of one wave), each over TPT consecutive tokens, turn the
@@ -529,12 +535,21 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         if (part == 0) gC[c] = __expf(total_la);
       }
       __syncthreads();
-      for (int e = tid; e < TB * DK; e += G::NT) {
-        const int b = e / DK, c = e - b * DK;
-        Lsb[e] = La[(16 * b) * LDA + c];
-        Leb[e] = La[(16 * b + 15) * LDA + c];
+      {
+        float m = 1.f;
+        for (int c = lane; c < DK; c += 64) m = fminf(m, gC[c]);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) m = fminf(m, __shfl_xor(m, d, 64));
+        fast = __builtin_amdgcn_readfirstlane(m >= __expf(-kExactDiag) ? 1 : 0) != 0;
       }
-      if (wave < TB) {
+      if (!fast) {
+        for (int e = tid; e < TB * DK; e += G::NT) {
+          const int b = e / DK, c = e - b * DK;
+          Lsb[e] = La[(16 * b) * LDA + c];
+          Leb[e] = La[(16 * b + 15) * LDA + c];
+        }
+      }
+      if (!fast && wave < TB) {
         // wave a owns diagonal tile a in the Gram step
         const int a = wave;
         float m = -1.f;
@@ -589,8 +604,11 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
 #pragma unroll
         for (int u = 0; u < VEC; ++u) {
           const float lt = La[t * LDA + c0 + u];
-          const float fs = __expf(lt - Lsb[tb * DK + c0 + u]);  // <= 1
-          const float fe = __expf(Leb[tb * DK + c0 + u] - lt);  // <= 1
+          // relative to the chunk start (fast) or to t's block
+          const float rs = fast ? 0.f : Lsb[tb * DK + c0 + u];
+          const float re = fast ? 0.f : Leb[tb * DK + c0 + u];
+          const float fs = __expf(lt - rs);  // <= 1
+          const float fe = __expf(re - lt);  // <= 1 (block split), <= e^60 (fast)
           const float kk = to_f32(kv[u]);
           xo[u] = from_f32<Tin>(kk * fe);
           if constexpr (kGdn2)
@@ -693,11 +711,14 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         fq.load(Qs + a * 16 * LDK, LDK);
         fx.load(Xs + b * 16 * LDK, LDK);
         if constexpr (kDecay) {
-          // exp(lambda_{s_a} - lambda_{e_b}) per key channel (exponent capped
-          // where an exact diagonal replaces the product anyway)
-          const float* ls = Lsb + a * DK;
-          const float* le = Leb + b * DK;
-          scale_row_frag(fx, [&](int c) { return __expf(fminf(ls[c] - le[c], 80.f)); });
+          // block split: exp(lambda_{s_a} - lambda_{e_b}) per key channel
+          // (exponent capped where an exact diagonal replaces the product
+          // anyway)
+          if (!fast) {
+            const float* ls = Lsb + a * DK;
+            const float* le = Leb + b * DK;
+            scale_row_frag(fx, [&](int c) { return __expf(fminf(ls[c] - le[c], 80.f)); });
+          }
         }
         // A tile (a, b); the scores as their transpose, tile (b, a) of
         // P^T = X Q^T, whose accumulator lanes hold exactly the scan's
@@ -778,13 +799,19 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
         Frag<C, Tin> fx;
         fx.load_kmajor_perm(Xs + db * 16, LDK);  // the scan's k order
         if constexpr (kDecay) {
-          // exit keys x_i gamma_C / gamma_i = X_i exp(lambda_C - lambda_{e_b})
+          // exit keys x_i gamma_C / gamma_i = X_i gamma_C (fast), or
+          // X_i exp(lambda_C - lambda_{e_b}) (block split)
           const int c = db * 16 + (lane & 15);
-          float fb[TB];
+          if (fast) {
+            const float gc = gC[c];
+            scale_kperm_frag(fx, [&](int) { return gc; });
+          } else {
+            float fb[TB];
 #pragma unroll
-          for (int b2 = 0; b2 < TB; ++b2)
-            fb[b2] = __expf(Leb[(TB - 1) * DK + c] - Leb[b2 * DK + c]);
-          scale_kperm_frag(fx, [&](int t) { return fb[t >> 4]; });
+            for (int b2 = 0; b2 < TB; ++b2)
+              fb[b2] = __expf(Leb[(TB - 1) * DK + c] - Leb[b2 * DK + c]);
+            scale_kperm_frag(fx, [&](int t) { return fb[t >> 4]; });
+          }
         }
         fx.store_global(wb.xp + xoff + (size_t)db * 16 * C);
       }
@@ -793,7 +820,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       }
     }
     __syncthreads();
-    if constexpr (kDecay) {
+    if (kDecay && !fast) {
       // read keys and queries relative to the chunk start from here on (for
       // Wk and the decayed queries): times exp(lambda_{s_b}) <= 1
       constexpr int VEC = G::VEC;
