@@ -529,7 +529,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="osdn-1.3b-apf",
                     choices=[w.name for w in W.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
