@@ -54,6 +54,7 @@ _KERNEL_SOURCES = {
     "gdn2_decode": ["decode.hip"],
     "osdn_bwd_record": ["backward.hip", "row_state.hpp"],
     "osdn_bwd": ["backward.hip", "row_state.hpp"],
+    "osdn_bwd_learner": ["backward.hip", "row_state.hpp"],
     "gated_bwd_record": ["backward_gated.hip", "row_state.hpp"],
     "gated_bwd": ["backward_gated.hip", "row_state.hpp"],
     "gdn2_bwd_record": ["backward_gated.hip", "row_state.hpp"],

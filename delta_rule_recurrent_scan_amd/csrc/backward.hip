@@ -7,36 +7,58 @@
 // eta, d0 and S0: the memory update's adjoint and, through k~ and the
 // learner's step, the adjoint of the phase-1 preconditioner scan.
 //
-// Two kernels, one workgroup (256 threads) per (batch, head), the state held
-// in registers in the row layout of row_state.hpp:
-//   record   runs the recurrence forward and stores, per token, the residual
-//            u_t (Dv fp32) and the preconditioner d_t (Dk fp32), plus the
-//            state every kCkpt tokens and after the last one (fp32);
-//   reverse  walks the tokens backwards with S and its adjoint dS in
-//            registers: S_{t-1} = S_t - beta_t u_t k~_t^T (reset exactly from
-//            the stored state every kCkpt tokens), dS carried down.
-// Per token, the sums over value rows (S_t^T do, dS^T u, S_{t-1}^T w, u.w)
-// are the four row groups of a wave by cross-row swaps, then the four waves
-// through LDS (one barrier, buffers alternating by token).
+// The recurrences of S and of its adjoint dS act on each value row on its
+// own (row i of S_t needs only row i of S_{t-1}; likewise dS), so a stream's
+// rows are split into slices of kBwdSliceRows, one workgroup each, which
+// fills the chip with B*H*Dv/32 workgroups. What couples the rows are the
+// gradient sums over value rows (S_t^T do, dS^T u, S_{t-1}^T w, u.w) and,
+// through dS^T u, the adjoint of the learner; so three kernels:
+//   record   (per slice) runs the recurrence forward and stores, per token,
+//            the residual u_t of its rows and (one slice) the preconditioner
+//            d_t, plus its rows of the state every kCkpt tokens and after
+//            the last one (fp32);
+//   reverse  (per slice) walks the tokens backwards with its rows of S and
+//            dS in registers: S_{t-1} = S_t - beta_t u_t k~_t^T (reset exactly
+//            from the stored state every kCkpt tokens), and writes, per
+//            token, the slice's share of the four row sums;
+//   learner  (one workgroup per stream) walks the tokens backwards once more,
+//            adds the slices' shares, and carries the adjoint of d through
+//            the learner's step: it forms the gradients of q, k, beta, r and
+//            eta, and d0's.
+// The state sits in registers in the row layout of row_state.hpp (a row over
+// 16 column lanes), with kBwdRG row groups of kBwdNR rows each.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "row_state.hpp"
 
 namespace osdn {
 
-constexpr int kCkpt = 64;  // tokens between stored states
+constexpr int kCkpt = 64;                         // tokens between stored states
+constexpr int kBwdNR = 2;                         // value rows per thread
+constexpr int kBwdThreads = 256;                  // 16 row groups x 16 column lanes
+constexpr int kBwdRG = kBwdThreads / 16;          // row groups
+constexpr int kBwdSliceRows = kBwdRG * kBwdNR;    // value rows per workgroup
+// How far ahead each kernel fetches its token operands (register ring sizes):
+// each token's chain step is a few hundred cycles, a fetch from HBM takes
+// thousands.
+constexpr int kRecAhead = 8, kRevAhead = 4;
 
 __host__ __device__ inline int nckpt(int T) { return (T + kCkpt - 1) / kCkpt; }
+// Per token and slice: S_t^T do, dS^T u, S_{t-1}^T w (Dk each), then u.w,
+// padded to a 16-byte multiple.
+__host__ __device__ constexpr int share_width(int Dk) { return 3 * Dk + 4; }
 
 size_t backward_workspace_bytes(int B, int H, int T, int Dk, int Dv) {
   const size_t BH = (size_t)B * H;
-  return BH * ((size_t)T * (Dv + Dk) + (size_t)(nckpt(T) + 1) * Dv * Dk) * 4;
+  const size_t rs = (size_t)Dv / kBwdSliceRows;
+  return BH * ((size_t)T * (Dv + Dk) + (size_t)(nckpt(T) + 1) * Dv * Dk +
+               (size_t)T * rs * share_width(Dk)) * 4;
 }
 
 namespace {
 
 struct BwdBufs {
-  float *u, *d, *ck;
+  float *u, *d, *ck, *sh;
 };
 
 BwdBufs bwd_bufs(void* ws, int BH, int T, int Dk, int Dv) {
@@ -45,17 +67,31 @@ BwdBufs bwd_bufs(void* ws, int BH, int T, int Dk, int Dv) {
   b.u = f;
   b.d = b.u + (size_t)BH * T * Dv;
   b.ck = b.d + (size_t)BH * T * Dk;
+  b.sh = b.ck + (size_t)BH * (nckpt(T) + 1) * Dv * Dk;
   return b;
 }
 
+// Workgroup -> (stream, slice): the slices of a stream are 8 workgroups
+// apart, so that workgroups dispatched round-robin over the eight XCDs put
+// all of a stream's slices on one XCD (they read the same keys and queries).
+__device__ __forceinline__ void slice_of(int RS, int& bh, int& sl) {
+  const int x = blockIdx.x, grp = x / (8 * RS), rr = x % (8 * RS);
+  sl = rr / 8;
+  bh = grp * 8 + rr % 8;
+}
+int bwd_grid(int BH, int RS) { return ((BH + 7) / 8) * 8 * RS; }
+
 template <int DK, int DV, typename Tin>
-__global__ __launch_bounds__(kDecThreads) void osdn_bwd_record_kernel(
-    int T, const Tin* __restrict__ k, const Tin* __restrict__ v,
+__global__ __launch_bounds__(kBwdThreads) void osdn_bwd_record_kernel(
+    int BH, int T, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ r, float eta,
     const float* __restrict__ d0, const float* __restrict__ S0, BwdBufs wb) {
-  constexpr int NC = DK / 16, NR = DV / 16;
-  const int bh = blockIdx.x;
+  constexpr int NC = DK / 16, NR = kBwdNR, RS = DV / kBwdSliceRows;
+  int bh, sl;
+  slice_of(RS, bh, sl);
+  if (bh >= BH) return;
   const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
+  const int row0 = sl * kBwdSliceRows + rg;  // rows row0 + kBwdRG i
   const int nck = nckpt(T);
   float* Ub = wb.u + (size_t)bh * T * DV;
   float* Db = wb.d + (size_t)bh * T * DK;
@@ -65,7 +101,7 @@ __global__ __launch_bounds__(kDecThreads) void osdn_bwd_record_kernel(
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     if (S0) {
-      load_cols<DK, float>(S0 + ((size_t)bh * DV + rg + 16 * i) * DK, cl, s[i]);
+      load_cols<DK, float>(S0 + ((size_t)bh * DV + row0 + kBwdRG * i) * DK, cl, s[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < NC; ++j) s[i][j] = 0.f;
@@ -78,309 +114,446 @@ __global__ __launch_bounds__(kDecThreads) void osdn_bwd_record_kernel(
     for (int j = 0; j < NC; ++j) dv[j] = 1.f;
   }
 
-  // the next token's inputs are loaded one token ahead, off the chain
+  // token inputs fetched kRecAhead tokens ahead into a ring of register
+  // sets (the loop is unrolled by the ring size, so each set is static)
+  struct Tok {
+    float kk[NC], vv[NR], bt, rt;
+  };
   const size_t tb = (size_t)bh * T;
-  float kn[NC], vn[NR], bn = 0.f, rn = 1.f;
+  auto fetch = [&](Tok& o, int t) {
+    const size_t tn = tb + t;
+    load_cols<DK, Tin>(k + tn * DK, cl, o.kk);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) o.vv[i] = to_f32(v[tn * DV + row0 + kBwdRG * i]);
+    o.bt = beta[tn];
+    o.rt = r ? r[tn] : 1.f;
+  };
+  // (fetches are unconditional, of clamped tokens, so that the compiler can
+  // count the loads in flight and waits only for the set it uses)
+  Tok ring[kRecAhead];
   if (T > 0) {
-    load_cols<DK, Tin>(k + tb * DK, cl, kn);
 #pragma unroll
-    for (int i = 0; i < NR; ++i) vn[i] = to_f32(v[tb * DV + rg + 16 * i]);
-    bn = beta[tb];
-    rn = r ? r[tb] : 1.f;
+    for (int u = 0; u < kRecAhead; ++u) fetch(ring[u], min(u, T - 1));
   }
-  for (int t = 0; t < T; ++t) {
-    if (t % kCkpt == 0) {
-      float* C = Cb + (size_t)(t / kCkpt) * DV * DK;
+  for (int base = 0; base < T; base += kRecAhead) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) store_cols<DK>(C + (size_t)(rg + 16 * i) * DK, cl, s[i]);
+    for (int u = 0; u < kRecAhead; ++u) {
+      const int t = base + u;
+      if (t >= T) break;
+      if (t % kCkpt == 0) {
+        float* C = Cb + (size_t)(t / kCkpt) * DV * DK;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) store_cols<DK>(C + (size_t)(row0 + kBwdRG * i) * DK, cl, s[i]);
+      }
+      const Tok cur = ring[u];
+      fetch(ring[u], min(t + kRecAhead, T - 1));
+      float n = 0.f, c = 0.f, kt[NC], p[NR];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const float a = cur.kk[j] * cur.kk[j];
+        n += a;
+        c += dv[j] * a;
+        kt[j] = dv[j] * cur.kk[j];
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) acc += s[i][j] * cur.kk[j];
+        p[i] = acc;
+      }
+      n = row16_sum(n);
+      c = row16_sum(c);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) p[i] = row16_sum(p[i]);
+      if (sl == 0 && rg == 0) store_cols<DK>(Db + (size_t)t * DK, cl, dv);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float u0 = cur.vv[i] - p[i];
+        Ub[(size_t)t * DV + row0 + kBwdRG * i] = u0;  // the row's 16 lanes agree
+        const float bu = cur.bt * u0;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) s[i][j] += bu * kt[j];
+      }
+      const float g = n > 0.f ? eta * cur.bt * (1.f - cur.bt * c) / n : 0.f;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) dv[j] = cur.rt * dv[j] + g * (cur.kk[j] * cur.kk[j]);
     }
-    float kk[NC], vv[NR];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) kk[j] = kn[j];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) vv[i] = vn[i];
-    const float bt = bn, rt = rn;
-    if (t + 1 < T) {
-      const size_t tn = tb + t + 1;
-      load_cols<DK, Tin>(k + tn * DK, cl, kn);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) vn[i] = to_f32(v[tn * DV + rg + 16 * i]);
-      bn = beta[tn];
-      rn = r ? r[tn] : 1.f;
-    }
-    float n = 0.f, c = 0.f, kt[NC], p[NR];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const float a = kk[j] * kk[j];
-      n += a;
-      c += dv[j] * a;
-      kt[j] = dv[j] * kk[j];
-    }
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < NC; ++j) acc += s[i][j] * kk[j];
-      p[i] = acc;
-    }
-    n = row16_sum(n);
-    c = row16_sum(c);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) p[i] = row16_sum(p[i]);
-    if (rg == 0) store_cols<DK>(Db + (size_t)t * DK, cl, dv);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const float u = vv[i] - p[i];
-      if (cl == (i & 15)) Ub[(size_t)t * DV + rg + 16 * i] = u;
-      const float bu = bt * u;
-#pragma unroll
-      for (int j = 0; j < NC; ++j) s[i][j] += bu * kt[j];
-    }
-    const float g = n > 0.f ? eta * bt * (1.f - bt * c) / n : 0.f;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) dv[j] = rt * dv[j] + g * (kk[j] * kk[j]);
   }
   float* C = Cb + (size_t)nck * DV * DK;
 #pragma unroll
-  for (int i = 0; i < NR; ++i) store_cols<DK>(C + (size_t)(rg + 16 * i) * DK, cl, s[i]);
+  for (int i = 0; i < NR; ++i) store_cols<DK>(C + (size_t)(row0 + kBwdRG * i) * DK, cl, s[i]);
 }
 
 template <int DK, int DV, typename Tin>
-__global__ __launch_bounds__(kDecThreads) void osdn_bwd_kernel(
-    int T, const Tin* __restrict__ q, const Tin* __restrict__ k,
-    const float* __restrict__ beta, const float* __restrict__ r, float eta, float scale,
-    const Tin* __restrict__ dout, const float* __restrict__ dST,
-    const float* __restrict__ ddT, BwdBufs wb, float* __restrict__ gq,
-    float* __restrict__ gk, float* __restrict__ gv, float* __restrict__ gbeta,
-    float* __restrict__ gr, float* __restrict__ geta, float* __restrict__ gd0,
+__global__ __launch_bounds__(kBwdThreads) void osdn_bwd_kernel(
+    int BH, int T, const Tin* __restrict__ q, const Tin* __restrict__ k,
+    const float* __restrict__ beta, float scale, const Tin* __restrict__ dout,
+    const float* __restrict__ dST, BwdBufs wb, float* __restrict__ gv,
     float* __restrict__ gS0) {
-  constexpr int NC = DK / 16, NR = DV / 16, NW = kDecThreads / kWave;
-  constexpr int RW = 3 * DK + 4;  // per wave: S^T do, dS^T u, S_{t-1}^T w, u.w
-  __shared__ float red[2][NW][RW];
-  const int bh = blockIdx.x;
+  constexpr int NC = DK / 16, NR = kBwdNR, RS = DV / kBwdSliceRows;
+  constexpr int NW = kBwdThreads / kWave, SW = share_width(DK);
+  __shared__ __attribute__((aligned(16))) float red[2][NW][SW];
+  int bh, sl;
+  slice_of(RS, bh, sl);
+  if (bh >= BH) return;
   const int cl = threadIdx.x & 15, rg = threadIdx.x >> 4;
   const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int row0 = sl * kBwdSliceRows + rg;
   const int nck = nckpt(T);
   const float* Ub = wb.u + (size_t)bh * T * DV;
   const float* Db = wb.d + (size_t)bh * T * DK;
   const float* Cb = wb.ck + (size_t)bh * (nck + 1) * DV * DK;
+  float* Sh = wb.sh + (size_t)bh * T * RS * SW + (size_t)sl * SW;
 
-  // S after the last token, dS and the adjoint of d after it
-  float s[NR][NC], ds[NR][NC], dd[NC];
+  // S after the last token and dS, for this slice's rows
+  float s[NR][NC], ds[NR][NC];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    load_cols<DK, float>(Cb + (size_t)nck * DV * DK + (size_t)(rg + 16 * i) * DK, cl, s[i]);
+    load_cols<DK, float>(Cb + (size_t)nck * DV * DK + (size_t)(row0 + kBwdRG * i) * DK, cl, s[i]);
     if (dST) {
-      load_cols<DK, float>(dST + ((size_t)bh * DV + rg + 16 * i) * DK, cl, ds[i]);
+      load_cols<DK, float>(dST + ((size_t)bh * DV + row0 + kBwdRG * i) * DK, cl, ds[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < NC; ++j) ds[i][j] = 0.f;
     }
   }
-  if (ddT) {
-    load_cols<DK, float>(ddT + (size_t)bh * DK, cl, dd);
-  } else {
-#pragma unroll
-    for (int j = 0; j < NC; ++j) dd[j] = 0.f;
-  }
-  float eta_acc = 0.f;
 
-  // the previous token's inputs are loaded one token ahead, off the chain
-  const size_t tb = (size_t)bh * T;
-  float kn[NC], qn[NC], dn_[NC], don[NR], un[NR], bn = 0.f, rn = 1.f;
-  auto prefetch = [&](int t) {
-    const size_t tt = tb + t;
-    load_cols<DK, Tin>(k + tt * DK, cl, kn);
-    load_cols<DK, Tin>(q + tt * DK, cl, qn);
-    load_cols<DK, float>(Db + (size_t)t * DK, cl, dn_);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      don[i] = to_f32(dout[tt * DV + rg + 16 * i]);
-      un[i] = Ub[(size_t)t * DV + rg + 16 * i];
-    }
-    bn = beta[tt];
-    rn = r ? r[tt] : 1.f;
+  // token inputs fetched kRevAhead tokens ahead into a ring of register
+  // sets (the loop is unrolled by the ring size, so each set is static)
+  struct Tok {
+    float kk[NC], qq[NC], dt[NC], dov[NR], uu[NR], bt;
   };
-  if (T > 0) prefetch(T - 1);
-  for (int t = T - 1; t >= 0; --t) {
+  const size_t tb = (size_t)bh * T;
+  auto fetch = [&](Tok& o, int t) {
     const size_t tt = tb + t;
-    float kk[NC], qq[NC], dt[NC], dov[NR], uu[NR];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      kk[j] = kn[j];
-      qq[j] = qn[j];
-      dt[j] = dn_[j];
-    }
+    load_cols<DK, Tin>(k + tt * DK, cl, o.kk);
+    load_cols<DK, Tin>(q + tt * DK, cl, o.qq);
+    load_cols<DK, float>(Db + (size_t)t * DK, cl, o.dt);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      dov[i] = don[i];
-      uu[i] = un[i];
+      o.dov[i] = to_f32(dout[tt * DV + row0 + kBwdRG * i]);
+      o.uu[i] = Ub[(size_t)t * DV + row0 + kBwdRG * i];
     }
-    const float bt = bn, rt = rn;
-    if (t > 0) prefetch(t - 1);
-    float n = 0.f, c = 0.f, a[NC], kt[NC];
+    o.bt = beta[tt];
+  };
+  Tok ring[kRevAhead];
+  if (T > 0) {
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      a[j] = kk[j] * kk[j];
-      n += a[j];
-      c += dt[j] * a[j];
-      kt[j] = dt[j] * kk[j];
-    }
-    n = row16_sum(n);
-    c = row16_sum(c);
-    const float g = n > 0.f ? eta * bt * (1.f - bt * c) / n : 0.f;
+    for (int u = 0; u < kRevAhead; ++u) fetch(ring[u], max(T - 1 - u, 0));
+  }
+  for (int base = 0; base < T; base += kRevAhead) {
+#pragma unroll
+    for (int u = 0; u < kRevAhead; ++u) {
+      const int t = T - 1 - (base + u);
+      if (t < 0) break;
+      const size_t tt = tb + t;
+      const Tok cur = ring[u];
+      fetch(ring[u], max(t - kRevAhead, 0));
+      float kt[NC];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) kt[j] = cur.dt[j] * cur.kk[j];
+      const float* kk = cur.kk;
+      const float* qq = cur.qq;
+      const float* dov = cur.dov;
+      const float* uu = cur.uu;
+      const float bt = cur.bt;
+      // o_t = scale S_t q_t:  dS += scale do q^T; then w = dS k~ (row sums)
+      // and dS^T u (column partials)
+      float w[NR], pu[NC], pq[NC], py[NC];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) pu[j] = pq[j] = py[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float sd = scale * dov[i];
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          ds[i][j] += sd * qq[j];
+          acc += ds[i][j] * kt[j];
+          pu[j] += ds[i][j] * uu[i];
+        }
+        w[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < NR; ++i) w[i] = row16_sum(w[i]);
+      // S_t^T do (column partials), then S_{t-1} = S_t - beta u k~^T (the
+      // stored state at a checkpoint), S_{t-1}^T w, and dS_{t-1} = dS -
+      // beta w k^T
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const float bu = bt * uu[i], bw = bt * w[i];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          pq[j] += s[i][j] * dov[i];
+          s[i][j] -= bu * kt[j];
+          ds[i][j] -= bw * kk[j];
+        }
+      }
+      if (t % kCkpt == 0) {
+        const float* C = Cb + (size_t)(t / kCkpt) * DV * DK;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) load_cols<DK, float>(C + (size_t)(row0 + kBwdRG * i) * DK, cl, s[i]);
+      }
+      float pb = 0.f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+#pragma unroll
+        for (int j = 0; j < NC; ++j) py[j] += s[i][j] * w[i];
+        pb += uu[i] * w[i];
+      }
+      pb = cl == 0 ? pb : 0.f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        if (cl == i) gv[tt * DV + row0 + kBwdRG * i] = bt * w[i];
 
-    // o_t = scale S_t q_t:  dS += scale do q^T; then w = dS k~ (row sums)
-    // and dS^T u (column partials)
-    float w[NR], pu[NC], pq[NC], py[NC];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) pu[j] = pq[j] = py[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const float sd = scale * dov[i];
-      float acc = 0.f;
+      // the slice's sums over its rows: four row groups per wave by swaps,
+      // the waves through LDS (buffers alternating by token, one barrier),
+      // one coalesced store per token
+      const int b = t & 1;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
-        ds[i][j] += sd * qq[j];
-        acc += ds[i][j] * kt[j];
-        pu[j] += ds[i][j] * uu[i];
+        pq[j] = add_swap32(add_swap16(pq[j]));
+        pu[j] = add_swap32(add_swap16(pu[j]));
+        py[j] = add_swap32(add_swap16(py[j]));
       }
-      w[i] = acc;
-    }
+      pb = wave_sum(pb);
+      if (lane < 16) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) w[i] = row16_sum(w[i]);
-    // S_t^T do (column partials), then S_{t-1} = S_t - beta u k~^T (the
-    // stored state at a checkpoint), S_{t-1}^T w, and dS_{t-1} = dS -
-    // beta w k^T
-    const bool ck = t % kCkpt == 0;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const float bu = bt * uu[i], bw = bt * w[i];
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        pq[j] += s[i][j] * dov[i];
-        s[i][j] -= bu * kt[j];
-        ds[i][j] -= bw * kk[j];
+        for (int j = 0; j < NC; ++j) {
+          const int col = dec_col<DK>(cl, j);
+          red[b][wave][col] = pq[j];
+          red[b][wave][DK + col] = pu[j];
+          red[b][wave][2 * DK + col] = py[j];
+        }
+        if (lane == 0) red[b][wave][3 * DK] = pb;
       }
-    }
-    if (ck) {
-      const float* C = Cb + (size_t)(t / kCkpt) * DV * DK;
+      __syncthreads();
+      float* sh = Sh + (size_t)t * RS * SW;
+      for (int e = threadIdx.x; e < 3 * DK + 1; e += kBwdThreads) {
+        float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < NR; ++i) load_cols<DK, float>(C + (size_t)(rg + 16 * i) * DK, cl, s[i]);
-    }
-    float pb = 0.f;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) py[j] += s[i][j] * w[i];
-      pb += uu[i] * w[i];
-    }
-    pb = cl == 0 ? pb : 0.f;
-
-    // sums over the 16 row groups: four per wave by swaps, four waves via LDS
-    const int b = t & 1;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      pq[j] = add_swap32(add_swap16(pq[j]));
-      pu[j] = add_swap32(add_swap16(pu[j]));
-      py[j] = add_swap32(add_swap16(py[j]));
-    }
-    pb = wave_sum(pb);
-    if (lane < 16) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int col = dec_col<DK>(cl, j);
-        red[b][wave][col] = pq[j];
-        red[b][wave][DK + col] = pu[j];
-        red[b][wave][2 * DK + col] = py[j];
+        for (int m = 0; m < NW; ++m) acc += red[b][m][e];
+        sh[e] = acc;
       }
-      if (lane == 0) red[b][wave][3 * DK] = pb;
-    }
-    __syncthreads();
-    float sq[NC], su[NC], sy[NC];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const int col = dec_col<DK>(cl, j);
-      sq[j] = su[j] = sy[j] = 0.f;
-#pragma unroll
-      for (int m = 0; m < NW; ++m) {
-        sq[j] += red[b][m][col];
-        su[j] += red[b][m][DK + col];
-        sy[j] += red[b][m][2 * DK + col];
-      }
-    }
-    float uw = 0.f;
-#pragma unroll
-    for (int m = 0; m < NW; ++m) uw += red[b][m][3 * DK];
-
-    // adjoints of v, q; of k~ and k through the write and the read
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-      if (cl == (i & 15)) gv[tt * DV + rg + 16 * i] = bt * w[i];
-    float dk[NC], ddt[NC], da[NC];
-    float pr = 0.f, pg = 0.f;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      sq[j] *= scale;
-      const float dkt = bt * su[j];
-      dk[j] = -bt * sy[j] + dkt * dt[j];
-      ddt[j] = dkt * kk[j] + rt * dd[j];
-      pr += dd[j] * dt[j];
-      pg += dd[j] * a[j];
-      da[j] = g * dd[j];
-    }
-    const float drt = row16_sum(pr);
-    const float dg = row16_sum(pg);
-    // the learner's step g = eta beta (1 - beta c)/n, only where n > 0
-    float dbt = uw;
-    if (n > 0.f) {
-      const float dc = -eta * bt * bt / n * dg;
-      dbt += eta * (1.f - 2.f * bt * c) / n * dg;
-      const float dn = -g / n * dg;
-      eta_acc += bt * (1.f - bt * c) / n * dg;
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        ddt[j] += dc * a[j];
-        da[j] += dc * dt[j] + dn;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      dk[j] += 2.f * kk[j] * da[j];
-      dd[j] = ddt[j];
-    }
-    if (rg == 0) {
-      store_cols<DK>(gq + tt * DK, cl, sq);
-      store_cols<DK>(gk + tt * DK, cl, dk);
-    }
-    if (threadIdx.x == 0) {
-      gbeta[tt] = dbt;
-      gr[tt] = drt;
     }
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i)
-    store_cols<DK>(gS0 + ((size_t)bh * DV + rg + 16 * i) * DK, cl, ds[i]);
-  if (rg == 0) store_cols<DK>(gd0 + (size_t)bh * DK, cl, dd);
-  if (threadIdx.x == 0) geta[bh] = eta_acc;
+    store_cols<DK>(gS0 + ((size_t)bh * DV + row0 + kBwdRG * i) * DK, cl, ds[i]);
+}
+
+// The learner's adjoint, one workgroup of four waves per stream. Wave 0
+// walks the tokens backwards (lane l holds channels l + 64 m, m < LM; at
+// Dk = 32 the upper half of the wave holds zeros) while waves 1-3 stage the
+// next block of kLearnBlock tokens in LDS: the slices' shares added up, d_t,
+// the key, beta and r. One barrier per block.
+constexpr int kLearnBlock = 16;
+constexpr int kLearnThreads = 256;
+
+template <int DK, int DV, typename Tin>
+__global__ __launch_bounds__(kLearnThreads) void osdn_bwd_learner_kernel(
+    int T, const Tin* __restrict__ k, const float* __restrict__ beta,
+    const float* __restrict__ r, float eta, float scale, const float* __restrict__ ddT,
+    BwdBufs wb, float* __restrict__ gq, float* __restrict__ gk, float* __restrict__ gbeta,
+    float* __restrict__ gr, float* __restrict__ geta, float* __restrict__ gd0) {
+  constexpr int LM = DK >= 64 ? DK / 64 : 1, RS = DV / kBwdSliceRows, SW = share_width(DK);
+  constexpr int LB = kLearnBlock;
+  // staged token: shares [0, SW) (S_t^T do, dS^T u, S_{t-1}^T w, u.w),
+  // d_t [SW, SW + DK), key [SW + DK, SW + 2 DK), beta and r after them
+  constexpr int OD = SW, OK = SW + DK, OB = SW + 2 * DK, TW = SW + 2 * DK + 4;
+  static_assert(kLearnThreads - kWave >= LB, "a staging thread per token for beta and r");
+  // staging: 16-byte pieces per token of the shares (NSH, each the sum of
+  // RS slices), of d_t and of the key (ND each); one item type per loop, so
+  // that every lane of a loop issues the same loads
+  constexpr int NSH = SW / 4, ND = DK / 4;
+  constexpr int NL = kLearnThreads - kWave;            // staging threads
+  constexpr int NIS = (LB * NSH + NL - 1) / NL;        // share items per thread
+  constexpr int NIK = (LB * ND + NL - 1) / NL;         // d_t or key items per thread
+  __shared__ __attribute__((aligned(16))) float stg[2][LB][TW];
+  const int bh = blockIdx.x, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const float* Db = wb.d + (size_t)bh * T * DK;
+  const float* Sh = wb.sh + (size_t)bh * T * RS * SW;
+  const size_t tb = (size_t)bh * T;
+  const int nblk = (T + LB - 1) / LB;
+
+  // block b holds tokens T - 1 - b LB - i, i < LB (those below 0 are not
+  // staged); every load is unconditional, of a clamped item and token, and
+  // all are issued before the first LDS write
+  auto stage = [&](int b, int buf) {
+    const int st = tid - kWave;
+    auto tok = [&](int i) { return max(T - 1 - b * LB - i, 0); };
+    float4 vs[NIS][RS], vd[NIK], vk[NIK];
+    float2 vb = float2{0.f, 1.f};
+#pragma unroll
+    for (int u = 0; u < NIS; ++u) {
+      const int it = min(st + u * NL, LB * NSH - 1), i = it / NSH, e = it - i * NSH;
+      const float* sh = Sh + (size_t)tok(i) * RS * SW + 4 * e;
+#pragma unroll
+      for (int sl = 0; sl < RS; ++sl) vs[u][sl] = *reinterpret_cast<const float4*>(sh + sl * SW);
+    }
+#pragma unroll
+    for (int u = 0; u < NIK; ++u) {
+      const int it = min(st + u * NL, LB * ND - 1), i = it / ND, e = it - i * ND;
+      const size_t t = (size_t)tok(i);
+      vd[u] = *reinterpret_cast<const float4*>(Db + t * DK + 4 * e);
+      const Tin* kp = k + (tb + t) * DK + 4 * e;
+      vk[u] = float4{to_f32(kp[0]), to_f32(kp[1]), to_f32(kp[2]), to_f32(kp[3])};
+    }
+    {
+      const size_t t = (size_t)tok(min(st, LB - 1));
+      vb = float2{beta[tb + t], r ? r[tb + t] : 1.f};
+    }
+#pragma unroll
+    for (int u = 0; u < NIS; ++u) {
+      const int it = st + u * NL, i = it / NSH, e = it - i * NSH;
+      float4 a = vs[u][0];
+#pragma unroll
+      for (int sl = 1; sl < RS; ++sl) {
+        a.x += vs[u][sl].x;
+        a.y += vs[u][sl].y;
+        a.z += vs[u][sl].z;
+        a.w += vs[u][sl].w;
+      }
+      if (it < LB * NSH) *reinterpret_cast<float4*>(&stg[buf][i][4 * e]) = a;
+    }
+#pragma unroll
+    for (int u = 0; u < NIK; ++u) {
+      const int it = st + u * NL, i = it / ND, e = it - i * ND;
+      if (it < LB * ND) {
+        *reinterpret_cast<float4*>(&stg[buf][i][OD + 4 * e]) = vd[u];
+        *reinterpret_cast<float4*>(&stg[buf][i][OK + 4 * e]) = vk[u];
+      }
+    }
+    if (st < LB) *reinterpret_cast<float2*>(&stg[buf][st][OB]) = vb;
+  };
+
+  float dd[LM];
+#pragma unroll
+  for (int m = 0; m < LM; ++m) {
+    const int j = lane + 64 * m;
+    dd[m] = (ddT && j < DK) ? ddT[(size_t)bh * DK + j] : 0.f;
+  }
+  float eta_acc = 0.f;
+
+  auto compute = [&](int b, int buf) {
+#pragma unroll 4
+    for (int i = 0; i < LB; ++i) {
+      const int t = T - 1 - b * LB - i;
+      if (t < 0) break;
+      const size_t tt = tb + t;
+      const float* src = &stg[buf][i][0];
+      float kk[LM], dt[LM], sq[LM], su[LM], sy[LM];
+#pragma unroll
+      for (int m = 0; m < LM; ++m) {
+        // lanes past Dk read a valid channel and keep zeros
+        const int j0 = lane + 64 * m, j = j0 < DK ? j0 : j0 - DK;
+        const float live = j0 < DK ? 1.f : 0.f;
+        kk[m] = live * src[OK + j];
+        dt[m] = live * src[OD + j];
+        sq[m] = live * src[j];
+        su[m] = live * src[DK + j];
+        sy[m] = live * src[2 * DK + j];
+      }
+      const float uw = src[3 * DK], bt = src[OB], rt = src[OB + 1];
+
+      float n = 0.f, c = 0.f, pr = 0.f, pg = 0.f;
+      float a[LM], dk[LM], ddt[LM];
+#pragma unroll
+      for (int m = 0; m < LM; ++m) {
+        a[m] = kk[m] * kk[m];
+        n += a[m];
+        c += dt[m] * a[m];
+        // the write and the read of the memory: k~'s adjoint beta dS^T u,
+        // the read key's -beta S_{t-1}^T w
+        const float dkt = bt * su[m];
+        dk[m] = -bt * sy[m] + dkt * dt[m];
+        ddt[m] = dkt * kk[m] + rt * dd[m];
+        pr += dd[m] * dt[m];
+        pg += dd[m] * a[m];
+      }
+      n = wave_sum(n);
+      c = wave_sum(c);
+      const float drt = wave_sum(pr);
+      const float dg = wave_sum(pg);
+      // the learner's step g = eta beta (1 - beta c)/n, only where n > 0
+      // (no step, no gradient through it, at a zero key)
+      const float in = n > 0.f ? 1.f / n : 0.f;
+      const float h = (1.f - bt * c) * in;   // (1 - beta c)/n
+      const float g = eta * bt * h;
+      const float hg = h * dg;
+      const float dc = -eta * bt * bt * in * dg;
+      const float dn = -g * in * dg;
+      const float dbt = uw + eta * (1.f - 2.f * bt * c) * in * dg;
+      eta_acc += bt * hg;
+      float da[LM];
+#pragma unroll
+      for (int m = 0; m < LM; ++m) {
+        ddt[m] += dc * a[m];
+        da[m] = g * dd[m] + dc * dt[m] + dn;
+      }
+#pragma unroll
+      for (int m = 0; m < LM; ++m) {
+        const int j = lane + 64 * m;
+        dk[m] += 2.f * kk[m] * da[m];
+        dd[m] = ddt[m];
+        if (DK >= 64 || j < DK) {
+          gq[tt * DK + j] = scale * sq[m];
+          gk[tt * DK + j] = dk[m];
+        }
+      }
+      // (every lane holds the same sums; all store them, no branch)
+      gbeta[tt] = dbt;
+      gr[tt] = drt;
+    }
+  };
+
+  if (nblk > 0 && wave > 0) stage(0, 0);
+  __syncthreads();
+  for (int b = 0; b < nblk; ++b) {
+    if (wave > 0) {
+      if (b + 1 < nblk) stage(b + 1, (b + 1) & 1);
+    } else {
+      compute(b, b & 1);
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int m = 0; m < LM; ++m) {
+      const int j = lane + 64 * m;
+      if (j < DK) gd0[(size_t)bh * DK + j] = dd[m];
+    }
+    if (lane == 0) geta[bh] = eta_acc;
+  }
 }
 
 template <int DK, int DV, typename Tin>
 int launch_bwd_t(const BackwardArgs& a, hipStream_t s) {
+  constexpr int RS = DV / kBwdSliceRows;
   const int BH = a.B * a.H;
   const BwdBufs wb = bwd_bufs(a.ws, BH, a.T, DK, DV);
+  const int grid = bwd_grid(BH, RS);
   const int tk1 = ktimer_before(s, "osdn_bwd_record");
-  hipLaunchKernelGGL((osdn_bwd_record_kernel<DK, DV, Tin>), dim3(BH), dim3(kDecThreads), 0, s,
-                     a.T, (const Tin*)a.k, (const Tin*)a.v, a.beta, a.r, a.eta, a.d0, a.S0, wb);
+  hipLaunchKernelGGL((osdn_bwd_record_kernel<DK, DV, Tin>), dim3(grid), dim3(kBwdThreads), 0, s,
+                     BH, a.T, (const Tin*)a.k, (const Tin*)a.v, a.beta, a.r, a.eta, a.d0, a.S0,
+                     wb);
   ktimer_after(s, tk1);
   int rc = (int)hipGetLastError();
   if (rc) return rc;
   const int tk2 = ktimer_before(s, "osdn_bwd");
-  hipLaunchKernelGGL((osdn_bwd_kernel<DK, DV, Tin>), dim3(BH), dim3(kDecThreads), 0, s, a.T,
-                     (const Tin*)a.q, (const Tin*)a.k, a.beta, a.r, a.eta, a.scale,
-                     (const Tin*)a.dout, a.dST, a.ddT, wb, a.dq, a.dk, a.dv, a.dbeta, a.dr,
-                     a.deta, a.dd0, a.dS0);
+  hipLaunchKernelGGL((osdn_bwd_kernel<DK, DV, Tin>), dim3(grid), dim3(kBwdThreads), 0, s, BH,
+                     a.T, (const Tin*)a.q, (const Tin*)a.k, a.beta, a.scale,
+                     (const Tin*)a.dout, a.dST, wb, a.dv, a.dS0);
   ktimer_after(s, tk2);
+  rc = (int)hipGetLastError();
+  if (rc) return rc;
+  const int tk3 = ktimer_before(s, "osdn_bwd_learner");
+  hipLaunchKernelGGL((osdn_bwd_learner_kernel<DK, DV, Tin>), dim3(BH), dim3(kLearnThreads), 0, s,
+                     a.T,
+                     (const Tin*)a.k, a.beta, a.r, a.eta, a.scale, a.ddT, wb, a.dq, a.dk,
+                     a.dbeta, a.dr, a.deta, a.dd0);
+  ktimer_after(s, tk3);
   return (int)hipGetLastError();
 }
 

@@ -344,15 +344,19 @@ int gdn2_decode(int B, int H, int T, int Dk, int Dv, int dtype,
  *   dS0      [B,H,Dv,Dk] fp32 OUT         (required)
  *   workspace  device scratch of osdn_backward_workspace_bytes() bytes,
  *            256-byte aligned; caller-owned, contents on entry ignored:
- *            per token the residual v - S k and the preconditioner, and the
- *            state every 64 tokens and after the last
+ *            per token the residual v - S k and the preconditioner, the
+ *            state every 64 tokens and after the last, and per token and
+ *            32-row slice of the value channels that slice's sums over its
+ *            rows (3 Dk + 4 floats)
  * Where a key is all zero the learner takes no step (as in the forward) and
  * no gradient flows through its step size. Gradients are fp32 whatever the
  * input dtype (bf16 inputs are widened; the recurrence runs in fp32). No
  * output may overlap another output, an input or the workspace
- * (OSDN_ERR_ALIASING). Dk, Dv in {32, 64, 128}; B*H workgroups, each holding
- * one (batch, head) state and its adjoint in registers; two kernels (the
- * forward storing what the reverse needs, then the reverse walk).
+ * (OSDN_ERR_ALIASING). Dk, Dv in {32, 64, 128}. Three kernels: the forward
+ * storing what the reverse needs and the reverse walk, each over B*H*Dv/32
+ * workgroups (a 32-row slice of one (batch, head) state and its adjoint in
+ * registers), then one wave per (batch, head) adding the slices' sums and
+ * carrying the adjoint of the preconditioner.
  */
 size_t osdn_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
 int osdn_backward(int B, int H, int T, int Dk, int Dv, int dtype,
@@ -437,10 +441,9 @@ void osdn_kernel_timing(int enable);
  * precond_rho (phase 1), wy_prep, wy_prep_fused (phase 2 forming the
  * preconditioned keys itself), wy_scan (phase 2), gdn2_prep, gdn2_scan
  * (GDN-2), gated_prep, gated_prep_fused, gated_scan (OSDN on a decaying
- * backbone),
- * osdn_decode, gdn2_decode (recurrent decode), osdn_bwd_record, osdn_bwd
- * (backward), gated_bwd_record, gated_bwd, gdn2_bwd_record, gdn2_bwd
- * (gate-aware backward).
+ * backbone), osdn_decode, gdn2_decode (recurrent decode), osdn_bwd_record,
+ * osdn_bwd, osdn_bwd_learner (backward), gated_bwd_record, gated_bwd,
+ * gdn2_bwd_record, gdn2_bwd (gate-aware backward).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

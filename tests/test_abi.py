@@ -385,11 +385,14 @@ def test_backward_error_paths_and_workspace():
                                 + [P] * 8 + [P, Z, P])
     L.osdn_backward_workspace_bytes.argtypes = [I] * 5
     L.osdn_backward_workspace_bytes.restype = Z
-    # per token u (Dv) and d (Dk), a state every 64 tokens and after the last
+    # per token u (Dv) and d (Dk), a state every 64 tokens and after the
+    # last, and per token and 32-row value slice the slice's row sums
+    # (3 Dk + 1, padded to 3 Dk + 4)
     for B, H, T, Dk, Dv in ((1, 1, 1, 32, 32), (2, 3, 64, 64, 128),
                             (1, 2, 65, 128, 32), (2, 1, 0, 32, 64)):
         nck = (T + 63) // 64
-        want = B * H * (T * (Dk + Dv) + (nck + 1) * Dv * Dk) * 4
+        want = B * H * (T * (Dk + Dv) + (nck + 1) * Dv * Dk
+                        + T * (Dv // 32) * (3 * Dk + 4)) * 4
         assert L.osdn_backward_workspace_bytes(B, H, T, Dk, Dv) == want
     assert L.osdn_backward_workspace_bytes(1, 1, 8, 48, 32) == 0
     assert L.osdn_backward_workspace_bytes(-1, 1, 8, 32, 32) == 0
