@@ -52,13 +52,15 @@ _KERNEL_SOURCES = {
     "gated_scan": ["wy_chunk.hip"],
     "osdn_decode": ["decode.hip"],
     "gdn2_decode": ["decode.hip"],
-    "osdn_bwd_record": ["backward.hip", "row_state.hpp"],
-    "osdn_bwd": ["backward.hip", "row_state.hpp"],
-    "osdn_bwd_learner": ["backward.hip", "row_state.hpp"],
-    "gated_bwd_record": ["backward_gated.hip", "row_state.hpp"],
-    "gated_bwd": ["backward_gated.hip", "row_state.hpp"],
-    "gdn2_bwd_record": ["backward_gated.hip", "row_state.hpp"],
-    "gdn2_bwd": ["backward_gated.hip", "row_state.hpp"],
+    "osdn_bwd_record": ["backward.hip", "bwd_common.hpp", "row_state.hpp"],
+    "osdn_bwd": ["backward.hip", "bwd_common.hpp", "row_state.hpp"],
+    "osdn_bwd_learner": ["backward.hip", "bwd_common.hpp", "row_state.hpp"],
+    "gated_bwd_record": ["backward_gated.hip", "bwd_common.hpp", "row_state.hpp"],
+    "gated_bwd": ["backward_gated.hip", "bwd_common.hpp", "row_state.hpp"],
+    "gated_bwd_learner": ["backward_gated.hip", "bwd_common.hpp", "row_state.hpp"],
+    "gdn2_bwd_record": ["backward_gated.hip", "bwd_common.hpp", "row_state.hpp"],
+    "gdn2_bwd": ["backward_gated.hip", "bwd_common.hpp", "row_state.hpp"],
+    "gdn2_bwd_out": ["backward_gated.hip", "bwd_common.hpp", "row_state.hpp"],
 }
 PRECOND_CHUNK = 64  # phase-1 chunk length (fixed in the library)
 

@@ -378,9 +378,11 @@ int osdn_backward(int B, int H, int T, int Dk, int Dv, int dtype,
  *   dlog_alpha [B,H,T,Dk] fp32 OUT       its gradient (required)
  * workspace: osdn_gated_backward_workspace_bytes() bytes, 256-byte aligned,
  * caller-owned: per token the preconditioner, the state every 64 tokens and
- * after the last, and one interval of min(T, 64) states per (batch, head)
- * (the reverse pass recomputes each interval from its stored state rather
- * than undo the decay). Other rules as in osdn_backward.
+ * after the last, one interval of min(T, 64) states per (batch, head) (the
+ * reverse pass recomputes each interval from its stored state rather than
+ * undo the decay), and per token and 32-row slice of the value channels
+ * that slice's sums over its rows (4 Dk + 4 floats). Other rules as in
+ * osdn_backward.
  */
 size_t osdn_gated_backward_workspace_bytes(int B, int H, int T, int Dk, int Dv);
 int osdn_gated_backward(int B, int H, int T, int Dk, int Dv, int dtype,
@@ -407,8 +409,9 @@ int osdn_gated_backward(int B, int H, int T, int Dk, int Dv, int dtype,
  *   dv, dw   [B,H,T,Dv]  fp32 OUT         (required)
  *   dS0      [B,H,Dk,Dv] fp32 OUT         (required)
  *   workspace  gdn2_backward_workspace_bytes() bytes, 256-byte aligned,
- *            caller-owned: the state every 64 tokens and after the last, and
- *            one interval of min(T, 64) states per (batch, head)
+ *            caller-owned: the state every 64 tokens and after the last, one
+ *            interval of min(T, 64) states per (batch, head), and per token
+ *            and 32-row value slice that slice's row sums (4 Dk + 4 floats)
  * No output may overlap another output, an input or the workspace. Dk, Dv in
  * {32, 64, 128}; gradients fp32 whatever the input dtype.
  */
@@ -443,7 +446,8 @@ void osdn_kernel_timing(int enable);
  * (GDN-2), gated_prep, gated_prep_fused, gated_scan (OSDN on a decaying
  * backbone), osdn_decode, gdn2_decode (recurrent decode), osdn_bwd_record,
  * osdn_bwd, osdn_bwd_learner (backward), gated_bwd_record, gated_bwd,
- * gdn2_bwd_record, gdn2_bwd (gate-aware backward).
+ * gated_bwd_learner, gdn2_bwd_record, gdn2_bwd, gdn2_bwd_out (gate-aware
+ * backward).
  */
 int osdn_kernel_times(int max, const char** names, int* counts, float* mean_ms);
 

@@ -437,11 +437,13 @@ def test_gated_backward_error_paths_and_workspace(gdn2):
     wsq.argtypes = [I] * 5
     wsq.restype = Z
     # OSDN: per token d (Dk); both: a state every 64 tokens and after the
-    # last, and an interval of min(T, 64) states
+    # last, an interval of min(T, 64) states, and per token and 32-row value
+    # slice the slice's row sums (4 Dk + 4)
     for B, H, T, Dk, Dv in ((1, 1, 1, 32, 32), (2, 3, 64, 64, 128),
                             (1, 2, 130, 128, 32), (2, 1, 0, 32, 64)):
         nck = (T + 63) // 64
-        per = (0 if gdn2 else T * Dk) + (nck + 1 + min(T, 64)) * Dv * Dk
+        per = ((0 if gdn2 else T * Dk) + (nck + 1 + min(T, 64)) * Dv * Dk
+               + T * (Dv // 32) * (4 * Dk + 4))
         assert wsq(B, H, T, Dk, Dv) == B * H * per * 4
     assert wsq(1, 1, 8, 48, 32) == 0
     need = wsq(1, 1, 4, 32, 32)
