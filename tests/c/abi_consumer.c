@@ -109,6 +109,76 @@ int main(void) {
                     P(0x30000), P(0x60000), P(0x70000), P(0x80000), P(0x70000),
                     1.f, P(0x50000), NULL) == OSDN_ERR_ALIASING);
 
+  /* backward entry points: workspace layouts and host-side validation */
+  {
+    const int Bq = 2, Hq = 3, Tq = 130, K = 128, V = 64;
+    const size_t nck = (Tq + 63) / 64, rs = V / 32, st = Tq < 64 ? Tq : 64;
+    CHECK(osdn_backward_workspace_bytes(Bq, Hq, Tq, K, V) ==
+          (size_t)Bq * Hq *
+              ((size_t)Tq * (K + V) + (nck + 1) * V * K + (size_t)Tq * rs * (3 * K + 4)) *
+              4);
+    CHECK(gdn2_backward_workspace_bytes(Bq, Hq, Tq, K, V) ==
+          (size_t)Bq * Hq *
+              ((nck + 1 + st) * V * K + (size_t)Tq * rs * (4 * K + 4)) * 4);
+    CHECK(osdn_gated_backward_workspace_bytes(Bq, Hq, Tq, K, V) ==
+          gdn2_backward_workspace_bytes(Bq, Hq, Tq, K, V) + (size_t)Bq * Hq * Tq * K * 4);
+    CHECK(osdn_backward_workspace_bytes(Bq, Hq, Tq, 48, V) == 0);
+  }
+  {
+    const size_t need = osdn_backward_workspace_bytes(1, 1, 4, 32, 32);
+    /* dq over q */
+    CHECK(osdn_backward(1, 1, 4, 32, 32, OSDN_BF16, P(0x10000), P(0x20000),
+                        P(0x30000), P(0x40000), NULL, 0.1f, NULL, NULL, 1.f,
+                        P(0x60000), NULL, NULL, P(0x10000 + 8), P(0x200000),
+                        P(0x300000), P(0x400000), P(0x500000), P(0x600000),
+                        P(0x700000), P(0x900000), P(0x4000000), need,
+                        NULL) == OSDN_ERR_ALIASING);
+    /* missing dout */
+    CHECK(osdn_backward(1, 1, 4, 32, 32, OSDN_BF16, P(0x10000), P(0x20000),
+                        P(0x30000), P(0x40000), NULL, 0.1f, NULL, NULL, 1.f,
+                        NULL, NULL, NULL, P(0x100000), P(0x200000),
+                        P(0x300000), P(0x400000), P(0x500000), P(0x600000),
+                        P(0x700000), P(0x900000), P(0x4000000), need,
+                        NULL) == OSDN_ERR_NULL_ARG);
+    /* workspace too small */
+    CHECK(osdn_backward(1, 1, 4, 32, 32, OSDN_BF16, P(0x10000), P(0x20000),
+                        P(0x30000), P(0x40000), NULL, 0.1f, NULL, NULL, 1.f,
+                        P(0x60000), NULL, NULL, P(0x100000), P(0x200000),
+                        P(0x300000), P(0x400000), P(0x500000), P(0x600000),
+                        P(0x700000), P(0x900000), P(0x4000000), need - 4,
+                        NULL) == OSDN_ERR_WORKSPACE);
+    /* GDN-2: the decay's gradient over the decay */
+    const size_t ng = gdn2_backward_workspace_bytes(1, 1, 4, 32, 32);
+    CHECK(gdn2_backward(1, 1, 4, 32, 32, OSDN_BF16, P(0x10000), P(0x20000),
+                        P(0x30000), P(0x80000), P(0x90000), P(0x98000), NULL,
+                        1.f, P(0x60000), NULL, P(0x100000), P(0x200000),
+                        P(0x300000), P(0x80000), P(0x400000), P(0x500000),
+                        P(0x900000), P(0x4000000), ng, NULL) == OSDN_ERR_ALIASING);
+    /* gated OSDN: unsupported head dim */
+    CHECK(osdn_gated_backward(1, 1, 4, 16, 32, OSDN_BF16, P(0x10000),
+                              P(0x20000), P(0x30000), P(0x40000), NULL, 0.1f,
+                              P(0x80000), NULL, NULL, 1.f, P(0x60000), NULL,
+                              NULL, P(0x100000), P(0x200000), P(0x300000),
+                              P(0x400000), P(0x500000), P(0x600000),
+                              P(0xa00000), P(0x700000), P(0x900000),
+                              P(0x4000000), 1u << 20, NULL) == OSDN_ERR_UNSUPPORTED);
+  }
+
+  /* the allocation-free forward rejects sizes beyond its static scratch on
+   * the host, before touching any device */
+  CHECK(osdn_forward_noalloc(64, 16, 8192, 128, 128, 64, OSDN_BF16, P(0x10000),
+                             P(0x20000), P(0x30000), P(0x40000), NULL, 0.1f,
+                             NULL, NULL, 1.f, P(0x50000), NULL, NULL, NULL,
+                             NULL, NULL) == OSDN_ERR_WORKSPACE);
+  CHECK(osdn_forward_noalloc(0, 16, 64, 128, 128, 64, OSDN_BF16, NULL, NULL,
+                             NULL, NULL, NULL, 0.1f, NULL, NULL, 1.f, NULL,
+                             NULL, NULL, NULL, NULL, NULL) == OSDN_OK);
+
+  /* kernel timing: enabling and reading with nothing recorded */
+  osdn_kernel_timing(1);
+  CHECK(osdn_kernel_times(0, NULL, NULL, NULL) == 0);
+  osdn_kernel_timing(0);
+
   if (failures == 0) printf("abi_consumer: all checks passed\n");
   return failures;
 }
