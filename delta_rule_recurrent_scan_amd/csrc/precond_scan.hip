@@ -55,8 +55,14 @@ struct P1Cfg {
   static constexpr int LDH = DK + 8;
   static constexpr int LDF = C + 4;
   static constexpr int LDYS = 16 + 4;
+  // shared Y of the widest doubling level (C/2 x C/2), rows 16 banks apart
+  // for the k-major reads
+  static constexpr int LDY = C / 2 + 16;
+  static constexpr size_t uY = (size_t)NW * (C / 2) * LDYS * 4 > (size_t)(C / 2) * LDY * 4
+                                   ? (size_t)NW * (C / 2) * LDYS * 4
+                                   : (size_t)(C / 2) * LDY * 4;
   static constexpr size_t uSplit = (size_t)2 * C * LDH * 2;
-  static constexpr size_t uT = (size_t)C * LDF * 4 + (size_t)NW * (C / 2) * LDYS * 4;
+  static constexpr size_t uT = (size_t)C * LDF * 4 + uY;
   static constexpr size_t pAh = 0, pAl = (size_t)C * LDH * 2;
   static constexpr size_t pT = 0, pY = (size_t)C * LDF * 4;
   static constexpr size_t pM = uSplit > uT ? uSplit : uT;
@@ -176,25 +182,24 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
       rho[t] = e * bt;
       hv[t] = e * bt * expf(lpv[t]);
     }
-    // Tile list: wave w owns the diagonal tile (w, w) and a share of the
-    // off-diagonal lower tiles, and keeps its accumulators in registers.
-    constexpr int NL = TB * (TB + 1) / 2;
-    constexpr int NJ = 1 + (NL - TB + G::NW - 1) / G::NW;
+    // Gram tiles (row block a >= column block b), dealt so that wave w < 2
+    // owns those of diagonal pair w, (2w, 2w), (2w+1, 2w+1) and (2w+1, 2w),
+    // and can invert the pair by itself; waves 2 and 3 own (w, 0) and (w, 1),
+    // the tiles the second doubling level reads. Accumulators stay in
+    // registers.
+    static_assert(TB == 4 && G::NW == 4, "four 16-token blocks, four waves");
+    constexpr int NJ = 3;
     f32x4 gacc[NJ];
     int gja[NJ], gjb[NJ];
 #pragma unroll
     for (int s2 = 0; s2 < NJ; ++s2) {
       int a = -1, b = -1;
-      const int job = wave + G::NW * s2;
-      if (s2 == 0) {
-        if (wave < TB) { a = wave; b = wave; }
-      } else {
-        // off-diagonal tiles in row-major order, dealt round-robin
-        int l = job - G::NW, aa = 1;
-        if (l >= 0) {
-          while (l >= aa) { l -= aa; ++aa; }
-          if (aa < TB) { a = aa; b = l; }
-        }
+      if (wave < 2) {
+        a = 2 * wave + (s2 >= 1);
+        b = 2 * wave + (s2 == 1);
+      } else if (s2 < 2) {
+        a = wave;
+        b = s2;
       }
       gja[s2] = a;
       gjb[s2] = b;
@@ -235,96 +240,128 @@ __global__ __launch_bounds__(256) void precond_prep_kernel(
         *reinterpret_cast<float4*>(Tf + rr * LDF + cc) = float4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- diagonal 16x16 blocks of T = (I + M)^-1 ----------------------------
-    // Wave b wrote diagonal tile (b, b) of M itself; lane c < 16 owns column c.
-    if (wave < TB) {
+    if (wave < 2) {
+      // ---- diagonal pair `wave` of T = (I + M)^-1, by this wave alone -------
+      // 16x16 diagonal blocks by forward substitution: lanes 0-15 take block
+      // 2w, lanes 16-31 block 2w + 1, lane c % 16 owns column c % 16.
       wave_lds_sync();
-      if (lane < 16) {
-        const int b = wave, c = lane;
+      if (lane < 32) {
+        const int b = 2 * wave + (lane >> 4), c = lane & 15;
         const float* Mblk = Mf + b * 16 * LDF + b * 16;
-        float x[16], s[16];
+        float x[16], sv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = (i == c) ? 1.f : 0.f;
+        for (int i = 0; i < 16; ++i) sv[i] = (i == c) ? 1.f : 0.f;
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-          x[m] = s[m];
+          x[m] = sv[m];
 #pragma unroll
-          for (int i = m + 1; i < 16; ++i) s[i] -= Mblk[i * LDF + m] * x[m];
+          for (int i = m + 1; i < 16; ++i) sv[i] -= Mblk[i * LDF + m] * x[m];
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) Tf[(b * 16 + i) * LDF + b * 16 + c] = x[i];
       }
+      wave_lds_sync();
+      // first doubling level, T21 = -T22 (M21 T11) for the pair: Y to the
+      // wave's own scratch, then T21; right operands read k-major, tiles
+      // formed transposed (a lane writes four consecutive columns of a row)
+      const int rb = 32 * wave + 16, cb = 32 * wave;
+      float* ys = Ysc + wave * 16 * LDYS;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      {
+        Frag<16, float> fa, fb;
+        fa.load(Mf + rb * LDF + cb, LDF);
+        fb.load_kmajor(Tf + cb * LDF + cb, LDF);
+        mma(acc, fb, fa);
+      }
+      *reinterpret_cast<float4*>(ys + acc_col() * LDYS + acc_row(0)) =
+          float4{acc[0], acc[1], acc[2], acc[3]};
+      wave_lds_sync();
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        Frag<16, float> fa, fb;
+        fa.load(Tf + rb * LDF + rb, LDF);
+        fb.load_kmajor(ys, LDYS);
+        mma(acc, fb, fa);
+      }
+      *reinterpret_cast<float4*>(Tf + (rb + acc_col()) * LDF + cb + acc_row(0)) =
+          float4{-acc[0], -acc[1], -acc[2], -acc[3]};
+    } else {
+      // record: the gate prefix, the ratios P_C / P_{t+1} and P_C
+      const int u = tid - 128;
+      for (int e = u; e <= C; e += 128) out[G::R_LP + e] = lpv[e];
+      if (u < C) out[G::R_CF + u] = expf(lpv[C] - lpv[u + 1]);
+      if (u == 0) out[G::R_PC] = expf(lpv[C]);
     }
     __syncthreads();
 
-    // ---- recursive doubling in fp32, T21 = -T22 (M21 T11) --------------------
-    // One job = one 16-wide column of T21 in one pair: that column of
-    // Y = M21 T11 goes to the wave's own scratch, then the same column of
-    // T21 = -T22 Y; the right operands are read k-major.
+    // ---- second doubling level: T21 = -T22 Y, Y = M21 T11 (32 x 32) ---------
+    // One 16x16 tile of Y per wave; beside it, the record rows t < 32, which
+    // the first level completed: g0 = T e and V = T diag(h) (V's blocks above
+    // the block diagonal are zero and the chain never reads them, so they are
+    // not written).
+    constexpr int LDY = G::LDY;
+    float* Ysh = Ysc;
     {
-      float* ys = Ysc + wave * (C / 2) * LDYS;
+      const int rt = wave >> 1, c = wave & 1;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 16; s < C; s *= 2) {
-        const int nt = s / 16, jobs = (C / (2 * s)) * nt;
-        for (int job = wave; job < jobs; job += G::NW) {
-          const int pp = job / nt, c = job % nt;
-          const int rb = 2 * s * pp + s, cb = 2 * s * pp;
-          for (int rt = 0; rt < nt; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < s; kk += 16) {
-              Frag<16, float> fa, fb;
-              fa.load(Mf + (rb + rt * 16) * LDF + cb + kk, LDF);
-              fb.load_kmajor(Tf + (cb + kk) * LDF + cb + c * 16, LDF);
-              mma(acc, fb, fa);  // transposed: four consecutive columns per lane
-            }
-            *reinterpret_cast<float4*>(ys + (rt * 16 + acc_col()) * LDYS + acc_row(0)) =
-                float4{acc[0], acc[1], acc[2], acc[3]};
-          }
-          wave_lds_sync();
-          for (int rt = 0; rt < nt; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < s; kk += 16) {
-              Frag<16, float> fa, fb;
-              fa.load(Tf + (rb + rt * 16) * LDF + rb + kk, LDF);
-              fb.load_kmajor(ys + kk * LDYS, LDYS);
-              mma(acc, fb, fa);
-            }
-            *reinterpret_cast<float4*>(Tf + (rb + rt * 16 + acc_col()) * LDF + cb + c * 16 +
-                                       acc_row(0)) =
-                float4{-acc[0], -acc[1], -acc[2], -acc[3]};
-          }
-          wave_lds_sync();  // the scratch is rewritten by this wave's next job
-        }
-        __syncthreads();
+      for (int kk = 0; kk < 32; kk += 16) {
+        Frag<16, float> fa, fb;
+        fa.load(Mf + (32 + rt * 16) * LDF + kk, LDF);
+        fb.load_kmajor(Tf + kk * LDF + c * 16, LDF);
+        mma(acc, fb, fa);
       }
+      *reinterpret_cast<float4*>(Ysh + (rt * 16 + acc_col()) * LDY + c * 16 + acc_row(0)) =
+          float4{acc[0], acc[1], acc[2], acc[3]};
     }
-
-    // ---- chunk record: lp, g0 = T e, V = T diag(h), gate ratios -------------
-    for (int e = tid; e <= C; e += G::NT) out[G::R_LP + e] = lpv[e];
-    for (int e = tid; e < C; e += G::NT) out[G::R_CF + e] = expf(lpv[C] - lpv[e + 1]);
-    if (tid == 0) out[G::R_PC] = expf(lpv[C]);
     {
-      // four threads per row, one 16-wide block each (zero above the diagonal)
-      const int t = tid >> 2, q = tid & 3;
-      float s = 0.f;
-      if (q <= (t >> 4)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += Tf[t * LDF + 16 * q + i] * ev[16 * q + i];
-      }
-      s = group_sum<4>(s);
-      if (q == 0) out[G::R_G + t] = s;
-    }
-    for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
-      const int t = e4 / (C / 4), c0 = (e4 % (C / 4)) * 4;
-      float4 v = {0.f, 0.f, 0.f, 0.f};
+      const int t = tid >> 3, q = tid & 7, c0 = 4 * q;
+      float sg = 0.f;
       if ((c0 >> 4) <= (t >> 4)) {
-        const float* tr = Tf + t * LDF + c0;
-        v.x = tr[0] * hv[c0];
-        v.y = tr[1] * hv[c0 + 1];
-        v.z = tr[2] * hv[c0 + 2];
-        v.w = tr[3] * hv[c0 + 3];
+        const float4 tr = *reinterpret_cast<const float4*>(Tf + t * LDF + c0);
+        const float4 h4 = *reinterpret_cast<const float4*>(hv + c0);
+        *reinterpret_cast<float4*>(out + G::R_V + t * C + c0) =
+            float4{tr.x * h4.x, tr.y * h4.y, tr.z * h4.z, tr.w * h4.w};
+        const float4 e4 = *reinterpret_cast<const float4*>(ev + c0);
+        sg = tr.x * e4.x + tr.y * e4.y + tr.z * e4.z + tr.w * e4.w;
       }
-      *reinterpret_cast<float4*>(out + G::R_V + t * C + c0) = v;
+      sg = group_sum<8>(sg);
+      if (q == 0) out[G::R_G + t] = sg;
+    }
+    __syncthreads();
+    {
+      const int rt = wave >> 1, c = wave & 1;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 32; kk += 16) {
+        Frag<16, float> fa, fb;
+        fa.load(Tf + (32 + rt * 16) * LDF + 32 + kk, LDF);
+        fb.load_kmajor(Ysh + kk * LDY + c * 16, LDY);
+        mma(acc, fb, fa);
+      }
+      *reinterpret_cast<float4*>(Tf + (32 + rt * 16 + acc_col()) * LDF + c * 16 + acc_row(0)) =
+          float4{-acc[0], -acc[1], -acc[2], -acc[3]};
+    }
+    __syncthreads();
+
+    // ---- record rows t >= 32: g0 = T e, V = T diag(h) ------------------------
+    {
+      const int t = 32 + (tid >> 3), q = tid & 7;
+      float sg = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c0 = 8 * q + 4 * h;
+        if ((c0 >> 4) <= (t >> 4)) {
+          const float4 tr = *reinterpret_cast<const float4*>(Tf + t * LDF + c0);
+          const float4 h4 = *reinterpret_cast<const float4*>(hv + c0);
+          *reinterpret_cast<float4*>(out + G::R_V + t * C + c0) =
+              float4{tr.x * h4.x, tr.y * h4.y, tr.z * h4.z, tr.w * h4.w};
+          const float4 e4 = *reinterpret_cast<const float4*>(ev + c0);
+          sg += tr.x * e4.x + tr.y * e4.y + tr.z * e4.z + tr.w * e4.w;
+        }
+      }
+      sg = group_sum<8>(sg);
+      if (q == 0) out[G::R_G + t] = sg;
     }
     __syncthreads();  // the next chunk's split squares overwrite T
   }
