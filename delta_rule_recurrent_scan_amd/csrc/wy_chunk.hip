@@ -80,6 +80,29 @@ struct alignas(4 * sizeof(Tin)) RawQuad {
   Tin v[4];
 };
 
+// Two consecutive key channels of one token as one LDS access, unpacked to
+// fp32 and packed back (bf16: round to nearest even).
+template <typename Tin>
+struct KeyPairOf;
+template <>
+struct KeyPairOf<__bf16> {
+  using T = unsigned;
+  __device__ static float lo(T p) { return __uint_as_float(p << 16); }
+  __device__ static float hi(T p) { return __uint_as_float(p & 0xffff0000u); }
+  __device__ static T pack(float a, float b) {
+    const __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (unsigned)__builtin_bit_cast(unsigned short, x) |
+           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+  }
+};
+template <>
+struct KeyPairOf<float> {
+  using T = float2;
+  __device__ static float lo(T p) { return p.x; }
+  __device__ static float hi(T p) { return p.y; }
+  __device__ static T pack(float a, float b) { return float2{a, b}; }
+};
+
 // Per-chunk operands in the workspace, each [B*H*nchunks][...] in the
 // storage dtype: Wk as 16-row A fragments (row block tb at tb*16*Dk); the
 // scores P as 16-row A fragments (row block tb at tb*16*C) and X' as k-major
@@ -256,14 +279,20 @@ struct PrepCfg {
   static constexpr size_t oA = oTb + (size_t)C * LDC * E;
   static constexpr size_t oYs = oA + (size_t)TB * 16 * LDD * 4;
   static constexpr size_t oG = oYs + (size_t)NW * (C / 2) * LDS16 * E;
-  // fused OSDN only: squares of the keys, gate prefix (C + 4), step sizes,
-  // entry d, gate products P_t
-  static constexpr size_t oAs = oG + (size_t)DK * 4;
-  static constexpr size_t oLp = oAs + (kFused ? (size_t)C * LDK * E : 0);
-  static constexpr size_t oGs = oLp + (kFused ? (size_t)(C + 4) * 4 : 0);
+  // fused OSDN only: K~ comes from the preconditioner's recursion over NSEG
+  // segments of the chunk (one lane per segment and key channel pair): the
+  // segments' end values [NSEG][DK], step sizes g_t, entry d, gate factors
+  // r_t = P_{t+1} / P_t and P_t / P_s (s the first token of t's segment)
+  static constexpr int NSEG = kFused ? NW * (128 / DK) : 1;
+  static constexpr int SEGL = C / NSEG > 0 ? C / NSEG : 1;
+  static constexpr size_t oFe = oG + (size_t)DK * 4;
+  static constexpr size_t oGs = oFe + (kFused ? (size_t)NSEG * DK * 4 : 0);
   static constexpr size_t oDs = oGs + (kFused ? (size_t)C * 4 : 0);
-  static constexpr size_t oPv = oDs + (kFused ? (size_t)DK * 4 : 0);
-  static constexpr size_t oEnd = oPv + (kFused ? (size_t)C * 4 : 0);
+  static constexpr size_t oRt = oDs + (kFused ? (size_t)DK * 4 : 0);
+  static constexpr size_t oRa = oRt + (kFused ? (size_t)C * 4 : 0);
+  static constexpr size_t oEnd = oRa + (kFused ? (size_t)C * 4 : 0);
+  static_assert(!kFused || C != kPrecondChunk || (128 % DK == 0 && C % NSEG == 0),
+                "whole segments, one lane per segment and channel pair");
   // GDN-2 only: log alpha staged as fp32 rows, in a region of its own when
   // that fits, else over the Gram/inverse buffers (not in use yet during the
   // decay pass), whose zero blocks above the diagonal are then restored
@@ -273,8 +302,7 @@ struct PrepCfg {
   static constexpr bool kLaInGram = !kLaOwn && oAb + kLaBytes <= oG;
   static constexpr size_t oLa = kLaOwn ? oEnd : oAb;
   static constexpr size_t bytes = kLaOwn ? oEnd + kLaBytes : oEnd;
-  // (the fused decay variant forms L in the Gram buffer before its decay
-  // pass, so its log alpha needs a region of its own)
+  // (the fused decay variant keeps its log alpha in a region of its own)
   static constexpr bool fits =
       bytes <= 163840 && (kLaOwn || (kLaInGram && !(kFused && kDecayVariant<V>)));
   // GDN-2 decay pass: TPC threads per key channel, each over TPT tokens
@@ -306,7 +334,7 @@ struct PrepRegs {
   static constexpr int NLA = (C * DK / 4 + G::NT - 1) / G::NT;
   static constexpr bool kDecay = kDecayVariant<V>;
   uint4 la4[kDecay ? NLA : 1];     // decay variants: log alpha, 4 channels per load
-  float plp, pg, pd;               // fused OSDN: record entries, entry d
+  float plp, plp1, plps, pg, pd;   // fused OSDN: record entries, entry d
   int vrows;                       // valid rows of the fetched chunk
 
   // Loads are unconditional (rows past the sequence end read the last valid
@@ -332,8 +360,11 @@ struct PrepRegs {
     if constexpr (kFused) {
       // the phase-1 chunk of this engine chunk has the same index
       const float* rc = p.prec + (size_t)n * kRecStride;
-      plp = rc[kRecLp + min(tid, C)];
-      pg = rc[kRecG + min(tid, C - 1)];
+      const int tt = min(tid, C - 1);
+      plp = rc[kRecLp + tt];
+      plp1 = rc[kRecLp + tt + 1];
+      plps = rc[kRecLp + (tt / G::SEGL) * G::SEGL];
+      pg = rc[kRecG + tt];
       pd = p.pdent[(size_t)n * DK + min(tid, DK - 1)];
     }
 #pragma unroll
@@ -359,7 +390,7 @@ struct PrepRegs {
 
   // OSDN: Y = beta*k, X = k~, Q = q, Z = beta*v. GDN-2: raw k, b, q and
   // Z = w*v (the decay pass forms X, Y and Q in place). Fused OSDN: X = raw
-  // k (turned into K~ in place), the squares of k, and the record entries.
+  // k (turned into K~ in place) and the record entries.
   __device__ __forceinline__ void store(Tin* Ys, Tin* Xs, Tin* Qs, Tin* Zs,
                                         unsigned char* smem) const {
     const int tid = threadIdx.x;
@@ -382,14 +413,6 @@ struct PrepRegs {
           *reinterpret_cast<uint4*>(Ys + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(y);
           if constexpr (kFused) {
             *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = kk;
-            Tin a[VEC];
-#pragma unroll
-            for (int u = 0; u < VEC; ++u) {
-              const float xk = to_f32(kv[u]);
-              a[u] = from_f32<Tin>(xk * xk);
-            }
-            Tin* As = reinterpret_cast<Tin*>(smem + G::oAs);
-            *reinterpret_cast<uint4*>(As + rr * G::LDK + cc) = *reinterpret_cast<const uint4*>(a);
           } else {
             *reinterpret_cast<uint4*>(Xs + rr * G::LDK + cc) = keep_or_zero(x[i], live);
           }
@@ -408,11 +431,15 @@ struct PrepRegs {
       }
     }
     if constexpr (kFused) {
-      float* lps = reinterpret_cast<float*>(smem + G::oLp);
       float* gs = reinterpret_cast<float*>(smem + G::oGs);
       float* ds = reinterpret_cast<float*>(smem + G::oDs);
-      if (tid <= C) lps[tid] = plp;
-      if (tid < C) gs[tid] = pg;
+      float* rts = reinterpret_cast<float*>(smem + G::oRt);
+      float* ras = reinterpret_cast<float*>(smem + G::oRa);
+      if (tid < C) {
+        gs[tid] = pg;
+        rts[tid] = __expf(plp1 - plp);  // r_t = P_{t+1} / P_t
+        ras[tid] = __expf(plp - plps);  // P_t / P_s <= 1
+      }
       if (tid < DK) ds[tid] = pd;
     }
 #pragma unroll
@@ -634,47 +661,56 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     if constexpr (kDecay && !kFused) decay_pass();
     __syncthreads();
     if constexpr (kFused) {
-      // ---- K~ = (P d^T + L A) * K in place over the raw keys --------------
-      const float* lps = reinterpret_cast<const float*>(smem + G::oLp);
+      // ---- K~ = d_t * k_t in place over the raw keys --------------------------
+      // Inside the chunk the preconditioner follows its own recursion,
+      // d_{t+1} = r_t d_t + g_t a_t (a_t = k_t * k_t), from the entry value.
+      // One lane per (segment, channel pair): (A) the recursion over the
+      // segment from zero, F_{t+1} = r_t F_t + g_t a_t, keeping F_t and k_t
+      // of each token; (B) after a barrier, the segment's entry value from
+      // those before it, d_s' = (P_s' / P_s) d_s + F_end(s) (factors <= 1),
+      // then d_t = (P_t / P_s) d_s + F_t and K~_t = d_t * k_t.
+      constexpr int NPR = DK / 2, SEGL = G::SEGL, NSEG = G::NSEG;
+      using KP = KeyPairOf<Tin>;
       const float* gs = reinterpret_cast<const float*>(smem + G::oGs);
       const float* ds = reinterpret_cast<const float*>(smem + G::oDs);
-      float* Pv = reinterpret_cast<float*>(smem + G::oPv);
-      const Tin* As = reinterpret_cast<const Tin*>(smem + G::oAs);
-      Tin* Lb = Ab;  // L lives in the Gram buffer until the Gram step
-      // four consecutive entries of a row per thread and access
-      for (int e4 = tid; e4 < C * C / 4; e4 += G::NT) {
-        const int t = e4 / (C / 4), i0 = (e4 % (C / 4)) * 4;
-        Tin lv[4];
+      const float* rts = reinterpret_cast<const float*>(smem + G::oRt);
+      const float* ras = reinterpret_cast<const float*>(smem + G::oRa);
+      float* fe = reinterpret_cast<float*>(smem + G::oFe);
+      const int pr = lane % NPR, seg = wave * (64 / NPR) + lane / NPR;
+      const int s0 = seg * SEGL;
+      typename KP::T kp[SEGL];
+      float f0[SEGL], f1[SEGL];
+      float F0 = 0.f, F1 = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u;
-          lv[u] = from_f32<Tin>(i < t ? __expf(lps[t] - lps[i + 1]) * gs[i] : 0.f);
-        }
-        *reinterpret_cast<RawQuad<Tin>*>(Lb + t * LDC + i0) =
-            *reinterpret_cast<const RawQuad<Tin>*>(lv);
+      for (int m = 0; m < SEGL; ++m) {
+        const int t = s0 + m;
+        kp[m] = *reinterpret_cast<const typename KP::T*>(Xs + t * LDK + 2 * pr);
+        const float x0 = KP::lo(kp[m]), x1 = KP::hi(kp[m]);
+        f0[m] = F0;
+        f1[m] = F1;
+        const float r = rts[t], g = gs[t];
+        F0 = fmaf(r, F0, g * (x0 * x0));
+        F1 = fmaf(r, F1, g * (x1 * x1));
       }
-      if (tid < C) Pv[tid] = expf(lps[tid]);
+      *reinterpret_cast<float2*>(fe + seg * DK + 2 * pr) = float2{F0, F1};
       __syncthreads();
-      // one job = (16-token block tb, 16-channel block db), db-major so a
-      // wave keeps its squares fragment. The tile is formed transposed,
-      // (L A)^T = A^T L^T, so that a lane holds four consecutive channels of
-      // one token: its keys are read and K~ written 8 bytes at a time.
-      for (int job = wave; job < TB * DB; job += NW) {
-        const int db = job % DB, tb = job / DB;
-        Frag<C, Tin> fl, fa;
-        fl.load(Lb + tb * 16 * LDC, LDC);
-        fa.load_kmajor(As + db * 16, LDK);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        mma(acc, fa, fl);
-        const int t = tb * 16 + acc_col(), c0 = db * 16 + acc_row(0);
-        Tin* xe = Xs + t * LDK + c0;
-        Tin kk[4];
-        *reinterpret_cast<RawQuad<Tin>*>(kk) = *reinterpret_cast<const RawQuad<Tin>*>(xe);
-        const float pt = Pv[t];
+      float2 d = *reinterpret_cast<const float2*>(ds + 2 * pr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          kk[i] = from_f32<Tin>((pt * ds[c0 + i] + acc[i]) * to_f32(kk[i]));
-        *reinterpret_cast<RawQuad<Tin>*>(xe) = *reinterpret_cast<const RawQuad<Tin>*>(kk);
+      for (int v = 0; v + 1 < NSEG; ++v) {
+        if (v < seg) {
+          const int e1 = (v + 1) * SEGL - 1;  // last token of segment v
+          const float rho = ras[e1] * rts[e1];
+          const float2 fv = *reinterpret_cast<const float2*>(fe + v * DK + 2 * pr);
+          d.x = fmaf(rho, d.x, fv.x);
+          d.y = fmaf(rho, d.y, fv.y);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < SEGL; ++m) {
+        const int t = s0 + m;
+        const float ra = ras[t];
+        *reinterpret_cast<typename KP::T*>(Xs + t * LDK + 2 * pr) =
+            KP::pack(fmaf(ra, d.x, f0[m]) * KP::lo(kp[m]), fmaf(ra, d.y, f1[m]) * KP::hi(kp[m]));
       }
       __syncthreads();
       if constexpr (kDecay) {

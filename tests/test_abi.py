@@ -298,7 +298,7 @@ def _layout_bytes(L, B, H, T, Dk, Dv, C, dt, gated):
     p1 = L.osdn_precond_workspace_bytes(B, H, T, Dk, dt)
     if gated:
         p2 = L.gdn2_forward_workspace_bytes(B, H, T, Dk, Dv, C, dt)
-        fused = C == 64 and (dt == 1 or Dk == 32 or (Dk == 64 and Dv == 32))
+        fused = C == 64 and (dt == 1 or Dk == 32 or (Dk == 64 and Dv <= 64))
     else:
         p2 = L.osdn_chunk_workspace_bytes(B, H, T, Dk, Dv, C, dt)
         fused = C == 64

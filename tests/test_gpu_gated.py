@@ -66,6 +66,7 @@ SMALL = [
     BASE.scaled(B=1, H=2, T=90, Dk=128, Dv=64, apf=False),
     BASE.scaled(B=1, H=2, T=70, Dk=64, Dv=32, chunk=16, dtype="f32"),
     BASE.scaled(B=1, H=2, T=140, Dk=32, Dv=32, chunk=64, dtype="f32"),
+    BASE.scaled(B=1, H=2, T=150, Dk=64, Dv=64, chunk=64, dtype="f32"),
     BASE.scaled(B=1, H=2, T=130, Dk=32, Dv=64, chunk=64),
     BASE.scaled(B=2, H=1, T=64, chunk=64),
     BASE.scaled(B=1, H=1, T=1, chunk=64),

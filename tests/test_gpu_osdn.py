@@ -275,7 +275,7 @@ def test_parity_full_size_all_streams(name):
 
 
 @pytest.mark.parametrize("dk,dv", [(32, 32), (32, 64), (32, 128), (64, 32),
-                                   (64, 64)])
+                                   (64, 64), (64, 128)])
 def test_fp32_chunk64(dk, dv):
     """The fp32 OSDN forward at chunk 64 (phase 2 forms K~ from the phase-1
     records) for every (Dk, Dv) it supports, with and without the forgetting
