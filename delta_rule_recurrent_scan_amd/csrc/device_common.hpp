@@ -175,6 +175,21 @@ struct Frag<KEXT, __bf16> {
                                : base + N32 * 512 + lane * 4;
     d[i] = (__bf16)a;
   }
+  // Accumulator tile formed transposed over this fragment's 16 rows (lane
+  // l holds row l % 16, k = 16 cb + 4 (l / 16) + {0..3}), rounded and stored
+  // straight into the layout of store_global: the four values are one
+  // contiguous half of a lane's 16-byte slot.
+  __device__ __forceinline__ static void store_acc_kblock(__bf16* base, int cb,
+                                                          const f32x4& a) {
+    bf16x4 h;
+    h[0] = (__bf16)a[0]; h[1] = (__bf16)a[1]; h[2] = (__bf16)a[2]; h[3] = (__bf16)a[3];
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    __bf16* d = (cb >> 1) < N32
+                    ? base + (((cb >> 1) * 64 + ((cb & 1) * 2 + (g >> 1)) * 16 + r) * 8 +
+                              4 * (g & 1))
+                    : base + N32 * 512 + (g * 16 + r) * 4;
+    *reinterpret_cast<bf16x4*>(d) = h;
+  }
   __device__ __forceinline__ void store_global(__bf16* base) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -239,6 +254,14 @@ struct Frag<KEXT, float> {
   }
   __device__ __forceinline__ static void store_acc_elem(float* base, int b, int i, float a) {
     base[(4 * b + i) * 64 + (threadIdx.x & 63)] = a;
+  }
+  // As the bf16 fragment's: the accumulator tile over the fragment's 16
+  // rows at 16-wide k block cb, into the layout of store_global.
+  __device__ __forceinline__ static void store_acc_kblock(float* base, int cb,
+                                                          const f32x4& a) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) base[(4 * cb + g) * 64 + i * 16 + r] = a[i];
   }
   __device__ __forceinline__ void store_global(float* base) const {
     const int lane = threadIdx.x & 63;

@@ -478,10 +478,10 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDS16 = G::LDS16,
                 TB = G::TB, DB = G::DB, VBT = G::VBT, NW = G::NW;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::bytes];
-  Tin* Ys = reinterpret_cast<Tin*>(smem + G::oY);   // diag(rs) Y, then Wk
+  Tin* Ys = reinterpret_cast<Tin*>(smem + G::oY);   // diag(rs) Y
   Tin* Xs = reinterpret_cast<Tin*>(smem + G::oX);
   Tin* Qs = reinterpret_cast<Tin*>(smem + G::oQ);   // Q (GDN-2: Q^ = gamma q)
-  Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);   // diag(rs) Z, then U
+  Tin* Zs = reinterpret_cast<Tin*>(smem + G::oZ);   // diag(rs) Z
   Tin* Ab = reinterpret_cast<Tin*>(smem + G::oAb);
   Tin* Tb = reinterpret_cast<Tin*>(smem + G::oTb);
   float* Am = reinterpret_cast<float*>(smem + G::oA);
@@ -932,12 +932,12 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     }
 
     // ---- Wk = T diag(rs) Y and U = T diag(rs) Z --------------------------------
-    // One job = one 16-wide column block of Y (or Z), all row blocks. Wk
-    // overwrites Y in place (only the job's own wave reads that column
-    // block), formed transposed so that a lane writes four consecutive
-    // columns of one row at once; U goes from the accumulators straight to
-    // the workspace.
+    // One job = one 16-wide column block of Y (or Z), all row blocks. Both go
+    // from the accumulators straight to the workspace: Wk formed transposed,
+    // so that a lane's four consecutive columns of one row are one piece of
+    // the scan's row-block fragment; U as accumulator tiles.
     const size_t uoff = (size_t)n * C * DV;
+    const size_t koff = (size_t)n * C * DK;
     {
       Frag<C, Tin> ft[TB];
 #pragma unroll
@@ -969,31 +969,21 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
             mma(acc[tb], fm, ft[tb]);
           }
 #pragma unroll
-          for (int tb = 0; tb < TB; ++tb) {
-            Tin wv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = from_f32<Tin>(acc[tb][i]);
-            *reinterpret_cast<RawQuad<Tin>*>(M + (tb * 16 + acc_col()) * ld + ct * 16 +
-                                             acc_row(0)) =
-                *reinterpret_cast<const RawQuad<Tin>*>(wv);
-          }
+          for (int tb = 0; tb < TB; ++tb)
+            Frag<DK, Tin>::store_acc_kblock(wb.wk + koff + (size_t)tb * 16 * DK, ct, acc[tb]);
         }
       }
     }
-    __syncthreads();
 
-    // ---- Wk (and GDN-2's Q^) as row-block fragments -------------------------
-    {
-      const size_t koff = (size_t)n * C * DK;
-      constexpr int NJ = (kDecay ? 2 : 1) * TB;
+    // ---- decay variants: the decayed queries Q^ as row-block fragments ------
+    if constexpr (kDecay) {
 #pragma unroll
-      for (int it = 0; it < (NJ + NW - 1) / NW; ++it) {
-        const int job = wave + it * NW;
-        if (job >= NJ) break;
-        const int tb = job % TB, kind = job / TB;
+      for (int it = 0; it < (TB + NW - 1) / NW; ++it) {
+        const int tb = wave + it * NW;
+        if (tb >= TB) break;
         Frag<DK, Tin> f;
-        f.load((kind == 1 ? Qs : Ys) + tb * 16 * LDK, LDK);
-        f.store_global((kind == 1 ? wb.qh : wb.wk) + koff + (size_t)tb * 16 * DK);
+        f.load(Qs + tb * 16 * LDK, LDK);
+        f.store_global(wb.qh + koff + (size_t)tb * 16 * DK);
       }
     }
     __syncthreads();  // the next chunk's operands overwrite the tiles
