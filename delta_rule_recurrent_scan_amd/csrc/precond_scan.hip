@@ -450,16 +450,18 @@ struct ChainRegs {
       kr[i] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
                      rk, (row * DK + (unsigned)(q * SEG1 + i * VEC)) * ES, 0, 0));
-    // V is zero above its 16 x 16 block diagonal: only lanes whose columns
-    // reach row t's block load (the rest hold zeros)
+    // V is zero above its 16 x 16 block diagonal (and not written there):
+    // lanes whose columns lie beyond row t's block read the start of the row
+    // instead and hold zeros, so that every lane issues the same loads and
+    // the compiler can count them
     const bool vlive = NV * q < 16 * (t / 16 + 1);
+    const unsigned vcol = vlive ? (unsigned)(NV * q) : 0u;
 #pragma unroll
     for (int i = 0; i < NV / 4; ++i) {
-      vr[i] = float4{0.f, 0.f, 0.f, 0.f};
-      if (vlive)
-        vr[i] = __builtin_bit_cast(
-            float4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rr, (unsigned)(G::R_V + t * C + NV * q + 4 * i) * 4u, 0, 0));
+      const float4 x = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(
+                      rr, (unsigned)(G::R_V + t * C + vcol + 4 * i) * 4u, 0, 0));
+      vr[i] = vlive ? x : float4{0.f, 0.f, 0.f, 0.f};
     }
     g0 = __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rr, (unsigned)(G::R_G + t) * 4u, 0, 0));
