@@ -26,9 +26,10 @@
 //   ktilde  one workgroup per chunk: K~ from d, g and the keys.
 // Precision: d never passes through bf16. The Gram matrix of a is formed on
 // MFMA from an exact two-term bf16 split of a (a bf16 key squared has a 16-bit
-// significand), T and V are fp32 and the chain runs in fp32; only the
-// correction term L A of K~, rounded afterwards to the key dtype, uses
-// operands in the key dtype.
+// significand), T and V are fp32 and the chain runs in fp32; only the ktilde
+// kernel's correction term L A (chunks of 16 and 32 tokens), rounded
+// afterwards to the key dtype, uses operands in the key dtype (at chunk 64
+// the phase-2 prep forms K~ from d's own recursion in fp32).
 #include "device_common.hpp"
 #include "launch.hpp"
 

@@ -49,8 +49,9 @@ struct OsdnVariant {};
 struct Gdn2Variant {};
 // OSDN with the preconditioned keys formed in the engine from the raw keys,
 // the phase-1 chunk records (gate prefix, step sizes) and the entry values
-// of d: K~ = (P d^T + L A) * K, L[t][i] = (P_t / P_{i+1}) g_i for i < t,
-// A = K * K ([OSDN-it] 2.2). Requires chunk == the phase-1 chunk.
+// of d: K~_t = d_t * k_t, with d_t from the preconditioner's own recursion
+// inside the chunk, d_{t+1} = r_t d_t + g_t (k_t * k_t), in fp32 from the
+// entry value ([OSDN-it] 2.2-2.3). Requires chunk == the phase-1 chunk.
 struct OsdnFusedVariant {};
 // OSDN on a backbone with per-key-channel decay (Kimi-style; a Gated
 // DeltaNet scalar decay is the case of equal channels): S_t = S_{t-1}
