@@ -245,7 +245,7 @@ int osdn_gated_forward_supported(int Dk, int Dv, int chunk, int dtype);
 /* Device workspace, in bytes, that osdn_gated_forward needs (0 if the sizes
  * are invalid or unsupported, or the call needs none). chunk = 64, where the
  * engine's layout with the preconditioned keys formed inside it fits (bf16 at
- * every supported Dk, Dv; fp32 at Dk = 32, and at Dk = 64 with Dv = 32):
+ * every supported Dk, Dv; fp32 at Dk = 32, and at Dk = 64 with Dv <= 64):
  * osdn_precond_workspace_bytes followed by gdn2_forward_workspace_bytes.
  * Otherwise the preconditioned keys ([B,H,T,Dk] in the storage dtype, rounded
  * up to 256 bytes), then scratch shared by the two phases (the larger of the
