@@ -174,7 +174,8 @@ __global__ __launch_bounds__(kBwdThreads) void osdn_bwd_kernel(
     float* __restrict__ gS0) {
   constexpr int NC = DK / 16, NR = kBwdNR, RS = DV / kBwdSliceRows;
   constexpr int NW = kBwdThreads / kWave, SW = share_width(DK, false);
-  __shared__ __attribute__((aligned(16))) float red[2][NW][SW];
+  // per-wave row sums of a group of kRevAhead tokens (two groups in turn)
+  __shared__ __attribute__((aligned(16))) float red[2][kRevAhead][NW][SW];
   int bh, sl;
   slice_of(RS, bh, sl);
   if (bh >= BH) return;
@@ -224,6 +225,7 @@ __global__ __launch_bounds__(kBwdThreads) void osdn_bwd_kernel(
     for (int u = 0; u < kRevAhead; ++u) fetch(ring[u], max(T - 1 - u, 0));
   }
   for (int base = 0; base < T; base += kRevAhead) {
+    const int b = (base / kRevAhead) & 1;
 #pragma unroll
     for (int u = 0; u < kRevAhead; ++u) {
       const int t = T - 1 - (base + u);
@@ -289,9 +291,7 @@ __global__ __launch_bounds__(kBwdThreads) void osdn_bwd_kernel(
         if (cl == i) gv[tt * DV + row0 + kBwdRG * i] = bt * w[i];
 
       // the slice's sums over its rows: four row groups per wave by swaps,
-      // the waves through LDS (buffers alternating by token, one barrier),
-      // one coalesced store per token
-      const int b = t & 1;
+      // the waves through LDS, added up once per group of tokens (below)
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         pq[j] = add_swap32(add_swap16(pq[j]));
@@ -303,18 +303,25 @@ __global__ __launch_bounds__(kBwdThreads) void osdn_bwd_kernel(
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
           const int col = dec_col<DK>(cl, j);
-          red[b][wave][col] = pq[j];
-          red[b][wave][DK + col] = pu[j];
-          red[b][wave][2 * DK + col] = py[j];
+          red[b][u][wave][col] = pq[j];
+          red[b][u][wave][DK + col] = pu[j];
+          red[b][u][wave][2 * DK + col] = py[j];
         }
-        if (lane == 0) red[b][wave][3 * DK] = pb;
+        if (lane == 0) red[b][u][wave][3 * DK] = pb;
       }
-      __syncthreads();
-      float* sh = Sh + (size_t)t * RS * SW;
+    }
+    // one barrier per group of tokens (the two groups' buffers alternate),
+    // then one coalesced store per token
+    __syncthreads();
+    const int ng = min(kRevAhead, T - base);
+#pragma unroll
+    for (int u = 0; u < kRevAhead; ++u) {
+      if (u >= ng) break;
+      float* sh = Sh + (size_t)(T - 1 - (base + u)) * RS * SW;
       for (int e = threadIdx.x; e < 3 * DK + 1; e += kBwdThreads) {
         float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < NW; ++m) acc += red[b][m][e];
+        for (int m = 0; m < NW; ++m) acc += red[b][u][m][e];
         sh[e] = acc;
       }
     }
