@@ -260,7 +260,9 @@ __global__ __launch_bounds__(kBwdThreads) void gated_bwd_kernel(GParams p) {
   constexpr int NW = kBwdThreads / kWave, SW = share_width(DK, true);
   // per wave: S_dec^T do, dS^T u, S_dec^T w, then u.w, u.do (pad), then the
   // column sums of dS_dec * S_dec
-  __shared__ __attribute__((aligned(16))) float red[2][NW][SW];
+  // per-wave row sums of a group of kGRevAhead tokens (two groups in turn)
+  __shared__ __attribute__((aligned(16))) float red[2][kGRevAhead][NW][SW];
+  int grp = 0;  // groups so far (their buffers alternate across intervals)
   int bh, sl;
   slice_of(RS, bh, sl);
   if (bh >= p.BH) return;
@@ -335,7 +337,8 @@ __global__ __launch_bounds__(kBwdThreads) void gated_bwd_kernel(GParams p) {
     RTok ring[kGRevAhead];
 #pragma unroll
     for (int u = 0; u < kGRevAhead; ++u) rfetch(ring[u], max(t1 - u, t0));
-    for (int base = 0; base <= t1 - t0; base += kGRevAhead) {
+    for (int base = 0; base <= t1 - t0; base += kGRevAhead, ++grp) {
+      const int b = grp & 1;
 #pragma unroll
       for (int u = 0; u < kGRevAhead; ++u) {
         const int t = t1 - (base + u);
@@ -408,7 +411,8 @@ __global__ __launch_bounds__(kBwdThreads) void gated_bwd_kernel(GParams p) {
         ud = cl == 0 ? ud : 0.f;
         uw = cl == 0 ? uw : 0.f;
         // the slice's sums over its rows: four row groups per wave by
-        // swaps, the waves through LDS, one coalesced store per token
+        // swaps, the waves through LDS, added up once per group of tokens
+        // (below)
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
           pq[j] = add_swap32(add_swap16(pq[j]));
@@ -418,27 +422,32 @@ __global__ __launch_bounds__(kBwdThreads) void gated_bwd_kernel(GParams p) {
         }
         ud = wave_sum(ud);
         uw = wave_sum(uw);
-        const int b = t & 1;
         if (lane < 16) {
 #pragma unroll
           for (int j = 0; j < NC; ++j) {
             const int col = dec_col<DK>(cl, j);
-            red[b][wave][col] = pq[j];
-            red[b][wave][DK + col] = pu[j];
-            red[b][wave][2 * DK + col] = py[j];
-            red[b][wave][3 * DK + 4 + col] = pa[j];
+            red[b][u][wave][col] = pq[j];
+            red[b][u][wave][DK + col] = pu[j];
+            red[b][u][wave][2 * DK + col] = py[j];
+            red[b][u][wave][3 * DK + 4 + col] = pa[j];
           }
           if (lane == 0) {
-            red[b][wave][3 * DK] = uw;
-            red[b][wave][3 * DK + 1] = ud;
+            red[b][u][wave][3 * DK] = uw;
+            red[b][u][wave][3 * DK + 1] = ud;
           }
         }
-        __syncthreads();
-        float* sh = Shb + (size_t)t * RS * SW;
+      }
+      // one barrier per group of tokens, then one coalesced store per token
+      __syncthreads();
+      const int ng = min(kGRevAhead, t1 - t0 + 1 - base);
+#pragma unroll
+      for (int u = 0; u < kGRevAhead; ++u) {
+        if (u >= ng) break;
+        float* sh = Shb + (size_t)(t1 - (base + u)) * RS * SW;
         for (int e = threadIdx.x; e < SW; e += kBwdThreads) {
           float acc = 0.f;
 #pragma unroll
-          for (int m = 0; m < NW; ++m) acc += red[b][m][e];
+          for (int m = 0; m < NW; ++m) acc += red[b][u][m][e];
           sh[e] = acc;
         }
       }
