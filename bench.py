@@ -89,7 +89,7 @@ def measured_traffic(kernel, run):
 
 
 # ---------------------------------------------------------------------------
-# Algorithmic work (SURVEY 8(d) per-unit figures)
+# Algorithmic work: the bytes and flops the method itself must move and do
 # ---------------------------------------------------------------------------
 
 def _s(w):
