@@ -333,10 +333,14 @@ __global__ __launch_bounds__(kBwdThreads) void gated_bwd_kernel(GParams p) {
         }
       }
     }
-    // and backwards through it
+    // and backwards through it; the state before each token is fetched one
+    // token ahead (the state before the last token is still in s)
     RTok ring[kGRevAhead];
 #pragma unroll
     for (int u = 0; u < kGRevAhead; ++u) rfetch(ring[u], max(t1 - u, t0));
+    float sn[NR][NC];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) load_cols<DK, float>(sb_row(max(t1 - 1, t0) - t0, i), cl, sn[i]);
     for (int base = 0; base <= t1 - t0; base += kGRevAhead, ++grp) {
       const int b = grp & 1;
 #pragma unroll
@@ -345,8 +349,13 @@ __global__ __launch_bounds__(kBwdThreads) void gated_bwd_kernel(GParams p) {
         if (t < t0) break;
         if (t < t1) {
 #pragma unroll
-          for (int i = 0; i < NR; ++i) load_cols<DK, float>(sb_row(t - t0, i), cl, s[i]);
+          for (int i = 0; i < NR; ++i) {
+#pragma unroll
+            for (int j = 0; j < NC; ++j) s[i][j] = sn[i][j];
+          }
         }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) load_cols<DK, float>(sb_row(max(t - 1, t0) - t0, i), cl, sn[i]);
         const size_t tt = tb + t;
         const RTok cur = ring[u];
         rfetch(ring[u], max(t - kGRevAhead, t0));
