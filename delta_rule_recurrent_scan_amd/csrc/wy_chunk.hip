@@ -342,8 +342,13 @@ struct PrepRegs {
   // row and are zeroed when staged), so that the compiler can count them and
   // the fetch is only waited on where the staging uses it.
   __device__ __forceinline__ void load(const ChunkArgs& p, int n, int nchunks) {
+    load_a(p, n, nchunks);
+    load_b(p, n, nchunks);
+  }
+  // keys, queries (and the write or erase keys) with their beta
+  __device__ __forceinline__ void load_a(const ChunkArgs& p, int n, int nchunks) {
     const int bh = n / nchunks, j = n - bh * nchunks;
-    const int T = p.T, Dv = p.Dv, tid = threadIdx.x;
+    const int T = p.T, tid = threadIdx.x;
     const int valid = min(C, T - j * C);
     vrows = valid;
     const size_t t0 = (size_t)bh * T + (size_t)j * C;
@@ -358,6 +363,14 @@ struct PrepRegs {
       if constexpr (!kFused) x[i] = *reinterpret_cast<const uint4*>(xs + gi);
       if constexpr (!kGdn2) bk[i] = p.beta[t0 + rr];
     }
+  }
+  // the record entries (fused), values (and write gates) with their beta,
+  // and the decays
+  __device__ __forceinline__ void load_b(const ChunkArgs& p, int n, int nchunks) {
+    const int bh = n / nchunks, j = n - bh * nchunks;
+    const int T = p.T, Dv = p.Dv, tid = threadIdx.x;
+    const int valid = min(C, T - j * C);
+    const size_t t0 = (size_t)bh * T + (size_t)j * C;
     if constexpr (kFused) {
       // the phase-1 chunk of this engine chunk has the same index
       const float* rc = p.prec + (size_t)n * kRecStride;
@@ -514,8 +527,10 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
   for (int pos = blockIdx.x; pos < total; pos += gridDim.x) {
     const int n = chunk_of(pos);
     regs.store(Ys, Xs, Qs, Zs, smem);
-    // the next chunk's raw operands (the last chunk again at the end)
-    regs.load(p, chunk_of(min(pos + (int)gridDim.x, total - 1)), nchunks);
+    // the next chunk's raw operands (the last chunk again at the end), in
+    // two parts: the keys and queries here, the rest after the first barrier
+    const int nn = chunk_of(min(pos + (int)gridDim.x, total - 1));
+    regs.load_a(p, nn, nchunks);
     // Decay variants: lambda at the first and last token of each 16-token
     // block (doubling scratch), and, for this wave's diagonal tile when its
     // block decays too strongly for the factored form, the exact tile.
@@ -661,6 +676,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     };
     if constexpr (kDecay && !kFused) decay_pass();
     __syncthreads();
+    regs.load_b(p, nn, nchunks);
     if constexpr (kFused) {
       // ---- K~ = d_t * k_t in place over the raw keys --------------------------
       // Inside the chunk the preconditioner follows its own recursion,
