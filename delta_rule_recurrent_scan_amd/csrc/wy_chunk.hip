@@ -344,6 +344,7 @@ struct PrepRegs {
   __device__ __forceinline__ void load(const ChunkArgs& p, int n, int nchunks) {
     load_a(p, n, nchunks);
     load_b(p, n, nchunks);
+    load_c(p, n, nchunks);
   }
   // keys, queries (and the write or erase keys) with their beta
   __device__ __forceinline__ void load_a(const ChunkArgs& p, int n, int nchunks) {
@@ -364,8 +365,7 @@ struct PrepRegs {
       if constexpr (!kGdn2) bk[i] = p.beta[t0 + rr];
     }
   }
-  // the record entries (fused), values (and write gates) with their beta,
-  // and the decays
+  // the record entries (fused), values (and write gates) with their beta
   __device__ __forceinline__ void load_b(const ChunkArgs& p, int n, int nchunks) {
     const int bh = n / nchunks, j = n - bh * nchunks;
     const int T = p.T, Dv = p.Dv, tid = threadIdx.x;
@@ -392,6 +392,13 @@ struct PrepRegs {
       else
         bv[i] = p.beta[t0 + rr];
     }
+  }
+  // the decays (decay variants)
+  __device__ __forceinline__ void load_c(const ChunkArgs& p, int n, int nchunks) {
+    const int bh = n / nchunks, j = n - bh * nchunks;
+    const int T = p.T, tid = threadIdx.x;
+    const int valid = min(C, T - j * C);
+    const size_t t0 = (size_t)bh * T + (size_t)j * C;
     if constexpr (kDecay) {
 #pragma unroll
       for (int i = 0; i < NLA; ++i) {
@@ -528,7 +535,8 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
     const int n = chunk_of(pos);
     regs.store(Ys, Xs, Qs, Zs, smem);
     // the next chunk's raw operands (the last chunk again at the end), in
-    // two parts: the keys and queries here, the rest after the first barrier
+    // three parts: the keys and queries here, the values and record after the
+    // first barrier, the decays after the Gram section
     const int nn = chunk_of(min(pos + (int)gridDim.x, total - 1));
     regs.load_a(p, nn, nchunks);
     // Decay variants: lambda at the first and last token of each 16-token
@@ -873,6 +881,7 @@ __global__ __launch_bounds__(512) void wy_prep_kernel(ChunkArgs p, int nchunks,
       }
     }
     __syncthreads();
+    regs.load_c(p, nn, nchunks);
     if (kDecay && !fast) {
       // read keys and queries relative to the chunk start from here on (for
       // Wk and the decayed queries): times exp(lambda_{s_b}) <= 1
