@@ -1109,7 +1109,7 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
   const int bh = lin / nvt, vt = lin - bh * nvt;
-  const int tid = threadIdx.x, wave = wave_id();
+  const int wave = wave_id();
   const int v0 = vt * VT;
   Tin* o = (Tin*)p.o;
   const Tin* q = (const Tin*)p.q;
