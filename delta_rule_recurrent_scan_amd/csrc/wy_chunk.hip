@@ -1067,7 +1067,22 @@ struct ScanRegs {
       const int row = min(tb * 16 + (int)(threadIdx.x & 15), min(C, T - j * C) - 1);
       qh.load_row(q + ((size_t)bh * T + (size_t)j * C + row) * DK);
     }
-    pr.load_global(wb.pp + n * C * C + (size_t)tb * 16 * C);
+    if constexpr (sizeof(Tin) == 2 && C % 32 == 0) {
+      // P is zero right of its diagonal blocks. Its columns (tokens) are in
+      // the permuted slot order of W^T: piece i holds token tiles 2i and
+      // 2i + 1, so a piece is zero for row blocks below tile 2i. Such a
+      // piece is read from piece 0's addresses instead (so that it touches
+      // no further memory); the step zeroes it where P is used.
+      const int lane = threadIdx.x & 63;
+      const Tin* pb = wb.pp + n * C * C + (size_t)tb * 16 * C;
+#pragma unroll
+      for (int i = 0; i < C / 32; ++i) {
+        const int src = 2 * i <= tb ? i * 64 + lane : lane;
+        pr.v[i] = *reinterpret_cast<const bf16x8*>(pb + src * 8);
+      }
+    } else {
+      pr.load_global(wb.pp + n * C * C + (size_t)tb * 16 * C);
+    }
     const Tin* ub = wb.u + n * C * Dv;
     if constexpr (VB % 2 == 0) {
 #pragma unroll
@@ -1205,9 +1220,17 @@ __global__ __launch_bounds__(256) void wy_scan_kernel(ChunkArgs p, int nchunks,
       if (kAllRowWaves || wave < TB) {
         // the wave's 16 output rows go through LDS (rows of this wave only)
         // and out as one 16-byte store per lane
+        Frag<C, Tin> prz = cur.pr;
+        if constexpr (sizeof(Tin) == 2 && C % 32 == 0) {
+          // the pieces of P that the operand fetch skipped (zero in P)
+          const int tb = min(wave, TB - 1);
+#pragma unroll
+          for (int i = 0; i < C / 32; ++i)
+            if (2 * i > tb) prz.v[i] = bf16x8{};
+        }
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-          mma(oacc[vb], fw[vb], cur.pr);  // transposed: four columns per lane
+          mma(oacc[vb], fw[vb], prz);  // transposed: four columns per lane
           Tin ov[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) ov[i] = from_f32<Tin>(p.scale * oacc[vb][i]);
